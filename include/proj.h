@@ -1,0 +1,164 @@
+/*
+ * proj.h -- C ABI of libproj: shape-specialised bf16 weight projections
+ *           Y[M,N] = X[M,K] . W[N,K]^T on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the weight projection of a decoder layer and of its output
+ * head, as in the blog series "On descend d'un cran": weights and activations
+ * in bf16, accumulators in f32, nothing quantised ("On descend d'un cran"
+ * (post 0), section "Ce qu'il y aura dans le depot"; "#002 le meme compilateur
+ * sur un GPU", section "Le contrat numerique").  N and K are fixed when a plan
+ * is created; the row count M is the only dimension chosen per call ("#001 un
+ * compilateur pour moteur de LLM", section "Un compilateur, pas une
+ * bibliotheque de kernels").
+ *
+ * Conventions for every entry point below:
+ *   - X, W, Y and every other buffer argument are DEVICE pointers on the
+ *     plan's device unless stated otherwise; the caller owns them.
+ *   - X [M,K], W [N,K], Y [M,N] are dense row-major.  X and W hold bf16 bit
+ *     patterns; Y holds f32 (PROJ_OUT_F32) or bf16 (PROJ_OUT_BF16).  All three
+ *     must be 16-byte aligned; Y must not overlap X or W.
+ *   - Work is enqueued on `stream` (a HIP stream of the plan's device, or NULL
+ *     for the null stream) and the call returns without synchronising and
+ *     without allocating.
+ *   - Return codes are PROJ_OK (0) or a negative PROJ_E* value; on failure
+ *     nothing was enqueued and proj_last_error() describes the cause.
+ *   - The library is thread-safe across plans.  One plan may be used from
+ *     several host threads, but its launches that use the split-K workspace
+ *     must not overlap on the device: use one plan per concurrently running
+ *     stream.
+ */
+#ifndef PROJ_H
+#define PROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct proj_plan proj_plan; /* opaque; owned by the library */
+
+/* Storage type of Y.  X and W are always bf16. */
+enum { PROJ_OUT_F32 = 0, PROJ_OUT_BF16 = 1 };
+
+enum {
+    PROJ_OK = 0,
+    PROJ_EINVAL = -1,   /* bad argument: null or misaligned pointer, bad size or dtype, wrong device */
+    PROJ_EDEVICE = -2,  /* a HIP call failed (message holds the HIP error string) */
+    PROJ_ECOMPILE = -3, /* hipRTC could not compile the generated source */
+    PROJ_ENOCAND = -4,  /* no candidate kernel passed validation for some row bucket */
+    PROJ_ENOMEM = -5    /* device allocation failed */
+};
+
+/*
+ * Build a plan for Y = X . W^T with fixed N (rows of W) and K (row length).
+ *
+ * Emits HIP source with N, K, tile sizes and trip counts as literals, compiles
+ * it with hipRTC for the current device, then, for each row bucket
+ * {1}, {2..16}, {17..128}, {129..512}, {513..1024}, {1025..2048}, {2049..8192},
+ * validates every candidate kernel on synthetic probe inputs (full and partial
+ * block, NaN-sentinel output, integer probe bit-exact) against a plain
+ * reference kernel, times the ones that pass and keeps the fastest: the
+ * load-time tuner with its correctness gate of "#004 the same compiler on
+ * Apple's chips", sections "Catching up on prefill" and "The night the engine
+ * chose wrong".  Blocks for seconds.
+ *
+ * N >= 1, K >= 8 with K % 8 == 0, dtype in {PROJ_OUT_F32, PROJ_OUT_BF16}.
+ * The plan is bound to the device current at the call.  Returns NULL on
+ * failure (see proj_last_error()).
+ *
+ * Environment (read at creation): PROJ_LOG=1 prints the tuner log to stderr;
+ * PROJ_TUNE=0 skips timing and takes the first candidate that validates;
+ * PROJ_TUNE_REPS=<n> sets timed launches per candidate; PROJ_FORCE=<name>
+ * keeps only that candidate (plus the plain kernel) where it applies;
+ * PROJ_DUMP_DIR=<dir> writes the generated source and code object there.
+ */
+proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
+
+/*
+ * Enqueue Y[0:M, :] = X[0:M, :] . W^T on `stream`.  Rows of Y at or past M are
+ * never written.  M == 0 returns PROJ_OK without launching; M < 0, null or
+ * misaligned pointers, or a current device other than the plan's give
+ * PROJ_EINVAL; a failed launch gives PROJ_EDEVICE.  M above 8192 is processed
+ * as consecutive blocks of at most 8192 rows.
+ */
+int proj_run(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M,
+             hipStream_t stream);
+
+/* Free the plan's module and workspace.  NULL-safe.  No launch of this plan may
+ * still be pending on the device. */
+void proj_plan_destroy(proj_plan* plan);
+
+/* Message of the last failure on the calling thread ("" if none).  The pointer
+ * stays valid until the next library call on this thread. */
+const char* proj_last_error(void);
+
+/* ---- introspection and forced variants (tests, benchmarks, ablations) ---- */
+
+/*
+ * Write the HIP source a plan for (N, K, dtype) would compile for device
+ * architecture `arch` (e.g. "gfx950"), NUL-terminated, into host buffer `buf`
+ * of `cap` bytes; `*needed` (if not NULL) receives the size including the NUL.
+ * Needs no GPU.  Returns PROJ_EINVAL for bad shapes or if cap is too small
+ * (buf may be NULL to query the size).  The analogue of the pages' option that
+ * dumps emitted code ("#001 un compilateur pour moteur de LLM", section "Lire
+ * le meme emetteur rempli deux fois").
+ */
+int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* buf, size_t cap,
+                     size_t* needed);
+
+/* JSON text (host buffer) describing the plan: shape, candidates, per-bucket
+ * choice and timings, the tuner log, compile and tuning seconds.  Same size
+ * protocol as proj_emit_source. */
+int proj_plan_describe(const proj_plan* plan, char* buf, size_t cap, size_t* needed);
+
+/* Number of compiled candidates, and the name of candidate `idx` (host buffer). */
+int proj_plan_num_candidates(const proj_plan* plan);
+int proj_plan_candidate_name(const proj_plan* plan, int idx, char* buf, size_t cap);
+
+/* Rows this candidate accepts per launch (16 for the GEMV families, 8192 for
+ * the tiled GEMMs, fewer for a split-K GEMM whose partials would not fit the
+ * plan's workspace), or a negative error code. */
+int64_t proj_plan_candidate_max_m(const proj_plan* plan, int idx);
+
+/*
+ * Like proj_run but with candidate `idx` instead of the tuned choice; M must
+ * be within the candidate's limit (proj_plan_candidate_max_m).  The analogue of
+ * the pages' command-line override of a tuned variant ("#004 the same compiler
+ * on Apple's chips", section "Reproducing at home").
+ */
+int proj_run_candidate(const proj_plan* plan, int idx, const void* X, const void* W, void* Y,
+                       int64_t M, hipStream_t stream);
+
+/* Index of the candidate proj_run uses for M rows (M >= 1), or a negative error. */
+int proj_plan_choice(const proj_plan* plan, int64_t M);
+
+/* ---- measurement support (shape-independent) ---- */
+
+/*
+ * Enqueue one streaming read of `bytes` bytes at device pointer `buf`
+ * (16-byte aligned, bytes % 16 == 0) with non-temporal 16-byte loads over the
+ * whole device; `sink` is a device pointer to 4 writable bytes that is written
+ * only in the practically impossible case that the XOR of all data equals
+ * `never`.  Time it with events on `stream` to get the device's read bandwidth,
+ * the denominator the pages measure instead of assuming ("#001 un compilateur
+ * pour moteur de LLM", section "Mesurer la limite plutot que la supposer").
+ */
+int proj_probe_read(const void* buf, int64_t bytes, uint32_t never, void* sink, hipStream_t stream);
+
+/*
+ * Enqueue out[i] = bf16_rne(in[i]) for i < n with the exact device function
+ * the projection epilogue uses (in: f32 device array, out: uint16 device
+ * array).  Exposed so that the epilogue rounding can be checked on all 2^32
+ * f32 patterns, as the pages check their GPU's f32 -> f16 conversion ("#004
+ * the same compiler on Apple's chips", section "f16").
+ */
+int proj_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PROJ_H */

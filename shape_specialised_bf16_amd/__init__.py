@@ -1,0 +1,238 @@
+"""Python binding of libproj: shape-specialised bf16 projections Y = X . W^T on gfx950.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libproj.so`` (built in-tree by ``shape_specialised_bf16_amd.build``);
+torch supplies device memory and the current stream.  Importing this package
+without the built library raises ImportError: there is no fallback.
+
+    plan = Plan(N, K, "f32")          # emit, compile (hipRTC), validate and tune
+    Y = plan.run(X, W)                # X [M,K] bf16, W [N,K] bf16 -> Y [M,N] f32
+
+C entry points and their semantics: ``include/proj.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+__all__ = ["Plan", "ProjError", "emit_source", "probe_read", "round_bf16", "LIB_PATH",
+           "OUT_F32", "OUT_BF16", "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libproj.so")
+
+OUT_F32 = 0
+OUT_BF16 = 1
+_ERRORS = {-1: "PROJ_EINVAL", -2: "PROJ_EDEVICE", -3: "PROJ_ECOMPILE", -4: "PROJ_ENOCAND", -5: "PROJ_ENOMEM"}
+
+# Every function declared in include/proj.h.
+EXPORTED_SYMBOLS = (
+    "proj_plan_create", "proj_run", "proj_plan_destroy", "proj_last_error", "proj_emit_source",
+    "proj_plan_describe", "proj_plan_num_candidates", "proj_plan_candidate_name",
+    "proj_plan_candidate_max_m", "proj_run_candidate", "proj_plan_choice", "proj_probe_read",
+    "proj_round_bf16",
+)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m shape_specialised_bf16_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+# torch ships its own HIP runtime (SONAME libamdhip64.so.7, loaded by torch under
+# another file name).  Importing torch first makes libproj.so bind to that same
+# runtime instance, so torch's streams and allocations are valid in libproj;
+# loading libproj first would bring up a second, separate HIP runtime.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib.proj_plan_create.argtypes = [_i64, _i64, ctypes.c_int]
+_lib.proj_plan_create.restype = _p
+_lib.proj_run.argtypes = [_p, _p, _p, _p, _i64, _p]
+_lib.proj_run.restype = ctypes.c_int
+_lib.proj_plan_destroy.argtypes = [_p]
+_lib.proj_plan_destroy.restype = None
+_lib.proj_last_error.argtypes = []
+_lib.proj_last_error.restype = ctypes.c_char_p
+_lib.proj_emit_source.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_char_p, ctypes.c_char_p,
+                                  ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+_lib.proj_emit_source.restype = ctypes.c_int
+_lib.proj_plan_describe.argtypes = [_p, ctypes.c_char_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+_lib.proj_plan_describe.restype = ctypes.c_int
+_lib.proj_plan_num_candidates.argtypes = [_p]
+_lib.proj_plan_num_candidates.restype = ctypes.c_int
+_lib.proj_plan_candidate_name.argtypes = [_p, ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
+_lib.proj_plan_candidate_name.restype = ctypes.c_int
+_lib.proj_plan_candidate_max_m.argtypes = [_p, ctypes.c_int]
+_lib.proj_plan_candidate_max_m.restype = _i64
+_lib.proj_run_candidate.argtypes = [_p, ctypes.c_int, _p, _p, _p, _i64, _p]
+_lib.proj_run_candidate.restype = ctypes.c_int
+_lib.proj_plan_choice.argtypes = [_p, _i64]
+_lib.proj_plan_choice.restype = ctypes.c_int
+_lib.proj_probe_read.argtypes = [_p, _i64, ctypes.c_uint32, _p, _p]
+_lib.proj_probe_read.restype = ctypes.c_int
+_lib.proj_round_bf16.argtypes = [_p, _p, _i64, _p]
+_lib.proj_round_bf16.restype = ctypes.c_int
+
+
+class ProjError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.proj_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_ERRORS.get(code, code)}: {msg}")
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise ProjError(rc, where)
+    return rc
+
+
+def _text(fn, *args) -> str:
+    need = ctypes.c_size_t(0)
+    _check(fn(*args, None, 0, ctypes.byref(need)), fn.__name__)
+    buf = ctypes.create_string_buffer(need.value)
+    _check(fn(*args, buf, need.value, None), fn.__name__)
+    return buf.value.decode()
+
+
+def emit_source(N: int, K: int, dtype: str = "f32", arch: str = "gfx950") -> str:
+    """The HIP source a plan for (N, K, dtype) compiles (no GPU needed)."""
+    return _text(_lib.proj_emit_source, N, K, _dtype_code(dtype), arch.encode())
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in ("f32", "float32", OUT_F32):
+        return OUT_F32
+    if dtype in ("bf16", "bfloat16", OUT_BF16):
+        return OUT_BF16
+    try:
+        import torch
+        if dtype is torch.float32:
+            return OUT_F32
+        if dtype is torch.bfloat16:
+            return OUT_BF16
+    except ImportError:
+        pass
+    raise ValueError(f"unsupported output dtype {dtype!r} (f32 or bf16)")
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _bf16_2d(t, name: str, cols: int):
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 values (bfloat16 or 16-bit bit patterns), got {t.dtype}")
+    if t.dim() != 2 or t.shape[1] != cols or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [*, {cols}] matrix, got {tuple(t.shape)}")
+
+
+class Plan:
+    """A compiled, tuned projection plan for fixed (N, K) and output dtype."""
+
+    def __init__(self, N: int, K: int, dtype="f32"):
+        self.N, self.K = int(N), int(K)
+        self.dtype_code = _dtype_code(dtype)
+        h = _lib.proj_plan_create(self.N, self.K, self.dtype_code)
+        if not h:
+            raise ProjError(-1, f"proj_plan_create({N}, {K}, {dtype})")
+        self._h = ctypes.c_void_p(h)
+
+    @property
+    def out_dtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype_code == OUT_BF16 else torch.float32
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.proj_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _prep(self, X, W, Y):
+        import torch
+        _bf16_2d(X, "X", self.K)
+        _bf16_2d(W, "W", self.K)
+        if W.shape[0] != self.N:
+            raise ValueError(f"W must be [{self.N}, {self.K}], got {tuple(W.shape)}")
+        M = X.shape[0]
+        if Y is None:
+            Y = torch.empty((M, self.N), dtype=self.out_dtype, device=X.device)
+        elif (Y.dtype != self.out_dtype or Y.dim() != 2 or Y.shape[1] != self.N or Y.shape[0] < M
+              or not Y.is_contiguous()):
+            raise ValueError(f"Y must be a contiguous [>= {M}, {self.N}] {self.out_dtype} matrix")
+        return M, Y
+
+    def run(self, X, W, Y=None, stream=None):
+        """Y[:M] = X . W^T for all M rows of X, enqueued on `stream` (default: current)."""
+        M, Y = self._prep(X, W, Y)
+        _check(_lib.proj_run(self._h, X.data_ptr(), W.data_ptr(), Y.data_ptr(), M, _stream_handle(stream)),
+               "proj_run")
+        return Y
+
+    def run_ptr(self, X_ptr: int, W_ptr: int, Y_ptr: int, M: int, stream_handle) -> None:
+        """proj_run on raw device addresses (benchmark loops)."""
+        _check(_lib.proj_run(self._h, X_ptr, W_ptr, Y_ptr, M, stream_handle), "proj_run")
+
+    def run_candidate(self, idx: int, X, W, Y=None, stream=None):
+        M, Y = self._prep(X, W, Y)
+        _check(_lib.proj_run_candidate(self._h, idx, X.data_ptr(), W.data_ptr(), Y.data_ptr(), M,
+                                       _stream_handle(stream)), "proj_run_candidate")
+        return Y
+
+    def num_candidates(self) -> int:
+        return _check(_lib.proj_plan_num_candidates(self._h), "proj_plan_num_candidates")
+
+    def candidate_name(self, idx: int) -> str:
+        buf = ctypes.create_string_buffer(128)
+        _check(_lib.proj_plan_candidate_name(self._h, idx, buf, 128), "proj_plan_candidate_name")
+        return buf.value.decode()
+
+    def candidates(self):
+        return [self.candidate_name(i) for i in range(self.num_candidates())]
+
+    def candidate_max_m(self, idx: int) -> int:
+        return _check(_lib.proj_plan_candidate_max_m(self._h, idx), "proj_plan_candidate_max_m")
+
+    def choice(self, M: int) -> str:
+        return self.candidate_name(_check(_lib.proj_plan_choice(self._h, M), "proj_plan_choice"))
+
+    def describe(self) -> dict:
+        return json.loads(_text(_lib.proj_plan_describe, self._h))
+
+
+def probe_read(buf, sink, never: int = 0x9E3779B9, stream=None) -> None:
+    """Enqueue one streaming read of the whole device tensor `buf` (see proj.h)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.proj_probe_read(buf.data_ptr(), nbytes, never, sink.data_ptr(), _stream_handle(stream)),
+           "proj_probe_read")
+
+
+def round_bf16(inp, out, stream=None) -> None:
+    """out[i] = bf16_rne(inp[i]) with the epilogue's device conversion."""
+    import torch
+    if inp.dtype != torch.float32 or out.dtype not in (torch.int16, torch.uint16, torch.bfloat16):
+        raise TypeError("round_bf16: float32 in, 16-bit out")
+    if out.numel() < inp.numel():
+        raise ValueError("round_bf16: out too small")
+    _check(_lib.proj_round_bf16(inp.data_ptr(), out.data_ptr(), inp.numel(), _stream_handle(stream)),
+           "proj_round_bf16")

@@ -1,0 +1,226 @@
+// api.cpp -- the extern "C" entry points declared in include/proj.h.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <sstream>
+
+#include "proj.h"
+#include "proj_internal.h"
+
+namespace proj {
+extern thread_local std::string g_last_error;
+int set_error(int code, const char* f, ...);
+int compile_source(const std::string& src, const std::string& arch, const char* name,
+                   std::shared_ptr<std::vector<char>>* code);
+int device_arch(int dev, std::string* arch, int* cus);
+int create_plan(int64_t N, int64_t K, int dtype, proj_plan** out);
+void destroy_plan(proj_plan* p);
+int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream);
+int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M);
+int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y,
+                     int64_t M, hipStream_t stream);
+
+// Shape-independent support module, one per device, loaded on first use.
+struct SupportModule {
+    hipModule_t mod = nullptr;
+    hipFunction_t probe = nullptr, round = nullptr;
+    int cus = 256;
+};
+static std::mutex g_support_mu;
+static std::map<int, SupportModule> g_support;
+
+static int support_module(SupportModule** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_error(PROJ_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lk(g_support_mu);
+    SupportModule& sm = g_support[dev];
+    if (!sm.mod) {
+        std::string arch;
+        int rc = device_arch(dev, &arch, &sm.cus);
+        if (rc) return rc;
+        std::shared_ptr<std::vector<char>> code;
+        rc = compile_source(emit_support_source(), arch, "proj_support.hip", &code);
+        if (rc) return rc;
+        if ((e = hipModuleLoadData(&sm.mod, code->data())) != hipSuccess)
+            return set_error(PROJ_EDEVICE, "hipModuleLoadData(support): %s", hipGetErrorString(e));
+        if ((e = hipModuleGetFunction(&sm.probe, sm.mod, "proj_probe_read")) != hipSuccess ||
+            (e = hipModuleGetFunction(&sm.round, sm.mod, "proj_round_bf16")) != hipSuccess)
+            return set_error(PROJ_EDEVICE, "hipModuleGetFunction(support): %s", hipGetErrorString(e));
+    }
+    *out = &sm;
+    return PROJ_OK;
+}
+
+static int copy_text(const std::string& s, char* buf, size_t cap, size_t* needed)
+{
+    if (needed) *needed = s.size() + 1;
+    if (!buf) return cap == 0 ? PROJ_OK : set_error(PROJ_EINVAL, "buffer is NULL");
+    if (cap < s.size() + 1)
+        return set_error(PROJ_EINVAL, "buffer of %zu bytes is too small (%zu needed)", cap, s.size() + 1);
+    memcpy(buf, s.c_str(), s.size() + 1);
+    return PROJ_OK;
+}
+
+static std::string json_escape(const std::string& s)
+{
+    std::string o;
+    for (char c : s) {
+        if (c == '"' || c == '\\') { o += '\\'; o += c; }
+        else if (c == '\n') o += "\\n";
+        else if ((unsigned char)c < 0x20) { char b[8]; snprintf(b, sizeof b, "\\u%04x", c); o += b; }
+        else o += c;
+    }
+    return o;
+}
+
+static std::string describe(const proj_plan* p)
+{
+    std::ostringstream s;
+    s << "{\"N\": " << p->N << ", \"K\": " << p->K << ", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
+      << "\", \"arch\": \"" << p->arch << "\", \"device\": " << p->device << ", \"compile_s\": " << p->compile_s
+      << ", \"tune_s\": " << p->tune_s << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
+      << ",\n \"candidates\": [";
+    for (size_t i = 0; i < p->cands.size(); ++i) s << (i ? ", " : "") << "\"" << p->cands[i].name << "\"";
+    s << "],\n \"buckets\": [";
+    for (int b = 0; b < kNumBuckets; ++b) {
+        s << (b ? ",\n  " : "\n  ") << "{\"lo\": " << kBuckets[b].lo << ", \"hi\": " << kBuckets[b].hi
+          << ", \"choice\": \"" << (p->choice[b] >= 0 ? p->cands[p->choice[b]].name : "") << "\", \"us\": "
+          << p->choice_us[b] << ", \"timings_us\": {";
+        if (b < (int)p->timings.size())
+            for (size_t i = 0; i < p->timings[b].size(); ++i)
+                s << (i ? ", " : "") << "\"" << p->cands[p->timings[b][i].first].name << "\": "
+                  << p->timings[b][i].second;
+        s << "}, \"rejected\": [";
+        if (b < (int)p->rejected.size())
+            for (size_t i = 0; i < p->rejected[b].size(); ++i)
+                s << (i ? ", " : "") << "\"" << p->cands[p->rejected[b][i].first].name << "\"";
+        s << "]}";
+    }
+    s << "],\n \"log\": [";
+    for (size_t i = 0; i < p->log.size(); ++i) s << (i ? ",\n  " : "\n  ") << "\"" << json_escape(p->log[i]) << "\"";
+    s << "]}\n";
+    return s.str();
+}
+
+}  // namespace proj
+
+using namespace proj;
+
+extern "C" {
+
+proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype)
+{
+    g_last_error.clear();
+    proj_plan* p = nullptr;
+    if (create_plan(N, K, dtype, &p) != PROJ_OK) return nullptr;
+    return p;
+}
+
+int proj_run(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream)
+{
+    return run_plan(plan, X, W, Y, M, stream);
+}
+
+void proj_plan_destroy(proj_plan* plan) { destroy_plan(plan); }
+
+const char* proj_last_error(void) { return g_last_error.c_str(); }
+
+int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* buf, size_t cap, size_t* needed)
+{
+    if (N < 1 || K < 8 || K % 8 != 0)
+        return set_error(PROJ_EINVAL, "invalid shape N=%lld K=%lld", (long long)N, (long long)K);
+    if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16) return set_error(PROJ_EINVAL, "invalid dtype %d", dtype);
+    const std::string a = (arch && *arch) ? arch : "gfx950";
+    return copy_text(emit_source(N, K, dtype, a, enumerate_candidates(N, K)), buf, cap, needed);
+}
+
+int proj_plan_describe(const proj_plan* plan, char* buf, size_t cap, size_t* needed)
+{
+    if (!plan) return set_error(PROJ_EINVAL, "plan is NULL");
+    return copy_text(describe(plan), buf, cap, needed);
+}
+
+int proj_plan_num_candidates(const proj_plan* plan)
+{
+    if (!plan) return set_error(PROJ_EINVAL, "plan is NULL");
+    return (int)plan->cands.size();
+}
+
+int proj_plan_candidate_name(const proj_plan* plan, int idx, char* buf, size_t cap)
+{
+    if (!plan) return set_error(PROJ_EINVAL, "plan is NULL");
+    if (idx < 0 || idx >= (int)plan->cands.size()) return set_error(PROJ_EINVAL, "candidate %d out of range", idx);
+    return copy_text(plan->cands[idx].name, buf, cap, nullptr);
+}
+
+int64_t proj_plan_candidate_max_m(const proj_plan* plan, int idx)
+{
+    if (!plan) return set_error(PROJ_EINVAL, "plan is NULL");
+    if (idx < 0 || idx >= (int)plan->cands.size()) return set_error(PROJ_EINVAL, "candidate %d out of range", idx);
+    const Candidate& c = plan->cands[idx];
+    int64_t m = c.max_m;
+    if (c.needs_ws()) m = std::min<int64_t>(m, (int64_t)(plan->ws_bytes / ((size_t)c.SK * plan->N * sizeof(float))));
+    return m;
+}
+
+int proj_run_candidate(const proj_plan* plan, int idx, const void* X, const void* W, void* Y, int64_t M,
+                       hipStream_t stream)
+{
+    int rc = check_run_args(plan, X, W, Y, M);
+    if (rc || M == 0) return rc;
+    if (idx < 0 || idx >= (int)plan->cands.size()) return set_error(PROJ_EINVAL, "candidate %d out of range", idx);
+    return launch_candidate(plan, plan->cands[idx], X, W, Y, M, stream);
+}
+
+int proj_plan_choice(const proj_plan* plan, int64_t M)
+{
+    if (!plan) return set_error(PROJ_EINVAL, "plan is NULL");
+    if (M < 1) return set_error(PROJ_EINVAL, "M=%lld must be >= 1", (long long)M);
+    return plan->choice[bucket_of(std::min<int64_t>(M, kMaxBlockRows))];
+}
+
+int proj_probe_read(const void* buf, int64_t bytes, uint32_t never, void* sink, hipStream_t stream)
+{
+    if (!buf || !sink) return set_error(PROJ_EINVAL, "null pointer");
+    if (bytes < 0 || bytes % 16 || ((uintptr_t)buf & 15) || ((uintptr_t)sink & 3))
+        return set_error(PROJ_EINVAL, "buf must be 16-byte aligned with bytes %% 16 == 0, sink 4-byte aligned");
+    if (bytes == 0) return PROJ_OK;
+    SupportModule* sm = nullptr;
+    int rc = support_module(&sm);
+    if (rc) return rc;
+    const int cus = sm->cus;
+    const void* p = buf;
+    long n16 = (long)(bytes / 16);
+    uint32_t nv = never;
+    void* s = sink;
+    void* args[] = {&p, &n16, &nv, &s};
+    const unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * 16, (n16 + 255) / 256));
+    hipError_t e = hipModuleLaunchKernel(sm->probe, gx, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
+    if (e != hipSuccess) return set_error(PROJ_EDEVICE, "probe launch: %s", hipGetErrorString(e));
+    return PROJ_OK;
+}
+
+int proj_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream)
+{
+    if (n < 0) return set_error(PROJ_EINVAL, "n is negative");
+    if (n == 0) return PROJ_OK;
+    if (!in || !out) return set_error(PROJ_EINVAL, "null pointer");
+    SupportModule* sm = nullptr;
+    int rc = support_module(&sm);
+    if (rc) return rc;
+    const float* i = in;
+    uint16_t* o = out;
+    long nn = (long)n;
+    void* args[] = {&i, &o, &nn};
+    const unsigned gx = (unsigned)std::min<int64_t>(65536, (n + 255) / 256);
+    hipError_t e = hipModuleLaunchKernel(sm->round, gx, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
+    if (e != hipSuccess) return set_error(PROJ_EDEVICE, "round launch: %s", hipGetErrorString(e));
+    return PROJ_OK;
+}
+
+}  // extern "C"

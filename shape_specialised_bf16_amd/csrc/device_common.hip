@@ -1,0 +1,106 @@
+// device_common.hip -- types and helpers shared by every device translation unit
+// of the projection library (prepended by the host before hipRTC compiles).
+
+typedef unsigned short u16;
+typedef unsigned int u32;
+typedef unsigned long long u64;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+#define OUT_F32 0
+#define OUT_BF16 1
+
+// Bit patterns written into outputs before a validation run: both are NaNs,
+// which a projection of finite inputs never produces.
+#define SENTINEL_F32 0x7FBADBADu
+#define SENTINEL_BF16 0x7FBAu
+
+namespace dev {
+
+__device__ __forceinline__ float lo_bf16(u32 v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float hi_bf16(u32 v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
+
+// f32 -> bf16, IEEE round to nearest even (lowers to v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ u16 to_bf16(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+__device__ __forceinline__ u32 to_bf16x2(float a, float b)
+{
+    return (u32)to_bf16(a) | ((u32)to_bf16(b) << 16);
+}
+
+template <int NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+// acc += sum of the 8 products of two 16-byte bf16 chunks (f32 FMA, k ascending).
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc)
+{
+    acc = __builtin_fmaf(lo_bf16(w.x), lo_bf16(x.x), acc);
+    acc = __builtin_fmaf(hi_bf16(w.x), hi_bf16(x.x), acc);
+    acc = __builtin_fmaf(lo_bf16(w.y), lo_bf16(x.y), acc);
+    acc = __builtin_fmaf(hi_bf16(w.y), hi_bf16(x.y), acc);
+    acc = __builtin_fmaf(lo_bf16(w.z), lo_bf16(x.z), acc);
+    acc = __builtin_fmaf(hi_bf16(w.z), hi_bf16(x.z), acc);
+    acc = __builtin_fmaf(lo_bf16(w.w), lo_bf16(x.w), acc);
+    acc = __builtin_fmaf(hi_bf16(w.w), hi_bf16(x.w), acc);
+    return acc;
+}
+
+template <int OUT>
+__device__ __forceinline__ void store1(void* Y, long idx, float v)
+{
+    if constexpr (OUT == OUT_F32) reinterpret_cast<float*>(Y)[idx] = v;
+    else reinterpret_cast<u16*>(Y)[idx] = to_bf16(v);
+}
+
+// Four consecutive outputs starting at idx (idx a multiple of 4).
+template <int OUT>
+__device__ __forceinline__ void store4(void* Y, long idx, f32x4 v)
+{
+    if constexpr (OUT == OUT_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Y) + idx) = v;
+    } else {
+        u32x2 p = {to_bf16x2(v.x, v.y), to_bf16x2(v.z, v.w)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<u16*>(Y) + idx) = p;
+    }
+}
+
+// Butterfly reduce-scatter over the 64 lanes of a wave.  On entry every lane
+// holds V partial sums; on exit lane L holds in v[0] the full sum of value
+// index (L >> (6 - log2 V)).  Each halving step exchanges half of the values
+// with the partner lane and keeps the half named by the partner bit, so the
+// total shuffle count is about V instead of 6 V.  The order of additions is
+// fixed, so the result is the same on every run.
+template <int V>
+__device__ __forceinline__ float wave_reduce_scatter(float (&v)[V], int lane)
+{
+    static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
+    int cnt = V;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        if (cnt >= 2) {
+            const int half = cnt / 2;
+            const bool up = (lane & o) != 0;
+#pragma unroll
+            for (int i = 0; i < half; ++i) {
+                float keep = up ? v[i + half] : v[i];
+                float give = up ? v[i] : v[i + half];
+                v[i] = keep + __shfl_xor(give, o);
+            }
+            cnt = half;
+        } else {
+            v[0] += __shfl_xor(v[0], o);
+        }
+    }
+    return v[0];
+}
+
+template <int V> struct log2_of { static constexpr int value = 1 + log2_of<V / 2>::value; };
+template <> struct log2_of<1> { static constexpr int value = 0; };
+
+}  // namespace dev

@@ -1,0 +1,628 @@
+// plan.cpp -- plan creation (emit, hipRTC compile, load), the load-time tuner
+// with its correctness gate, and run-time dispatch on M.
+//
+// The tuner follows "#004 the same compiler on Apple's chips" (blog series "On
+// descend d'un cran"): at load time several variants of each kernel are
+// measured per matrix shape and the fastest is kept (section "Catching up on
+// prefill"), but only after each candidate has been run once against a kernel
+// already trusted, on a full block and on a partial block with the output
+// cleared beforehand, and rejected -- with a log line -- when it departs from it
+// (section "The night the engine chose wrong").  Here the trusted kernel is a
+// plain one-thread-per-output reference that is itself checked against exact
+// integer arithmetic on the host; the output is cleared to a NaN sentinel
+// rather than zero, so an unwritten element cannot pass for a small value; and
+// the acceptance rule is the elementwise tolerance of the numerical contract,
+// with an integer probe that must match bit for bit.
+#include <hip/hiprtc.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <sstream>
+
+#include "proj.h"
+#include "proj_internal.h"
+
+namespace proj {
+
+// ---------------------------------------------------------------- errors
+thread_local std::string g_last_error;
+
+int set_error(int code, const char* f, ...) __attribute__((format(printf, 2, 3)));
+int set_error(int code, const char* f, ...)
+{
+    char buf[2048];
+    va_list ap;
+    va_start(ap, f);
+    vsnprintf(buf, sizeof buf, f, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                         \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return set_error(PROJ_EDEVICE, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), \
+                             __FILE__, __LINE__);                                             \
+    } while (0)
+
+static double now_s()
+{
+    return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+static int env_int(const char* name, int dflt)
+{
+    const char* v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+// ---------------------------------------------------------------- hipRTC
+// Code objects compiled in this process, keyed by the full source text and
+// architecture, so that two plans of the same shape compile once.
+static std::mutex g_cache_mu;
+static std::map<std::string, std::shared_ptr<std::vector<char>>> g_code_cache;
+
+int compile_source(const std::string& src, const std::string& arch, const char* name,
+                   std::shared_ptr<std::vector<char>>* code)
+{
+    const std::string key = arch + "\n" + src;
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        auto it = g_code_cache.find(key);
+        if (it != g_code_cache.end()) {
+            *code = it->second;
+            return PROJ_OK;
+        }
+    }
+    hiprtcProgram prog;
+    if (hiprtcCreateProgram(&prog, src.c_str(), name, 0, nullptr, nullptr) != HIPRTC_SUCCESS)
+        return set_error(PROJ_ECOMPILE, "hiprtcCreateProgram failed");
+    const std::string arch_opt = "--offload-arch=" + arch;
+    // -packed-fp32-ops: no packed f32 ALU instructions in any kernel.
+    const char* opts[] = {arch_opt.c_str(), "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+                          "-packed-fp32-ops"};
+    hiprtcResult r = hiprtcCompileProgram(prog, (int)(sizeof opts / sizeof opts[0]), opts);
+    if (r != HIPRTC_SUCCESS) {
+        size_t ls = 0;
+        hiprtcGetProgramLogSize(prog, &ls);
+        std::string log(ls, '\0');
+        if (ls) hiprtcGetProgramLog(prog, &log[0]);
+        hiprtcDestroyProgram(&prog);
+        if (log.size() > 1800) log = log.substr(0, 1800) + "...";
+        return set_error(PROJ_ECOMPILE, "hipRTC compile of %s failed: %s", name, log.c_str());
+    }
+    size_t cs = 0;
+    hiprtcGetCodeSize(prog, &cs);
+    auto buf = std::make_shared<std::vector<char>>(cs);
+    hiprtcGetCode(prog, buf->data());
+    hiprtcDestroyProgram(&prog);
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        g_code_cache[key] = buf;
+    }
+    *code = buf;
+    return PROJ_OK;
+}
+
+int device_arch(int dev, std::string* arch, int* cus)
+{
+    hipDeviceProp_t p;
+    HIP_TRY(hipGetDeviceProperties(&p, dev));
+    std::string a = p.gcnArchName;
+    const size_t colon = a.find(':');
+    if (colon != std::string::npos) a = a.substr(0, colon);
+    *arch = a;
+    if (cus) *cus = p.multiProcessorCount;
+    return PROJ_OK;
+}
+
+// ---------------------------------------------------------------- launching
+struct LaunchGeom {
+    unsigned gx, gy, threads;
+};
+
+static LaunchGeom geom(const Candidate& c, int64_t N, int64_t M)
+{
+    switch (c.fam) {
+    case Family::GemvValu: return {(unsigned)(N / (c.R * (4 / c.S))), 1u, 256u};
+    case Family::GemvMfma: return {(unsigned)(N / (16 * (4 / c.S))), 1u, 256u};
+    case Family::Gemm: {
+        const int64_t tm = (M + c.BM - 1) / c.BM;
+        return {(unsigned)(tm * (N / c.BN)), (unsigned)c.SK, (unsigned)c.threads};
+    }
+    case Family::Plain:
+    default: return {(unsigned)((M * N + 255) / 256), 1u, 256u};
+    }
+}
+
+// Enqueue candidate c for one block of M <= c.max_m rows.
+int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y,
+                     int64_t M, hipStream_t stream)
+{
+    if (M > c.max_m) return set_error(PROJ_EINVAL, "M=%lld exceeds %s's limit of %lld rows",
+                                      (long long)M, c.name.c_str(), (long long)c.max_m);
+    if (c.ws_bytes(M, p->N) > p->ws_bytes)
+        return set_error(PROJ_EINVAL, "%s needs %zu bytes of split-K workspace at M=%lld, plan has %zu",
+                         c.name.c_str(), c.ws_bytes(M, p->N), (long long)M, p->ws_bytes);
+    const LaunchGeom g = geom(c, p->N, M);
+    const void* x = X;
+    const void* w = W;
+    void* y = Y;
+    float* ws = (float*)p->ws;
+    int m = (int)M;
+    void* args[] = {&x, &w, &y, &ws, &m};
+    HIP_TRY(hipModuleLaunchKernel(c.fn, g.gx, g.gy, 1, g.threads, 1, 1, 0, stream, args, nullptr));
+    if (c.needs_ws()) {
+        const int64_t total4 = M * p->N / 4;
+        const unsigned gx = (unsigned)((total4 + 255) / 256);
+        const float* wsc = ws;
+        void* rargs[] = {&wsc, &y, &m};
+        HIP_TRY(hipModuleLaunchKernel(c.reduce_fn, gx, 1, 1, 256, 1, 1, 0, stream, rargs, nullptr));
+    }
+    return PROJ_OK;
+}
+
+// ---------------------------------------------------------------- the tuner
+struct CheckStats {
+    uint32_t bad, unwritten, guard, max_err, max_ref, pad[3];
+};
+
+static float bits_f(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static float bf16_to_f(uint16_t b) { return bits_f((uint32_t)b << 16); }
+
+// Device buffers and helper kernels used while tuning one plan.
+struct Tuner {
+    proj_plan* p;
+    hipStream_t st = nullptr;
+    hipFunction_t f_fill_probe = nullptr, f_fill_u32 = nullptr, f_ref = nullptr, f_check = nullptr,
+                  f_probe = nullptr;
+    void *Xr = nullptr, *Xi = nullptr, *Wr = nullptr, *Wi = nullptr, *Y = nullptr;
+    float *ref_r = nullptr, *ref_i = nullptr;
+    int* rows_d = nullptr;
+    CheckStats* stats_d = nullptr;
+    void* flush = nullptr;
+    size_t flush_bytes = 0;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    int64_t mmax = 0;
+    static constexpr int64_t kGuardRows = 3;
+
+    ~Tuner()
+    {
+        for (void* q : {Xr, Xi, Wr, Wi, Y, (void*)ref_r, (void*)ref_i, (void*)rows_d, (void*)stats_d, flush})
+            if (q) (void)hipFree(q);
+        if (e0) (void)hipEventDestroy(e0);
+        if (e1) (void)hipEventDestroy(e1);
+        if (st) (void)hipStreamDestroy(st);
+    }
+
+    size_t ysize() const { return p->dtype == PROJ_OUT_BF16 ? 2 : 4; }
+
+    int fill_probe(void* buf, int64_t n, uint32_t seed, int kind, float scale)
+    {
+        unsigned gx = (unsigned)std::min<int64_t>((n + 255) / 256, 65536);
+        long nn = (long)n;
+        void* args[] = {&buf, &nn, &seed, &kind, &scale};
+        HIP_TRY(hipModuleLaunchKernel(f_fill_probe, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
+        return PROJ_OK;
+    }
+
+    int fill_sentinel(int64_t rows)
+    {
+        const int64_t bytes = rows * p->N * (int64_t)ysize();
+        long n32 = (long)(bytes / 4);
+        uint32_t v = p->dtype == PROJ_OUT_BF16 ? 0x7FBA7FBAu : 0x7FBADBADu;
+        unsigned gx = (unsigned)std::min<int64_t>((n32 + 255) / 256, 65536);
+        void* yp = Y;
+        void* args[] = {&yp, &n32, &v};
+        HIP_TRY(hipModuleLaunchKernel(f_fill_u32, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
+        return PROJ_OK;
+    }
+
+    int setup(int64_t max_rows)
+    {
+        mmax = max_rows;
+        HIP_TRY(hipStreamCreate(&st));
+        HIP_TRY(hipEventCreate(&e0));
+        HIP_TRY(hipEventCreate(&e1));
+        HIP_TRY(hipModuleGetFunction(&f_fill_probe, p->module, "proj_fill_probe"));
+        HIP_TRY(hipModuleGetFunction(&f_fill_u32, p->module, "proj_fill_u32"));
+        HIP_TRY(hipModuleGetFunction(&f_ref, p->module, "proj_ref_rows"));
+        HIP_TRY(hipModuleGetFunction(&f_probe, p->module, "proj_probe_read"));
+        HIP_TRY(hipModuleGetFunction(&f_check, p->module,
+                                     p->dtype == PROJ_OUT_BF16 ? "proj_check_bf16" : "proj_check_f32"));
+        const size_t xb = (size_t)mmax * p->K * 2, wb = (size_t)p->N * p->K * 2;
+        const size_t yb = (size_t)(mmax + kGuardRows) * p->N * ysize();
+        if (hipMalloc(&Xr, xb) != hipSuccess || hipMalloc(&Xi, xb) != hipSuccess ||
+            hipMalloc(&Wr, wb) != hipSuccess || hipMalloc(&Wi, wb) != hipSuccess ||
+            hipMalloc(&Y, yb) != hipSuccess || hipMalloc(&ref_r, 8 * p->N * 4) != hipSuccess ||
+            hipMalloc(&ref_i, 8 * p->N * 4) != hipSuccess || hipMalloc(&rows_d, 8 * 4) != hipSuccess ||
+            hipMalloc(&stats_d, sizeof(CheckStats)) != hipSuccess)
+            return set_error(PROJ_ENOMEM, "tuner probe buffers (%zu MiB) could not be allocated",
+                             (2 * xb + 2 * wb + yb) >> 20);
+        // A read of more than the 256 MB last-level cache before each timed launch,
+        // so the launch reads its weights from HBM, as every decode step does.
+        flush_bytes = (size_t)512 << 20;
+        if (hipMalloc(&flush, flush_bytes) != hipSuccess) {
+            flush = nullptr;
+            flush_bytes = 0;
+        } else {
+            HIP_TRY(hipMemsetAsync(flush, 0, flush_bytes, st));
+        }
+        int rc;
+        if ((rc = fill_probe(Xr, mmax * p->K, 1, 0, 1.0f))) return rc;
+        if ((rc = fill_probe(Wr, p->N * p->K, 2, 0, 0.0625f))) return rc;
+        if ((rc = fill_probe(Xi, mmax * p->K, 3, 1, 1.0f))) return rc;
+        if ((rc = fill_probe(Wi, p->N * p->K, 4, 1, 1.0f))) return rc;
+        HIP_TRY(hipStreamSynchronize(st));
+        return PROJ_OK;
+    }
+
+    // Reference rows (f32) for both probes; rows must be < mmax, at most 8.
+    int reference(const std::vector<int>& rows)
+    {
+        HIP_TRY(hipMemcpyAsync(rows_d, rows.data(), rows.size() * 4, hipMemcpyHostToDevice, st));
+        int nr = (int)rows.size();
+        unsigned gx = (unsigned)((p->N + 255) / 256);
+        for (int pass = 0; pass < 2; ++pass) {
+            const void* x = pass ? Xi : Xr;
+            const void* w = pass ? Wi : Wr;
+            float* r = pass ? ref_i : ref_r;
+            int* rd = rows_d;
+            void* args[] = {&x, &w, &rd, &nr, &r};
+            HIP_TRY(hipModuleLaunchKernel(f_ref, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
+        }
+        HIP_TRY(hipStreamSynchronize(st));
+        return PROJ_OK;
+    }
+
+    // The reference kernel itself is checked on the integer probe, where the
+    // exact result is an integer computed here with int64 arithmetic.
+    int self_check_reference(const std::vector<int>& rows)
+    {
+        const int64_t K = p->K, N = p->N;
+        std::vector<uint16_t> xrow(K), wrow(K);
+        std::vector<float> refrow(N);
+        const int64_t cols[] = {0, N - 1, N / 2, N / 3, (N * 7) / 11};
+        for (size_t j = 0; j < rows.size(); ++j) {
+            HIP_TRY(hipMemcpy(xrow.data(), (char*)Xi + (size_t)rows[j] * K * 2, K * 2, hipMemcpyDeviceToHost));
+            HIP_TRY(hipMemcpy(refrow.data(), ref_i + j * N, N * 4, hipMemcpyDeviceToHost));
+            for (int64_t n : cols) {
+                HIP_TRY(hipMemcpy(wrow.data(), (char*)Wi + (size_t)n * K * 2, K * 2, hipMemcpyDeviceToHost));
+                int64_t acc = 0;
+                for (int64_t k = 0; k < K; ++k)
+                    acc += (int64_t)bf16_to_f(xrow[k]) * (int64_t)bf16_to_f(wrow[k]);
+                if ((float)acc != refrow[n])
+                    return set_error(PROJ_EDEVICE,
+                                     "reference kernel self-check failed at row %d col %lld: %g vs exact %lld",
+                                     rows[j], (long long)n, refrow[n], (long long)acc);
+            }
+        }
+        return PROJ_OK;
+    }
+
+    // Run candidate c at M rows on one probe, then compare against the reference.
+    int run_and_check(const Candidate& c, int64_t M, bool integer, int nrows, CheckStats* out)
+    {
+        int rc;
+        if ((rc = fill_sentinel(M + kGuardRows))) return rc;
+        HIP_TRY(hipMemsetAsync(stats_d, 0, sizeof(CheckStats), st));
+        if ((rc = launch_candidate(p, c, integer ? Xi : Xr, integer ? Wi : Wr, Y, M, st))) return rc;
+        const void* yp = Y;
+        long ra = (long)(M + kGuardRows);
+        int m = (int)M;
+        const float* r = integer ? ref_i : ref_r;
+        const int* rd = rows_d;
+        int ex = integer ? 1 : 0;
+        CheckStats* sd = stats_d;
+        void* args[] = {&yp, &ra, &m, &r, &rd, &nrows, &ex, &sd};
+        HIP_TRY(hipModuleLaunchKernel(f_check, 1024, 1, 1, 256, 1, 1, 0, st, args, nullptr));
+        HIP_TRY(hipMemcpyAsync(out, stats_d, sizeof(CheckStats), hipMemcpyDeviceToHost, st));
+        HIP_TRY(hipStreamSynchronize(st));
+        return PROJ_OK;
+    }
+
+    int flush_cache()
+    {
+        if (!flush) return PROJ_OK;
+        const void* fp = flush;
+        long n16 = (long)(flush_bytes / 16);
+        uint32_t never = 0x9E3779B9u;
+        uint32_t* sink = (uint32_t*)stats_d;  // written only if the XOR equals `never`
+        void* args[] = {&fp, &n16, &never, &sink};
+        HIP_TRY(hipModuleLaunchKernel(f_probe, 4096, 1, 1, 256, 1, 1, 0, st, args, nullptr));
+        return PROJ_OK;
+    }
+
+    // Median launch time in microseconds over `reps` launches at M rows.
+    int time_candidate(const Candidate& c, int64_t M, int reps, double* us)
+    {
+        int rc;
+        for (int i = 0; i < 2; ++i)
+            if ((rc = launch_candidate(p, c, Xr, Wr, Y, M, st))) return rc;
+        std::vector<double> t;
+        for (int i = 0; i < reps; ++i) {
+            if ((rc = flush_cache())) return rc;
+            HIP_TRY(hipEventRecord(e0, st));
+            if ((rc = launch_candidate(p, c, (i & 1) ? Xi : Xr, (i & 1) ? Wi : Wr, Y, M, st))) return rc;
+            HIP_TRY(hipEventRecord(e1, st));
+            HIP_TRY(hipEventSynchronize(e1));
+            float ms = 0;
+            HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+            t.push_back(ms * 1000.0);
+        }
+        std::sort(t.begin(), t.end());
+        *us = t[t.size() / 2];
+        return PROJ_OK;
+    }
+};
+
+static bool applies(const Candidate& c, int b, const proj_plan* p)
+{
+    const BucketRange br = kBuckets[b];
+    if (c.max_m < br.hi) return false;
+    if (c.ws_bytes(br.hi, p->N) > p->ws_bytes) return false;
+    switch (c.fam) {
+    case Family::GemvValu:
+        if (b == 0) return c.MMAX == 1;
+        return b == 1 && c.MMAX == 16;
+    case Family::GemvMfma: return b <= 1;
+    case Family::Gemm:
+        if (b <= 1) return false;
+        if (b == 2) return c.BM <= 128;
+        if (b == 3) return c.BM <= 256;
+        return c.BM >= 128 && c.SK <= 2;
+    case Family::Plain: return false;  // only as a last resort
+    }
+    return false;
+}
+
+static void plog(proj_plan* p, const std::string& line)
+{
+    p->log.push_back(line);
+    if (env_int("PROJ_LOG", 0)) fprintf(stderr, "%s\n", line.c_str());
+}
+
+int tune_plan(proj_plan* p)
+{
+    const double t0 = now_s();
+    const size_t ws_cap = (size_t)env_int("PROJ_WS_MB", 256) << 20;
+    const bool do_time = env_int("PROJ_TUNE", 1) != 0;
+    const int reps = std::max(3, env_int("PROJ_TUNE_REPS", 10));
+    const char* force = getenv("PROJ_FORCE");
+
+    // split-K workspace: enough for every split-K candidate at the largest block,
+    // capped; a candidate then runs up to the row count the workspace holds.
+    size_t need = 0;
+    for (const Candidate& c : p->cands) need = std::max(need, c.ws_bytes(kMaxBlockRows, p->N));
+    need = std::min(need, ws_cap);
+    if (need) {
+        if (hipMalloc(&p->ws, need) != hipSuccess)
+            return set_error(PROJ_ENOMEM, "split-K workspace of %zu bytes", need);
+        p->ws_bytes = need;
+    }
+
+    Tuner T;
+    T.p = p;
+    int rc;
+    if ((rc = T.setup(kBuckets[kNumBuckets - 1].hi))) return rc;
+
+    p->timings.assign(kNumBuckets, {});
+    p->rejected.assign(kNumBuckets, {});
+    bool ref_checked = false;
+    char line[1024];
+    for (int b = 0; b < kNumBuckets; ++b) {
+        const BucketRange br = kBuckets[b];
+        const int64_t Mfull = br.hi;
+        const int64_t Mpart = br.lo == br.hi ? br.hi : br.hi - 1;
+        const int64_t Modd = br.lo == br.hi ? br.hi : std::min<int64_t>(br.hi, br.lo + ((br.hi - br.lo) / 3 | 1));
+        std::vector<int64_t> tests = {Mfull, Mpart, Modd};
+        std::sort(tests.begin(), tests.end());
+        tests.erase(std::unique(tests.begin(), tests.end()), tests.end());
+        std::vector<int> rows = {0, (int)(Mfull - 1), (int)(Mpart - 1), (int)(Modd - 1), (int)(Modd / 2),
+                                 (int)std::min<int64_t>(Mfull - 1, 31), (int)std::min<int64_t>(Mfull - 1, 32),
+                                 (int)(Mfull / 2)};
+        std::sort(rows.begin(), rows.end());
+        rows.erase(std::unique(rows.begin(), rows.end()), rows.end());
+        if ((rc = T.reference(rows))) return rc;
+        if (!ref_checked) {
+            if ((rc = T.self_check_reference(rows))) return rc;
+            ref_checked = true;
+        }
+        const int nrows = (int)rows.size();
+
+        std::vector<int> ok;
+        auto validate = [&](int ci) -> int {
+            const Candidate& c = p->cands[ci];
+            for (int64_t M : tests) {
+                for (int integer = 0; integer < 2; ++integer) {
+                    if (integer && M != Mpart) continue;
+                    CheckStats cs{};
+                    int r2 = T.run_and_check(c, M, integer != 0, nrows, &cs);
+                    if (r2) return r2;
+                    if (cs.bad || cs.unwritten || cs.guard) {
+                        snprintf(line, sizeof line,
+                                 "[autotune] proj %lldx%lld %lld rows at %lld: wrong against ref, never picked: %s "
+                                 "(%lld rows%s: max err %.3e of %.3e; %u outside tolerance, %u unwritten, %u "
+                                 "written past M)",
+                                 (long long)p->N, (long long)p->K, (long long)br.hi, (long long)br.hi,
+                                 c.name.c_str(), (long long)M, integer ? ", integer probe" : "",
+                                 bits_f(cs.max_err), bits_f(cs.max_ref), cs.bad, cs.unwritten, cs.guard);
+                        plog(p, line);
+                        p->rejected[b].push_back({ci, line});
+                        return 1;
+                    }
+                }
+            }
+            return 0;
+        };
+
+        for (int ci = 0; ci < (int)p->cands.size(); ++ci) {
+            const Candidate& c = p->cands[ci];
+            if (!applies(c, b, p)) continue;
+            if (force && *force && c.name != force) continue;
+            int v = validate(ci);
+            if (v < 0) return v;
+            if (v == 0) ok.push_back(ci);
+        }
+        if (ok.empty()) {
+            // last resort: the plain kernel
+            const int pi = (int)p->cands.size() - 1;
+            int v = validate(pi);
+            if (v < 0) return v;
+            if (v) return set_error(PROJ_ENOCAND, "no candidate passed validation for %lld..%lld rows",
+                                    (long long)br.lo, (long long)br.hi);
+            ok.push_back(pi);
+        }
+
+        int best = ok[0];
+        double best_us = -1;
+        if (do_time && ok.size() > 1) {
+            std::string tl;
+            for (int ci : ok) {
+                double us = 0;
+                if ((rc = T.time_candidate(p->cands[ci], Mfull, reps, &us))) return rc;
+                p->timings[b].push_back({ci, us});
+                if (best_us < 0 || us < best_us) {
+                    best_us = us;
+                    best = ci;
+                }
+            }
+            std::ostringstream os;
+            os << "[autotune] proj " << p->N << "x" << p->K << " " << br.lo << ".." << br.hi << " rows at "
+               << Mfull << ":";
+            for (size_t i = 0; i < p->timings[b].size(); ++i) {
+                char t[64];
+                snprintf(t, sizeof t, " %.3f us", p->timings[b][i].second);
+                os << (i ? "," : "") << " " << p->cands[p->timings[b][i].first].name
+                   << (p->timings[b][i].first == best ? "*" : "") << t;
+            }
+            os << " -> " << p->cands[best].name;
+            plog(p, os.str());
+        } else {
+            snprintf(line, sizeof line, "[autotune] proj %lldx%lld %lld..%lld rows: %s (validated, not timed)",
+                     (long long)p->N, (long long)p->K, (long long)br.lo, (long long)br.hi,
+                     p->cands[best].name.c_str());
+            plog(p, line);
+        }
+        p->choice[b] = best;
+        p->choice_us[b] = best_us;
+    }
+    p->tune_s = now_s() - t0;
+    return PROJ_OK;
+}
+
+int create_plan(int64_t N, int64_t K, int dtype, proj_plan** out)
+{
+    *out = nullptr;
+    if (N < 1 || K < 8 || K % 8 != 0 || N > (int64_t)1 << 30 || K > (int64_t)1 << 24)
+        return set_error(PROJ_EINVAL, "invalid shape N=%lld K=%lld (need N >= 1, K >= 8, K %% 8 == 0)",
+                         (long long)N, (long long)K);
+    if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16)
+        return set_error(PROJ_EINVAL, "invalid dtype %d (PROJ_OUT_F32=0 or PROJ_OUT_BF16=1)", dtype);
+    std::unique_ptr<proj_plan> p(new proj_plan());
+    p->N = N;
+    p->K = K;
+    p->dtype = dtype;
+    HIP_TRY(hipGetDevice(&p->device));
+    int rc;
+    if ((rc = device_arch(p->device, &p->arch, nullptr))) return rc;
+    for (int b = 0; b < kNumBuckets; ++b) p->choice[b] = -1, p->choice_us[b] = -1;
+
+    p->cands = enumerate_candidates(N, K);
+    const std::string src = emit_source(N, K, dtype, p->arch, p->cands);
+    const double t0 = now_s();
+    std::shared_ptr<std::vector<char>> code;
+    char name[96];
+    snprintf(name, sizeof name, "proj_%lldx%lld_%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32");
+    if ((rc = compile_source(src, p->arch, name, &code))) return rc;
+    p->compile_s = now_s() - t0;
+    p->code_bytes = code->size();
+    if (const char* dir = getenv("PROJ_DUMP_DIR")) {
+        if (*dir) {
+            std::string base = std::string(dir) + "/" + name;
+            std::ofstream(base, std::ios::binary) << src;
+            std::ofstream(base + "." + p->arch + ".co", std::ios::binary).write(code->data(), code->size());
+        }
+    }
+    HIP_TRY(hipModuleLoadData(&p->module, code->data()));
+    for (Candidate& c : p->cands) {
+        HIP_TRY(hipModuleGetFunction(&c.fn, p->module, c.name.c_str()));
+        if (!c.reduce_name.empty()) HIP_TRY(hipModuleGetFunction(&c.reduce_fn, p->module, c.reduce_name.c_str()));
+    }
+    char line[256];
+    snprintf(line, sizeof line, "[proj] %lldx%lld %s: %zu candidates compiled for %s in %.2f s (%zu bytes)",
+             (long long)N, (long long)K, dtype ? "bf16" : "f32", p->cands.size(), p->arch.c_str(), p->compile_s,
+             p->code_bytes);
+    plog(p.get(), line);
+    if ((rc = tune_plan(p.get()))) {
+        if (p->ws) (void)hipFree(p->ws);
+        if (p->module) (void)hipModuleUnload(p->module);
+        return rc;
+    }
+    snprintf(line, sizeof line, "[proj] %lldx%lld: tuned %d row buckets in %.2f s", (long long)N, (long long)K,
+             kNumBuckets, p->tune_s);
+    plog(p.get(), line);
+    *out = p.release();
+    return PROJ_OK;
+}
+
+void destroy_plan(proj_plan* p)
+{
+    if (!p) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != p->device) (void)hipSetDevice(p->device);
+    if (p->ws) (void)hipFree(p->ws);
+    if (p->module) (void)hipModuleUnload(p->module);
+    if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
+    delete p;
+}
+
+int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M)
+{
+    if (!p) return set_error(PROJ_EINVAL, "plan is NULL");
+    if (M < 0) return set_error(PROJ_EINVAL, "M=%lld is negative", (long long)M);
+    if (M == 0) return PROJ_OK;
+    if (!X || !W || !Y) return set_error(PROJ_EINVAL, "null pointer (X=%p W=%p Y=%p)", X, W, (void*)Y);
+    if (((uintptr_t)X | (uintptr_t)W | (uintptr_t)Y) & 15)
+        return set_error(PROJ_EINVAL, "X, W and Y must be 16-byte aligned (X=%p W=%p Y=%p)", X, W, (void*)Y);
+    int cur = -1;
+    HIP_TRY(hipGetDevice(&cur));
+    if (cur != p->device)
+        return set_error(PROJ_EINVAL, "current device %d is not the plan's device %d", cur, p->device);
+    return PROJ_OK;
+}
+
+int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream)
+{
+    int rc = check_run_args(p, X, W, Y, M);
+    if (rc || M == 0) return rc;
+    const size_t ysz = p->dtype == PROJ_OUT_BF16 ? 2 : 4;
+    for (int64_t off = 0; off < M; off += kMaxBlockRows) {
+        const int64_t m = std::min<int64_t>(kMaxBlockRows, M - off);
+        const Candidate& c = p->cands[p->choice[bucket_of(m)]];
+        rc = launch_candidate(p, c, (const char*)X + (size_t)off * p->K * 2, W, (char*)Y + (size_t)off * p->N * ysz,
+                              m, stream);
+        if (rc) return rc;
+    }
+    return PROJ_OK;
+}
+
+}  // namespace proj

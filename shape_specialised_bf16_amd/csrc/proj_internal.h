@@ -1,0 +1,83 @@
+// proj_internal.h -- host-side structures of libproj (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace proj {
+
+// Row buckets of the tuner: each bucket gets its own validated, timed choice.
+// Every configured M in the workloads is a bucket's upper end.
+struct BucketRange {
+    int64_t lo, hi;
+};
+constexpr int kNumBuckets = 7;
+constexpr BucketRange kBuckets[kNumBuckets] = {
+    {1, 1}, {2, 16}, {17, 128}, {129, 512}, {513, 1024}, {1025, 2048}, {2049, 8192}};
+constexpr int64_t kMaxBlockRows = 8192;  // proj_run splits larger M into blocks of this size
+
+enum class Family { GemvValu, GemvMfma, Gemm, Plain };
+
+struct Candidate {
+    Family fam = Family::Plain;
+    // GEMV parameters
+    int R = 1, S = 1, MMAX = 1, U = 1, NT = 1;
+    // GEMM parameters
+    int BM = 0, BN = 0, WM = 0, WN = 0, SK = 1, GM = 8;
+
+    std::string name;          // extern "C" wrapper name in the generated module
+    std::string reduce_name;   // split-K reduce kernel (empty if SK == 1)
+    int threads = 256;
+    int64_t max_m = kMaxBlockRows;
+    hipFunction_t fn = nullptr;
+    hipFunction_t reduce_fn = nullptr;
+
+    bool needs_ws() const { return fam == Family::Gemm && SK > 1; }
+    size_t ws_bytes(int64_t M, int64_t N) const
+    {
+        return needs_ws() ? (size_t)SK * (size_t)M * (size_t)N * sizeof(float) : 0;
+    }
+};
+
+// Enumerate the candidates that tile (N, K) exactly.  Always ends with the
+// plain kernel, which fits any shape.
+std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K);
+
+// The full translation unit for (N, K, dtype): prelude with the shape as
+// literals, device helpers, kernel templates, one wrapper per candidate.
+std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch,
+                        const std::vector<Candidate>& cands);
+
+// Shape-independent support module (probe, rounding check).
+std::string emit_support_source();
+
+// Embedded device sources (generated from the .hip files at build time).
+extern const char* const kDeviceCommonSrc;
+extern const char* const kKernelsSrc;
+extern const char* const kSupportSrc;
+
+// Bucket index for M >= 1 (M > kMaxBlockRows maps to the last bucket).
+int bucket_of(int64_t M);
+
+}  // namespace proj
+
+struct proj_plan {
+    int64_t N = 0, K = 0;
+    int dtype = 0;
+    int device = -1;
+    std::string arch;
+    hipModule_t module = nullptr;
+    std::vector<proj::Candidate> cands;
+    int choice[proj::kNumBuckets];
+    double choice_us[proj::kNumBuckets];
+    std::vector<std::vector<std::pair<int, double>>> timings;  // per bucket: (cand, us)
+    std::vector<std::vector<std::pair<int, std::string>>> rejected;  // per bucket: (cand, why)
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    double compile_s = 0, tune_s = 0;
+    size_t code_bytes = 0;
+    std::vector<std::string> log;
+};

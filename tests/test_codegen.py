@@ -1,0 +1,105 @@
+"""Emitted-source checks (no GPU): the shape appears as literals, every emitted
+candidate tiles the shape exactly, and the source compiles for gfx950."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import shape_specialised_bf16_amd as ssb
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden():
+    gpu, cpu = [], []
+    for line in open(os.path.join(HERE, "golden", "pages_emitted_constants.txt")):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        if line[0] == "gpu":
+            gpu.append(tuple(int(v) for v in line[1:]))
+        else:
+            cpu.append((int(line[1]), int(line[2], 16), None if line[3] == "-" else int(line[3], 16)))
+    return gpu, cpu
+
+
+@pytest.mark.parametrize("row", _golden()[0])
+def test_pages_gpu_module_constants_appear_as_literals(row):
+    """The pages' decode module for (N, K) carries N, K/8 and N-1 as constants;
+    the emitted HIP source carries the same values as literals."""
+    N, K, blocks16, last = row
+    assert blocks16 == K // 8 and last == N - 1          # the fixture is self-consistent
+    src = ssb.emit_source(N, K, "f32")
+    assert re.search(rf"constexpr long N = {N};", src)
+    assert re.search(rf"constexpr long K = {K};", src)
+    assert re.search(rf"constexpr long K_BLOCKS16 = {blocks16};", src)
+    assert re.search(rf"constexpr long N_LAST = {last};", src)
+    assert re.search(rf"constexpr long ROW_BYTES = {2 * K};", src)
+
+
+@pytest.mark.parametrize("row", _golden()[1])
+def test_trip_counts_and_block_strides_are_literals(row):
+    """The pages' x86 loop has its trip count (K/2) and the 16-row block stride
+    (16*K*2 bytes) as immediates.  Here: each candidate's trip count is a
+    literal checked by a static_assert, and the 16-row weight block stride
+    appears in the MFMA GEMV candidates' description."""
+    K, trips_x86, stride = row
+    assert trips_x86 == K // 2
+    src = ssb.emit_source(18432 if K == 2560 else 7168, K, "f32")
+    # vector GEMV: K/8 blocks over 64 lanes
+    assert f"static_assert(K_BLOCKS16 / 1 / 64 == {K // 8 // 64}, \"trip count\");" in src
+    # MFMA GEMV: K / (32*U) batches
+    assert f"static_assert(K / 1 / 128 == {K // 128}, \"trip count\");" in src
+    assert f"next 16-row weight block at +{32 * K} B" in src
+    if stride is not None:
+        assert stride == 32 * K
+
+
+def test_no_runtime_shape_arguments():
+    """Every candidate wrapper takes only pointers and M: no run-time N or K."""
+    src = ssb.emit_source(5120, 2560, "bf16")
+    sigs = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void (gemv_\w+|gemm_\w+)(\([^)]*\))', src)
+    assert len(sigs) >= 10
+    for name, sig in sigs:
+        assert sig == ("(const u16* __restrict__ X, const u16* __restrict__ W, void* __restrict__ Y, "
+                       "float* __restrict__ ws, int M)"), name
+
+
+@pytest.mark.parametrize("N,K", [(2048, 1024), (151936, 1024), (5120, 2560), (2560, 9216),
+                                 (34816, 5120), (5120, 17408), (1000, 520), (24, 8)])
+def test_candidates_tile_the_shape(N, K):
+    src = ssb.emit_source(N, K, "f32")
+    names = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\(', src)
+    assert "gemm_plain" in names
+    for n in names:
+        m = re.match(r"gemv_valu_r(\d+)_s(\d+)_m(\d+)_u(\d+)_nt(\d)", n)
+        if m:
+            R, S, MM, U, _ = map(int, m.groups())
+            assert (K // 8) % S == 0 and N % (R * (4 // S)) == 0
+            trips = K // 8 // S // 64
+            assert trips % U == 0 or trips == 0
+            continue
+        m = re.match(r"gemv_mfma_s(\d+)_u(\d+)_nt(\d)", n)
+        if m:
+            S, U, _ = map(int, m.groups())
+            assert N % (16 * (4 // S)) == 0 and K % (32 * U * S) == 0
+            continue
+        m = re.match(r"gemm_(\d+)x(\d+)_w(\d+)x(\d+)_sk(\d+)_g(\d+)", n)
+        if m:
+            BM, BN, WM, WN, SK, _ = map(int, m.groups())
+            assert N % BN == 0 and K % (64 * SK) == 0
+            continue
+        assert n == "gemm_plain", n
+
+
+def test_emitted_source_compiles_for_gfx950(tmp_path):
+    """A device-code build check: the emitted unit for an odd shape (tails in K,
+    few candidates) compiles with hipcc for gfx950."""
+    src = ssb.emit_source(1000, 520, "bf16")
+    f = tmp_path / "proj_1000x520.hip"
+    f.write_text(src)
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-device-only", "-c", "-O3",
+                        "-std=c++17", "-include", "hip/hip_runtime.h", str(f), "-o", str(f) + ".o"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]

@@ -1,0 +1,159 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Inputs follow the seeded recipe of ``synth``; tolerances are those of
+``oracle.tolerance``.  Large shapes are compared on sampled rows (first, last,
+tile boundaries, random), small ones in full.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ single projection
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [1, 16])
+def test_single_projection_1024(M, dtype):
+    cfg = synth.CONFIGS[0]
+    W = synth.weights(cfg, 0)
+    X = synth.activations(cfg, 0, M)
+    p = G.plan(1024, 1024, dtype)
+    Y = G.empty_out(M, 1024, dtype, extra_rows=2)
+    p.run(G.dev(X), G.dev(W), Y)
+    G.check_against_oracle(Y, X, W, dtype, label=f"1024x1024 {p.choice(M)}")
+    tail = G.host(Y)[M:]
+    pat = 0x7FC1 if dtype == "bf16" else 0x7FC00001
+    assert np.all(tail.view(np.uint16 if dtype == "bf16" else np.uint32) == pat), "rows past M were written"
+
+
+# ------------------------------------------------------------------ the pages' own decode shape
+@pytest.mark.parametrize("M", [1, 3, 16, 100])
+def test_pages_gate_up_shape_7168x1024(M):
+    pr = synth.PAGES_GATE_UP_08B
+    W = synth.normal_bf16(50, 0, (pr.N, pr.K), 0.02)
+    X = synth.normal_bf16(50, 1 + M, (M, pr.K), 1.0)
+    p = G.plan(pr.N, pr.K, "f32")
+    Y = p.run(G.dev(X), G.dev(W))
+    G.check_against_oracle(Y, X, W, "f32", label=f"7168x1024 {p.choice(M)}")
+
+
+# ------------------------------------------------------------------ odd shape: no MFMA tile fits
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 300])
+def test_odd_shape_1000x520(M):
+    W = synth.normal_bf16(51, 0, (1000, 520), 0.02)
+    X = synth.normal_bf16(51, 1 + M, (M, 520), 1.0)
+    p = G.plan(1000, 520, "bf16")
+    Y = p.run(G.dev(X), G.dev(W))
+    G.check_against_oracle(Y, X, W, "bf16", label=f"1000x520 {p.choice(M)}")
+
+
+# ------------------------------------------------------------------ every candidate, exact integers
+@pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16"), (1000, 520, "f32")])
+def test_every_candidate_bit_exact_on_integer_probe(N, K, dtype):
+    """With integer inputs in [-4, 4] every summation order is exact, so every
+    compiled candidate -- not only the tuned winners -- must reproduce the
+    oracle bit for bit, at full, partial and odd row counts."""
+    p = G.plan(N, K, dtype)
+    W = synth.int_bf16(60, (N, K))
+    Xall = synth.int_bf16(61, (600, K))
+    Wd = G.dev(W)
+    exact = oracle.matmul(Xall, W)
+    want = oracle.round_bf16(exact) if dtype == "bf16" else oracle.round_f32(exact)
+    for idx, name in enumerate(p.candidates()):
+        mmax = p.candidate_max_m(idx)
+        Ms = [1, 5, 16] if mmax <= 16 else [1, 17, 130, 600]
+        for M in [m for m in Ms if m <= mmax]:
+            Y = G.empty_out(M, N, dtype, extra_rows=1)
+            p.run_candidate(idx, G.dev(Xall[:M]), Wd, Y)
+            got = G.host(Y)
+            assert np.array_equal(got[:M].view(np.uint8), want[:M].view(np.uint8)), f"{name} M={M}"
+            assert np.all(got[M:].view(np.uint8) == G.host(G.empty_out(1, N, dtype))[0:1].view(np.uint8)), \
+                f"{name} wrote past M={M}"
+        G.log(f"  {N}x{K} {dtype} {name}: bit-exact")
+
+
+@pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16")])
+def test_every_candidate_within_tolerance_on_random_inputs(N, K, dtype):
+    p = G.plan(N, K, dtype)
+    W = synth.normal_bf16(62, 0, (N, K), 0.02)
+    X = synth.normal_bf16(62, 1, (300, K), 1.0)
+    Wd = G.dev(W)
+    ref = oracle.matmul(X, W)
+    for idx, name in enumerate(p.candidates()):
+        M = min(p.candidate_max_m(idx), 300)
+        Y = p.run_candidate(idx, G.dev(X[:M]), Wd)
+        rep = G.compare(G.host(Y), ref[:M], dtype)
+        assert rep.ok, f"{name}: {rep}"
+
+
+def test_plan_describe_and_no_rejections():
+    """Every bucket has a choice; no candidate of a regular shape is rejected by
+    the load-time gate (a rejection would mean a wrong kernel was compiled)."""
+    p = G.plan(7168, 1024, "f32")
+    d = p.describe()
+    assert d["N"] == 7168 and d["K"] == 1024 and d["arch"].startswith("gfx9")
+    assert len(d["buckets"]) == 7
+    for b in d["buckets"]:
+        assert b["choice"], b
+        assert not b["rejected"], b
+    assert any("[autotune]" in line for line in d["log"])
+
+
+def test_determinism_and_nondefault_stream():
+    import torch
+    N, K = 6144, 1024
+    W = synth.normal_bf16(63, 0, (N, K), 0.02)
+    X = synth.normal_bf16(63, 1, (200, K), 1.0)
+    p = G.plan(N, K, "f32")
+    Wd, Xd = G.dev(W), G.dev(X)
+    for M in (1, 16, 200):
+        a = p.run(Xd[:M], Wd)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            b = p.run(Xd[:M], Wd, stream=s)
+        s.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"M={M} not bitwise reproducible"
+
+
+def test_large_m_is_processed_in_blocks():
+    """M above 8192 runs as consecutive blocks of 8192 rows."""
+    N, K = 1024, 1024
+    W = synth.normal_bf16(64, 0, (N, K), 0.02)
+    X = synth.normal_bf16(64, 1, (8192 + 300, K), 1.0)
+    p = G.plan(N, K, "f32")
+    Y = G.empty_out(X.shape[0], N, "f32", extra_rows=1)
+    p.run(G.dev(X), G.dev(W), Y)
+    rows = G.sample_rows(X.shape[0], extra=(8191, 8192, 8193, 8491))
+    G.check_against_oracle(Y, X, W, "f32", rows=rows, label="1024x1024 M=8492")
+    assert np.all(G.host(Y)[X.shape[0]:].view(np.uint32) == 0x7FC00001)
+
+
+def test_m_zero_is_a_no_op():
+    p = G.plan(1024, 1024, "f32")
+    import torch
+    X = torch.zeros((0, 1024), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((1024, 1024), dtype=torch.bfloat16, device="cuda")
+    Y = p.run(X, W)
+    assert Y.shape == (0, 1024)
+
+
+def test_wrong_arguments_are_rejected():
+    import torch
+    from shape_specialised_bf16_amd import ProjError
+    p = G.plan(1024, 1024, "f32")
+    X = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((1024, 1024), dtype=torch.bfloat16, device="cuda")
+    Y = torch.zeros((4, 1024), dtype=torch.float32, device="cuda")
+    with pytest.raises(ProjError, match="aligned"):
+        p.run_ptr(X.data_ptr() + 2, W.data_ptr(), Y.data_ptr(), 4, None)
+    with pytest.raises(ProjError, match="negative"):
+        p.run_ptr(X.data_ptr(), W.data_ptr(), Y.data_ptr(), -1, None)
+    with pytest.raises(ProjError, match="null"):
+        p.run_ptr(0, W.data_ptr(), Y.data_ptr(), 4, None)
+    with pytest.raises(ValueError):
+        p.run(X, W[:512])

@@ -24,7 +24,6 @@ Progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,17 +41,11 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
-    h = hashlib.sha256()
-    for f in ("device_common.hip", "kernels.hip"):
-        with open(os.path.join(ROOT, "shape_specialised_bf16_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-def traffic_for(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+def traffic_for(key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy kernel of known size), if they were taken on
+    the current kernel source; else None."""
+    from shape_specialised_bf16_amd.profile_summary import kernel_source_sha
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -60,10 +53,42 @@ def traffic_for(kernel: str):
         d = json.load(open(path))
     except Exception:
         return None
-    e = d.get(kernel)
-    if not e or e.get("source_sha") != kernel_source_sha():
+    e = d.get(key)
+    if not e or e.get("source_sha") != kernel_source_sha(key.split("@")[0]):
         return None
-    return e.get("bytes_per_launch")
+    return round(e["bytes_per_launch"])
+
+
+def profile_mode(which: str, launches: int = 30):
+    """Only the dominant kernel of one bench leg at its bench configuration --
+    the decode head GEMV (151936x1024, M=1, f32 out, rotating weight copies) or
+    the prefill gate/up GEMM (18432x2560, M=2048, bf16 out) -- then a 1 GiB
+    device copy of known size that calibrates the FETCH_SIZE / WRITE_SIZE
+    counters; for rocprofv3 counter runs."""
+    import torch
+
+    import synth
+    from shape_specialised_bf16_amd import Plan
+
+    if which == "decode":
+        cfg, pi, M, dt = synth.CONFIGS[1], len(synth.CONFIGS[1].projections) - 1, 1, "f32"
+    else:
+        cfg, pi, M, dt = synth.CONFIGS[2], 2, 2048, "bf16"
+    p = cfg.projections[pi]
+    plan = Plan(p.N, p.K, dt)
+    W = upload(synth.weights(cfg, pi))
+    X = upload(synth.activations(cfg, pi, M))
+    Y = torch.empty((M, p.N), dtype=plan.out_dtype, device="cuda")
+    copies = [W] + [W.clone() for _ in range(4 if which == "decode" else 0)]
+    for i in range(launches if which == "decode" else 10):
+        plan.run(X, copies[i % len(copies)], Y)
+    torch.cuda.synchronize()
+    a = torch.ones(1 << 29, dtype=torch.int16, device="cuda")      # 1 GiB
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"profile mode: {plan.choice(M)} on {p.N}x{p.K} M={M}, then 3 x 1 GiB copy")
 
 
 def upload(a):
@@ -122,11 +147,23 @@ def time_decode(steps: int, warmup: int):
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
-    head_us = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+    in_step_us = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
     ms_per_step = ms_total / steps
+    # The head alone, back to back on the same stream (rotating weight copies):
+    # with no other kernel between launches the event pair brackets kernel time
+    # plus the per-launch dispatch gap only.
+    reps = 100
+    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0.record(stream)
+    for s in range(reps):
+        plans[head].run_ptr(Xs[head].data_ptr(), Wrot[head][s % copies].data_ptr(), Ys[head].data_ptr(), 1, sh)
+    h1.record(stream)
+    torch.cuda.synchronize()
+    head_us = h0.elapsed_time(h1) / reps * 1e3
     # correctness of what was timed: the last step's head output vs the oracle (sampled)
     return dict(plans=plans, projs=projs, host=host, Ys=Ys, step_bytes=step_bytes, ms_per_step=ms_per_step,
-                head_us=head_us, head_bytes=head_bytes, head_kernel=plans[head].choice(1), copies=copies)
+                head_us=head_us, in_step_us=in_step_us, head_bytes=head_bytes,
+                head_kernel=plans[head].choice(1), copies=copies)
 
 
 def time_prefill(reps: int = 20):
@@ -164,9 +201,12 @@ def time_prefill(reps: int = 20):
         out[f"M{M}"] = dict(value=round(flops / tot_us / 1e6, 1), unit="TFLOP/s",
                             pct_peak=round(100 * flops / tot_us / 1e6 / MFMA_BF16_PEAK_TFS, 1),
                             layer_us=round(tot_us, 2), projections=per,
-                            roofline=dict(bound="mfma", kernel=dom["kernel"], achieved=dom["tflops"],
-                                          peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
-                                          frac=round(dom["tflops"] / MFMA_BF16_PEAK_TFS, 4)))
+                            roofline=dict(bound="mfma", kernel=dom["kernel"], shape=f"{dom['N']}x{dom['K']}",
+                                          achieved=dom["tflops"], peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                                          frac=round(dom["tflops"] / MFMA_BF16_PEAK_TFS, 4),
+                                          mean_launch_us=dom["us"],
+                                          traffic=traffic_for(f"{dom['kernel']}@{dom['N']}x{dom['K']}m{M}"),
+                                          algorithmic_bytes=2 * (M * dom["K"] + dom["N"] * dom["K"] + M * dom["N"])))
         log(f"  prefill M={M}: {out[f'M{M}']['value']} TFLOP/s over the layer ({tot_us:.1f} us)")
     for p in plans:
         p.close()
@@ -216,13 +256,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--mode", default="full", choices=["full", "profile-decode", "profile-prefill"],
+                    help="profile-*: only that leg's dominant kernel and a calibration copy, for rocprofv3 "
+                         "counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the projection shards "
               "by output rows across GPUs but no multi-GPU path is built", file=sys.stderr)
         sys.exit(2)
+    if args.mode != "full":
+        profile_mode(args.mode.split("-")[1])
+        return
 
-    import numpy as np
     import torch
 
     import oracle
@@ -274,6 +319,8 @@ def main():
             "traffic": traffic_for(d["head_kernel"] + "@151936x1024"),
             "bytes_per_launch": d["head_bytes"],
             "mean_launch_us": round(d["head_us"], 3),
+            "timing": "HIP events around 100 back-to-back launches on the launch stream, after the timed steps",
+            "in_step_launch_us": round(d["in_step_us"], 3),
         },
     }
     for p in d["plans"]:

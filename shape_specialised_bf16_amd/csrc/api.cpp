@@ -199,7 +199,8 @@ int proj_probe_read(const void* buf, int64_t bytes, uint32_t never, void* sink, 
     uint32_t nv = never;
     void* s = sink;
     void* args[] = {&p, &n16, &nv, &s};
-    const unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * 16, (n16 + 255) / 256));
+    (void)cus;
+    const unsigned gx = (unsigned)((n16 + 2047) / 2048);  // one 32 KiB span per block
     hipError_t e = hipModuleLaunchKernel(sm->probe, gx, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
     if (e != hipSuccess) return set_error(PROJ_EDEVICE, "probe launch: %s", hipGetErrorString(e));
     return PROJ_OK;

@@ -41,7 +41,9 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K)
 
     // ---- vector-ALU GEMV: (R rows per wave, S waves splitting K), MMAX rows of X
     struct VG { int R, S, MMAX, NT; };
-    const VG vgs[] = {{1, 1, 1, 1}, {2, 1, 1, 1}, {4, 1, 1, 1}, {2, 1, 1, 0},
+    // (listed in order of preference: the tuner keeps an earlier candidate unless
+    //  a later one is clearly faster)
+    const VG vgs[] = {{2, 1, 1, 1}, {1, 1, 1, 1}, {4, 1, 1, 1}, {2, 1, 1, 0},
                       {1, 4, 1, 1}, {2, 4, 1, 1}, {1, 1, 16, 1}, {2, 1, 16, 1}, {1, 4, 16, 1}};
     for (const VG& v : vgs) {
         if (CH % v.S) continue;
@@ -77,21 +79,35 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K)
         }
     }
 
-    // ---- MFMA GEMM: block tile BM x BN (k step 64), WM x WN waves, split-K SK
-    struct GT { int BM, BN, WM, WN; };
-    const GT gts[] = {{256, 256, 2, 2}, {256, 128, 2, 2}, {128, 256, 2, 2}, {128, 128, 2, 2},
-                      {64, 128, 1, 2}, {64, 64, 1, 1}};
+    // ---- MFMA GEMM: block tile BM x BN, k-tile BK, ST LDS buffers, WM x WN waves,
+    //      LDS swizzle period SWZ, split-K SK (only for the smaller tiles).
+    //      gfx950's LDS serves a 16-byte-per-lane read 16 lanes (256 bytes, all 64
+    //      banks) at a time, so the 16 rows one operand read touches must land on
+    //      distinct bank groups: XOR period 2 rows for 128-byte rows (BK = 64),
+    //      4 rows for 64-byte rows (BK = 32).
+    struct GT { int BM, BN, BK, ST, WM, WN, SWZ; int maxSK; int GM = 8; };
+    const GT gts[] = {
+        {256, 256, 64, 2, 2, 4, 1, 1}, {256, 256, 64, 2, 2, 4, 1, 1, 4}, {256, 256, 64, 2, 2, 4, 1, 1, 16},
+        {256, 256, 64, 2, 4, 2, 1, 1}, {256, 256, 32, 4, 2, 4, 2, 1},  {256, 256, 32, 3, 2, 4, 2, 1},
+        {256, 128, 64, 3, 4, 2, 1, 1, 4}, {128, 256, 64, 3, 2, 4, 1, 1, 4},
+        {256, 128, 32, 2, 2, 2, 2, 2}, {128, 256, 32, 2, 2, 2, 2, 2},
+        {128, 128, 64, 2, 2, 2, 1, 4}, {128, 128, 32, 3, 2, 2, 2, 4},
+        {64, 128, 64, 2, 1, 2, 1, 4}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
+        const int cpr = g.BK / 8, rpi = 64 * g.WM * g.WN / cpr;
+        if ((rpi >> g.SWZ) % cpr) continue;  // the copy slots' swizzled column must not vary per copy
         for (int SK : {1, 2, 4}) {
-            if (K % (64 * SK)) continue;
-            if (SK > 1 && g.BM * g.BN > 128 * 256) continue;  // big tiles never need split-K
+            if (SK > g.maxSK) continue;
+            if (K % (g.BK * SK)) continue;
             Candidate c;
             c.fam = Family::Gemm;
-            c.BM = g.BM; c.BN = g.BN; c.WM = g.WM; c.WN = g.WN; c.SK = SK; c.GM = 8;
+            c.BM = g.BM; c.BN = g.BN; c.BK = g.BK; c.ST = g.ST; c.WM = g.WM; c.WN = g.WN;
+            c.SK = SK; c.GM = g.GM; c.SWZ = g.SWZ;
             c.threads = 64 * g.WM * g.WN;
             c.max_m = kMaxBlockRows;
-            c.name = fmt("gemm_%dx%d_w%dx%d_sk%d_g%d", c.BM, c.BN, c.WM, c.WN, c.SK, c.GM);
+            c.name = fmt("gemm_%dx%dx%d_st%d_w%dx%d_sw%d_g%d_sk%d", c.BM, c.BN, c.BK, c.ST, c.WM, c.WN, c.SWZ, c.GM,
+                         c.SK);
             if (SK > 1) c.reduce_name = fmt("splitk_reduce_sk%d", SK);
             out.push_back(c);
         }
@@ -131,7 +147,10 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
     s << "constexpr long N_LAST = " << N - 1 << ";       // last output row index\n";
     s << "constexpr long ROW_BYTES = " << 2 * K << ";    // stride between weight rows\n\n";
     s << kDeviceCommonSrc << "\n";
-    s << kKernelsSrc << "\n";
+    s << kKernelsHeadSrc << "\n";
+    s << kGemvSrc << "\n";
+    s << kGemmSrc << "\n";
+    s << kGateSrc << "\n";
     s << kSupportSrc << "\n";
     s << "// ===================== candidates for this shape =====================\n";
     bool reduce_emitted[5] = {false, false, false, false, false};
@@ -161,14 +180,15 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
             break;
         }
         case Family::Gemm: {
-            const int64_t kt = K / c.SK / 64;
-            s << "// " << c.name << ": " << c.BM << "x" << c.BN << " tile, " << c.WM * c.WN
-              << " waves, K split " << c.SK << " ways, " << kt << " k-tile(s) of 64, " << N / c.BN
-              << " tile column(s)\n";
-            s << "static_assert(K / " << c.SK << " / 64 == " << kt << ", \"trip count\");\n";
+            const int64_t kt = K / c.SK / c.BK;
+            s << "// " << c.name << ": " << c.BM << "x" << c.BN << " tile, " << c.WM * c.WN << " waves, "
+              << c.ST << " LDS buffers of " << (c.BM + c.BN) * c.BK * 2 << " B, K split " << c.SK << " ways, "
+              << kt << " k-tile(s) of " << c.BK << ", " << N / c.BN << " tile column(s), weight row stride "
+              << 2 * K << " B\n";
+            s << "static_assert(K / " << c.SK << " / " << c.BK << " == " << kt << ", \"trip count\");\n";
             s << "extern \"C\" __global__ __launch_bounds__(" << c.threads << ") void " << c.name << sig
-              << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.WM << ", " << c.WN << ", " << c.SK
-              << ", " << c.GM << ", " << out << ">(X, W, Y, ws, M); }\n";
+              << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.BK << ", " << c.ST << ", " << c.WM << ", "
+              << c.WN << ", " << c.SK << ", " << c.GM << ", " << c.SWZ << ", " << out << ">(X, W, Y, ws, M); }\n";
             if (c.SK > 1 && !reduce_emitted[c.SK]) {
                 reduce_emitted[c.SK] = true;
                 s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.reduce_name

@@ -1,0 +1,155 @@
+// gate.hip -- validation-gate kernels of the load-time tuner (part of the shape module)
+
+// ===========================================================================
+// Support kernels: validation gate, probes, measurement.  Not templated on a
+// candidate; one instance per module.
+// ===========================================================================
+
+// Reference rows for the validation gate: for each listed row rows[j], the f32
+// dot products with every W row, k ascending, one thread per output column n.
+// W is read once per launch (all listed rows share the thread's W row).
+extern "C" __global__ __launch_bounds__(256) void proj_ref_rows(const u16* __restrict__ X,
+                                                                const u16* __restrict__ W,
+                                                                const int* __restrict__ rows,
+                                                                int nrows, float* __restrict__ ref)
+{
+    constexpr int MAXR = 8;
+    const long n = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    float acc[MAXR];
+#pragma unroll
+    for (int j = 0; j < MAXR; ++j) acc[j] = 0.f;
+    const u32x4* wp = reinterpret_cast<const u32x4*>(W + n * K);
+    for (long c = 0; c < K / 8; ++c) {
+        const u32x4 w = wp[c];
+#pragma unroll
+        for (int j = 0; j < MAXR; ++j)
+            if (j < nrows) {
+                const u32x4 x = reinterpret_cast<const u32x4*>(X + (long)rows[j] * K)[c];
+                acc[j] = dev::dot8(w, x, acc[j]);
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < MAXR; ++j)
+        if (j < nrows) ref[(long)j * N + n] = acc[j];
+}
+
+// Counter-based generator for probe inputs (SplitMix-style mixer of seed and
+// index).  kind 0: uniform in [-scale, scale) rounded to bf16; kind 1: integers
+// uniform in [-4, 4] (exact in bf16).
+__device__ __forceinline__ u32 mix32(u64 z)
+{
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (u32)(z >> 32);
+}
+
+extern "C" __global__ __launch_bounds__(256) void proj_fill_probe(u16* __restrict__ out, long n, u32 seed,
+                                                                  int kind, float scale)
+{
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+        const u32 h = mix32(((u64)seed << 40) ^ (u64)i);
+        float v;
+        if (kind == 0) v = ((float)(h >> 8) * (1.0f / 8388608.0f) - 1.0f) * scale;
+        else v = (float)((int)(h % 9u) - 4);
+        out[i] = dev::to_bf16(v);
+    }
+}
+
+extern "C" __global__ __launch_bounds__(256) void proj_fill_u32(u32* __restrict__ out, long n, u32 value)
+{
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+        out[i] = value;
+}
+
+// Gate statistics written by proj_check: counters and the max error / max |ref|
+// over the listed rows (non-negative floats compare like their bit patterns).
+struct CheckStats {
+    u32 bad;          // listed-row elements outside the tolerance (or not bit-equal when exact)
+    u32 unwritten;    // elements of rows < M still holding the sentinel
+    u32 guard;        // elements of rows >= M that no longer hold the sentinel
+    u32 max_err;      // f32 bits of max |y - ref| over listed rows
+    u32 max_ref;      // f32 bits of max |ref| over listed rows
+    u32 pad[3];
+};
+
+template <int OUT>
+__device__ __forceinline__ float load_out(const void* Y, long i)
+{
+    if constexpr (OUT == OUT_F32) return reinterpret_cast<const float*>(Y)[i];
+    else return __builtin_bit_cast(float, (u32)reinterpret_cast<const u16*>(Y)[i] << 16);
+}
+
+template <int OUT>
+__device__ __forceinline__ bool is_sentinel(const void* Y, long i)
+{
+    if constexpr (OUT == OUT_F32) return reinterpret_cast<const u32*>(Y)[i] == SENTINEL_F32;
+    else return reinterpret_cast<const u16*>(Y)[i] == SENTINEL_BF16;
+}
+
+// Scans rows [0, rows_alloc) of Y: sentinel bookkeeping on every element, and
+// the comparison with ref on the listed rows.  Tolerance (exact == 0):
+//   f32 out:  |y - r| <= 1e-3 (|r| + 1)
+//   bf16 out: |y - R| <= ulp(R) with R = bf16(r), or the f32 rule.
+// exact == 1: y must equal the reference rounded to the output type, bit for bit.
+template <int OUT>
+__device__ __forceinline__ void check_body(const void* __restrict__ Y, long rows_alloc, int M,
+                                           const float* __restrict__ ref, const int* __restrict__ rows,
+                                           int nrows, int exact, CheckStats* __restrict__ st)
+{
+    const long total = rows_alloc * N;
+    u32 bad = 0, unw = 0, grd = 0;
+    float merr = 0.f, mref = 0.f;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+        const long row = i / N, col = i % N;
+        const bool sent = is_sentinel<OUT>(Y, i);
+        if (row < M) unw += sent ? 1u : 0u;
+        else grd += sent ? 0u : 1u;
+        if (row >= M) continue;
+        for (int j = 0; j < nrows; ++j) {
+            if (rows[j] != row) continue;
+            const float r = ref[(long)j * N + col];
+            const float y = load_out<OUT>(Y, i);
+            const float err = __builtin_fabsf(y - r);
+            bool ok;
+            if (exact) {
+                if constexpr (OUT == OUT_F32) ok = __builtin_bit_cast(u32, y) == __builtin_bit_cast(u32, r);
+                else ok = reinterpret_cast<const u16*>(Y)[i] == dev::to_bf16(r);
+            } else {
+                ok = err <= 1e-3f * (__builtin_fabsf(r) + 1.f);
+                if constexpr (OUT == OUT_BF16) {
+                    const float R = __builtin_bit_cast(float, (u32)dev::to_bf16(r) << 16);
+                    const float aR = __builtin_fabsf(R);
+                    int e = aR > 0.f ? (int)((__builtin_bit_cast(u32, aR) >> 23) & 0xFF) - 127 : -126;
+                    e = e < -126 ? -126 : e;
+                    const float ulp = __builtin_ldexpf(1.f, e - 7);
+                    ok = ok || (__builtin_fabsf(y - R) <= ulp);
+                }
+            }
+            bad += ok ? 0u : 1u;
+            merr = (err > merr || err != err) ? (err != err ? __builtin_inff() : err) : merr;
+            mref = __builtin_fabsf(r) > mref ? __builtin_fabsf(r) : mref;
+        }
+    }
+    if (bad) atomicAdd(&st->bad, bad);
+    if (unw) atomicAdd(&st->unwritten, unw);
+    if (grd) atomicAdd(&st->guard, grd);
+    atomicMax(&st->max_err, __builtin_bit_cast(u32, merr));
+    atomicMax(&st->max_ref, __builtin_bit_cast(u32, mref));
+}
+
+extern "C" __global__ __launch_bounds__(256) void proj_check_f32(const void* Y, long rows_alloc, int M,
+                                                                 const float* ref, const int* rows,
+                                                                 int nrows, int exact, CheckStats* st)
+{
+    check_body<OUT_F32>(Y, rows_alloc, M, ref, rows, nrows, exact, st);
+}
+
+extern "C" __global__ __launch_bounds__(256) void proj_check_bf16(const void* Y, long rows_alloc, int M,
+                                                                  const float* ref, const int* rows,
+                                                                  int nrows, int exact, CheckStats* st)
+{
+    check_body<OUT_BF16>(Y, rows_alloc, M, ref, rows, nrows, exact, st);
+}

@@ -1,0 +1,292 @@
+// gemm.hip -- prefill kernels (part of the shape module; see kernels_head.hip).
+
+// ---------------------------------------------------------------------------
+// Prefill GEMM on MFMA (any M; block tile BM x BN, k-tile BK).
+//
+// Both operands are K-contiguous ("TN").  Each k-tile of X (BM x BK) and W
+// (BN x BK) goes straight from global memory into LDS with
+// global_load_lds_dwordx4 (no trip through VGPRs): the wave's 64 lanes fill 64
+// consecutive 16-byte LDS slots, and each lane fetches from global memory the
+// chunk that belongs in its slot.  LDS rows are BK*2 bytes (CPR 16-byte
+// chunks); chunk c of row r lives in slot c ^ ((r >> SWZ) & (CPR-1)) of the
+// row, so that the 32 rows read by one MFMA operand load spread over all LDS
+// banks (SWZ picks the period that matches the bank count).
+//
+// STAGES buffers form a ring: while the waves run MFMAs on tile kt, the copies
+// of tiles kt+1 .. kt+STAGES-1 are in flight.  Each wave waits only for its own
+// copies of tile kt (s_waitcnt vmcnt with the count of younger copies), then a
+// barrier makes every wave's part visible and also tells that tile kt-1's
+// buffer is free for tile kt+STAGES-1.  Each buffer is its own __shared__
+// array so the compiler can see which copy writes which buffer.
+//
+// WM x WN waves; each wave owns a (BM/WM) x (BN/WN) sub-tile of 32 x 32 MFMA
+// blocks (v_mfma_f32_32x32x16_bf16, X as the A operand, W as the B operand),
+// and double-buffers its operand fragments in registers across the 16-wide k
+// steps of a tile.  Rows of X at or past M are clamped to M-1 on load and never
+// stored.
+//
+// Split-K (SK > 1): block (tile, z) sums k in [z*K/SK, (z+1)*K/SK) and writes
+// an f32 partial into ws[z][M][N]; splitk_reduce then adds the SK partials in
+// ascending z, so the result does not depend on which block finishes first.
+//
+// Tile order: the hardware deals consecutive workgroup ids round-robin to the
+// 8 XCDs, each with its own L2.  The id is first remapped so that each XCD gets
+// a contiguous range of ids, then that range walks the tiles GROUP_M tile-rows
+// at a time, so tiles sharing X rows and W rows run together under one L2.
+// ---------------------------------------------------------------------------
+namespace gemm_detail {
+
+// s_waitcnt until at most N vector-memory operations of this wave are
+// outstanding and none of its LDS operations (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8 = 0).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that orders the surrounding LDS accesses in the compiler
+// without draining the outstanding global->LDS copies (their waits are
+// explicit, above).  Nothing is scheduled across it.
+__device__ __forceinline__ void barrier_lds()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+}  // namespace gemm_detail
+
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SK, int GROUP_M, int SWZ, int OUT>
+__device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* __restrict__ W,
+                                          void* __restrict__ Y, float* __restrict__ ws, int M)
+{
+    using namespace gemm_detail;
+    constexpr int NTHR = WM * WN * 64;
+    constexpr int CPR = BK / 8;                       // 16-byte chunks per LDS row
+    static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
+    static_assert(STAGES >= 2 && STAGES <= 4, "2..4 buffers");
+    static_assert(K % (SK * BK) == 0, "K splits are whole k-tiles");
+    constexpr long KS = K / SK;
+    constexpr long KT = KS / BK;                      // k-tiles per split (trip count)
+    constexpr int WTM = BM / WM, WTN = BN / WN;       // wave sub-tile
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    static_assert(N % BN == 0, "tiles cover N exactly");
+    constexpr int CA = BM * CPR, CB = BN * CPR;       // chunks per buffer
+    static_assert(CA % NTHR == 0 && CB % NTHR == 0, "copies split evenly over threads");
+    constexpr int IA = CA / NTHR, IB = CB / NTHR;     // copy instructions per thread per tile
+    constexpr int PER_TILE = IA + IB;
+    static_assert((STAGES - 2) * PER_TILE <= 63, "younger copies fit the vmcnt counter");
+    constexpr int STAGE = CA + CB;                    // 16-byte slots per buffer
+    constexpr long TILES_N = N / BN;
+    constexpr int KK = BK / 16;                       // MFMA k-steps per tile
+
+    __shared__ u32x4 lds0[STAGE];
+    __shared__ u32x4 lds1[STAGE];
+    __shared__ u32x4 lds2[STAGES > 2 ? STAGE : 1];
+    __shared__ u32x4 lds3[STAGES > 3 ? STAGE : 1];
+    auto buf = [&](int s) -> u32x4* { return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : lds3; };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    // ---- tile index: XCD-contiguous remap, then grouped ordering
+    const long tiles_m = (M + BM - 1) / BM;
+    const long nblk = tiles_m * TILES_N;
+    const long pid0 = blockIdx.x;
+    const long q = nblk / 8, rem = nblk % 8;
+    const long xcd = pid0 % 8, local = pid0 / 8;
+    const long pid = (xcd < rem) ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+    const long in_group = (long)GROUP_M * TILES_N;
+    const long group = pid / in_group;
+    const long first_m = group * GROUP_M;
+    const long gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+    const long tm = first_m + (pid % in_group) % gsz;
+    const long tn = (pid % in_group) / gsz;
+    const long m0 = tm * BM, n0 = tn * BN;
+    const int z = blockIdx.y;
+    const long kbeg = (long)z * KS;
+
+    // ---- global sources of the copy slots.  Copy instruction i of thread t fills
+    //      slot i*NTHR + t, i.e. row i*RPI + t/CPR of the buffer; the chunk's column
+    //      (t%CPR) ^ swizzle(row) does not depend on i because RPI >> SWZ is a
+    //      multiple of CPR.  Offsets are 32-bit and relative to the tile's first
+    //      row (at most BN*K*2 bytes), on a block-uniform 64-bit base.
+    constexpr int RPI = NTHR / CPR;                   // buffer rows per copy instruction
+    static_assert(NTHR % CPR == 0 && (RPI >> SWZ) % CPR == 0, "swizzle column is copy-invariant");
+    const int r0 = tid / CPR;
+    const int ccol = (tid % CPR) ^ ((r0 >> SWZ) & (CPR - 1));
+    const u16* __restrict__ abase = X + m0 * K + kbeg;
+    const u16* __restrict__ bbase = W + n0 * K + kbeg;
+    const long mlast = (long)M - 1 - m0;              // last valid row relative to m0
+    unsigned aoff[IA];
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+        long r = i * RPI + r0;
+        r = r < mlast ? r : mlast;
+        aoff[i] = (unsigned)(r * K + ccol * 8);
+    }
+    const unsigned boff0 = (unsigned)(r0 * K + ccol * 8);
+    auto issue = [&](u32x4* dst, long kt) {
+        const u16* a = abase + kt * BK;
+        const u16* b = bbase + kt * BK;
+#pragma unroll
+        for (int i = 0; i < IA; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(a + aoff[i]),
+                                             (lds_void*)(dst + i * NTHR + wave * 64), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < IB; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(b + boff0 + (unsigned)(i * RPI * K)),
+                                             (lds_void*)(dst + CA + i * NTHR + wave * 64), 16, 0, 0);
+    };
+
+    // ---- operand fragment addressing (slot of lane's row/chunk within a buffer)
+    const int lrow = lane & 31;
+    const int lhalf = lane >> 5;
+    auto frag_a = [&](const u32x4* b, int i, int kk) -> bf16x8 {
+        const int row = wm * WTM + i * 32 + lrow;
+        const int c = kk * 2 + lhalf;
+        return __builtin_bit_cast(bf16x8, b[row * CPR + (c ^ ((row >> SWZ) & (CPR - 1)))]);
+    };
+    auto frag_b = [&](const u32x4* b, int j, int kk) -> bf16x8 {
+        const int row = wn * WTN + j * 32 + lrow;
+        const int c = kk * 2 + lhalf;
+        return __builtin_bit_cast(bf16x8, b[CA + row * CPR + (c ^ ((row >> SWZ) & (CPR - 1)))]);
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // ---- prologue: tiles 0 .. STAGES-2 in flight
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(buf(s), s < KT ? s : KT - 1);
+
+    // One k-tile: wait for its copies, barrier, start the copy of the tile
+    // STAGES-1 ahead into the buffer freed by the previous tile, then the MFMAs.
+    // Past the last tile the copy re-reads tile KT-1 into a free buffer, so every
+    // step issues the same number of copies and the vmcnt bound stays exact
+    // without branches (branches here hide from the compiler which buffer a copy
+    // writes, and it then drains every copy before each LDS read).
+    auto step = [&](const u32x4* b, u32x4* nxt, long kt) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lds<(STAGES - 2) * PER_TILE>();
+        barrier_lds();
+        const long ahead = kt + STAGES - 1;
+        issue(nxt, ahead < KT ? ahead : KT - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[0][i] = frag_a(b, i, 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[0][j] = frag_b(b, j, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < KK) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = frag_a(b, i, kk + 1);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = frag_b(b, j, kk + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        }
+        // Instruction order for the scheduler: the first step's operand reads,
+        // then, for each step, its MFMAs with the next step's reads slotted in
+        // between them, so those reads are in flight while the MFMA pipe works
+        // (left to itself the scheduler keeps one set of operand registers and
+        // waits on every read).
+        constexpr int NMF = TM * TN, NRD = TM + TN;
+        constexpr int PAIRS = NMF < NRD ? NMF : NRD;
+        __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+#pragma unroll
+            for (int r = 0; r < PAIRS; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+            if constexpr (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    };
+    constexpr long KMAIN = KT - KT % STAGES;
+    for (long kt = 0; kt < KMAIN; kt += STAGES) {
+        step(lds0, buf(STAGES - 1), kt);
+        step(lds1, lds0, kt + 1);
+        if constexpr (STAGES > 2) step(lds2, lds1, kt + 2);
+        if constexpr (STAGES > 3) step(lds3, lds2, kt + 3);
+    }
+    if constexpr (KT % STAGES > 0) step(lds0, buf(STAGES - 1), KMAIN);
+    if constexpr (KT % STAGES > 1) step(lds1, lds0, KMAIN + 1);
+    if constexpr (KT % STAGES > 2) step(lds2, lds1, KMAIN + 2);
+    wait_vm_lds<0>();   // no copy may still write LDS when the block ends
+
+    // ---- epilogue.  acc[i][j][e] of lane l is C[row][col] of its 32x32 block with
+    //      row = 8*(e>>2) + 4*(l>>5) + (e&3), col = l & 31.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const long col = n0 + wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const long row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lhalf + (e & 3);
+                if (row < M) {
+                    if constexpr (SK == 1) dev::store1<OUT>(Y, row * N + col, acc[i][j][e]);
+                    else ws[((long)z * M + row) * N + col] = acc[i][j][e];
+                }
+            }
+        }
+    }
+}
+
+// Sum of the SK split-K partials in ascending split order, then the epilogue.
+template <int SK, int OUT>
+__device__ __forceinline__ void splitk_reduce(const float* __restrict__ ws, void* __restrict__ Y, int M)
+{
+    const long total4 = (long)M * N / 4;
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total4) return;
+    const long stride = (long)M * N;
+    f32x4 t = reinterpret_cast<const f32x4*>(ws)[i];
+#pragma unroll
+    for (int z = 1; z < SK; ++z) t += reinterpret_cast<const f32x4*>(ws + z * stride)[i];
+    dev::store4<OUT>(Y, i * 4, t);
+}
+
+// ---------------------------------------------------------------------------
+// Plain kernel for any shape: one thread per output, k ascending, f32 FMA.
+// Serves shapes no tiled candidate divides.
+// ---------------------------------------------------------------------------
+template <int OUT>
+__device__ __forceinline__ void gemm_plain(const u16* __restrict__ X, const u16* __restrict__ W,
+                                           void* __restrict__ Y, int M)
+{
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)M * N) return;
+    const long m = idx / N, n = idx % N;
+    const u32x4* xp = reinterpret_cast<const u32x4*>(X + m * K);
+    const u32x4* wp = reinterpret_cast<const u32x4*>(W + n * K);
+    float acc = 0.f;
+    for (long c = 0; c < K / 8; ++c) acc = dev::dot8(wp[c], xp[c], acc);
+    dev::store1<OUT>(Y, idx, acc);
+}
+

@@ -1,0 +1,174 @@
+// gemv.hip -- decode kernels for M <= 16 (part of the shape module; see kernels_head.hip)
+
+// ---------------------------------------------------------------------------
+// Decode GEMV on the vector ALU (M <= MMAX, MMAX small).
+//
+// One wave walks R rows of W; lane l reads 16-byte chunk l, l+64, l+128, ... of
+// each row, so one load instruction covers 1 KiB of a row contiguously.  The
+// GPU analogue of the pages' decode module: one subgroup per output row,
+// lanes striding over 16-byte (8 x bf16) blocks of the weight row, the row
+// length in blocks and the row count as constants ("#002 le meme compilateur
+// sur un GPU", section "Emettre pour un GPU").  The S waves of a row group
+// split K and combine through LDS in a fixed order.
+//
+// Block: 256 threads = 4 waves = (4/S) row groups x S K-slices.
+// Grid:  N / (R * 4/S) blocks.
+// ---------------------------------------------------------------------------
+template <int R, int S, int MMAX, int U, int NT, int OUT>
+__device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* __restrict__ W,
+                                          void* __restrict__ Y, int M)
+{
+    static_assert(4 % S == 0, "S divides the 4 waves of a block");
+    constexpr long CH = K / 8;                  // 16-byte chunks per row
+    static_assert(K % 8 == 0 && CH % S == 0, "K slice must be whole chunks");
+    constexpr long CHS = CH / S;                // chunks per K-slice
+    constexpr long TRIPS = CHS / 64;            // full 64-lane trips per slice
+    constexpr int TAIL = (int)(CHS % 64);       // lanes busy in the last, partial trip
+    static_assert(U >= 1 && TRIPS % U == 0, "U divides the trip count");
+    constexpr int RG = 4 / S;
+    static_assert(N % (R * RG) == 0, "blocks tile N exactly");
+    constexpr int V = R * MMAX;
+    constexpr int LV = dev::log2_of<V>::value;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int s = wave % S;
+    const int rg = wave / S;
+    const long n0 = ((long)blockIdx.x * RG + rg) * R;
+
+    const u32x4* __restrict__ Wp = reinterpret_cast<const u32x4*>(W) + n0 * CH + s * CHS + lane;
+    const u32x4* __restrict__ Xp = reinterpret_cast<const u32x4*>(X) + s * CHS + lane;
+
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+
+    for (long t0 = 0; t0 < TRIPS; t0 += U) {
+        u32x4 w[U][R];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                w[u][r] = dev::load16<NT>(Wp + r * CH + (t0 + u) * 64);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int m = 0; m < MMAX; ++m) {
+                if (m < M) {
+                    const u32x4 x = Xp[m * CH + (t0 + u) * 64];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r * MMAX + m] = dev::dot8(w[u][r], x, acc[r * MMAX + m]);
+                }
+            }
+        }
+    }
+    if constexpr (TAIL > 0) {
+        if (lane < TAIL) {
+            u32x4 w[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) w[r] = dev::load16<NT>(Wp + r * CH + TRIPS * 64);
+#pragma unroll
+            for (int m = 0; m < MMAX; ++m) {
+                if (m < M) {
+                    const u32x4 x = Xp[m * CH + TRIPS * 64];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r * MMAX + m] = dev::dot8(w[r], x, acc[r * MMAX + m]);
+                }
+            }
+        }
+    }
+
+    const float sum = dev::wave_reduce_scatter<V>(acc, lane);
+    const int idx = lane >> (6 - LV);               // value index held by this lane
+    const bool writer = (lane & ((64 >> LV) - 1)) == 0;
+    const int r = idx / MMAX, m = idx % MMAX;
+
+    if constexpr (S == 1) {
+        if (writer && m < M) dev::store1<OUT>(Y, (long)m * N + n0 + r, sum);
+    } else {
+        __shared__ float red[4][V];
+        if (writer) red[wave][idx] = sum;
+        __syncthreads();
+        if (s == 0 && writer && m < M) {
+            float t = red[wave][idx];
+#pragma unroll
+            for (int j = 1; j < S; ++j) t += red[wave + j][idx];
+            dev::store1<OUT>(Y, (long)m * N + n0 + r, t);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny GEMM on MFMA for M <= 16 (decode and tiny prefill blocks).
+//
+// One wave computes 16 rows of W (n) x 16 rows of X (m) with
+// v_mfma_f32_16x16x32_bf16: W is the A operand, X the B operand.  Lane
+// (r = l & 15, g = l >> 4) loads, for each batch of U MFMA steps, U contiguous
+// 16-byte chunks of row r starting at k = batch*32U + g*8U, and MFMA u takes
+// chunk u from every lane.  A and B use the same assignment of k to lanes, so
+// each MFMA step sums 32 distinct k and the batch covers [batch*32U,
+// (batch+1)*32U) exactly once: only the summation order differs from k
+// ascending.  Rows of X at or past M are not read (the last real row is
+// re-read) and their outputs are not stored.
+//
+// Block: 256 threads = 4 waves = (4/S) row tiles x S K-slices.
+// Grid:  N / (16 * 4/S) blocks.
+// ---------------------------------------------------------------------------
+template <int S, int U, int NT, int OUT>
+__device__ __forceinline__ void gemv_mfma(const u16* __restrict__ X, const u16* __restrict__ W,
+                                          void* __restrict__ Y, int M)
+{
+    static_assert(4 % S == 0, "S divides the 4 waves of a block");
+    constexpr int RG = 4 / S;
+    static_assert(N % (16 * RG) == 0, "blocks tile N exactly");
+    static_assert(K % (32 * U * S) == 0, "K slices are whole batches");
+    constexpr long KS = K / S;
+    constexpr long BATCHES = KS / (32 * U);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int s = wave % S;
+    const int rg = wave / S;
+    const long n0 = ((long)blockIdx.x * RG + rg) * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int mrow = r < M ? r : M - 1;
+
+    const u16* __restrict__ Wrow = W + (n0 + r) * K + s * KS + g * 8 * U;
+    const u16* __restrict__ Xrow = X + (long)mrow * K + s * KS + g * 8 * U;
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (long b = 0; b < BATCHES; ++b) {
+        u32x4 w[U], x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            w[u] = dev::load16<NT>(reinterpret_cast<const u32x4*>(Wrow + b * 32 * U + u * 8));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            x[u] = *reinterpret_cast<const u32x4*>(Xrow + b * 32 * U + u * 8);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[u]),
+                                                          __builtin_bit_cast(bf16x8, x[u]),
+                                                          acc, 0, 0, 0);
+    }
+
+    // acc[i] of lane l is C[n = n0 + 4*(l>>4) + i][m = l & 15].
+    const int m = lane & 15;
+    const long nbase = n0 + 4 * (lane >> 4);
+    if constexpr (S == 1) {
+        if (m < M) dev::store4<OUT>(Y, (long)m * N + nbase, acc);
+    } else {
+        __shared__ f32x4 red[4][64];
+        red[wave][lane] = acc;
+        __syncthreads();
+        if (s == 0 && m < M) {
+            f32x4 t = red[wave][lane];
+#pragma unroll
+            for (int j = 1; j < S; ++j) t += red[wave + j][lane];
+            dev::store4<OUT>(Y, (long)m * N + nbase, t);
+        }
+    }
+}
+

@@ -25,8 +25,9 @@ struct Candidate {
     Family fam = Family::Plain;
     // GEMV parameters
     int R = 1, S = 1, MMAX = 1, U = 1, NT = 1;
-    // GEMM parameters
-    int BM = 0, BN = 0, WM = 0, WN = 0, SK = 1, GM = 8;
+    // GEMM parameters: block tile, k-tile, LDS buffers, wave grid, split-K,
+    // tile-row group, LDS swizzle period
+    int BM = 0, BN = 0, BK = 64, ST = 2, WM = 0, WN = 0, SK = 1, GM = 8, SWZ = 0;
 
     std::string name;          // extern "C" wrapper name in the generated module
     std::string reduce_name;   // split-K reduce kernel (empty if SK == 1)
@@ -56,7 +57,10 @@ std::string emit_support_source();
 
 // Embedded device sources (generated from the .hip files at build time).
 extern const char* const kDeviceCommonSrc;
-extern const char* const kKernelsSrc;
+extern const char* const kKernelsHeadSrc;
+extern const char* const kGemvSrc;
+extern const char* const kGemmSrc;
+extern const char* const kGateSrc;
 extern const char* const kSupportSrc;
 
 // Bucket index for M >= 1 (M > kMaxBlockRows maps to the last bucket).

@@ -10,23 +10,25 @@
 // sequential read, best of several passes, taken as the denominator beside the
 // vendor figure ("#001 un compilateur pour moteur de LLM", section "Mesurer la
 // limite plutot que la supposer").
+//
+// Each block reads one contiguous 32 KiB span (8 loads in flight per lane, each
+// wave instruction 1 KiB contiguous) and exits, so the device keeps many short
+// waves in flight, the access pattern of a weight-streaming GEMV.
+// Grid: ceil(n16 / 2048) blocks of 256 threads.
 extern "C" __global__ __launch_bounds__(256) void proj_probe_read(const u32x4* __restrict__ p, long n16,
                                                                   u32 never, u32* __restrict__ sink)
 {
-    const long stride = (long)gridDim.x * blockDim.x;
-    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    constexpr int LOADS = 8;
+    const long base = (long)blockIdx.x * (256 * LOADS) + threadIdx.x;
+    u32x4 v[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const long i = base + j * 256;
+        v[j] = i < n16 ? __builtin_nontemporal_load(p + i) : u32x4{0u, 0u, 0u, 0u};
+    }
     u32 acc = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4 a = __builtin_nontemporal_load(p + i);
-        const u32x4 b = __builtin_nontemporal_load(p + i + stride);
-        const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
-        const u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
-        acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
-    }
-    for (; i < n16; i += stride) {
-        const u32x4 a = __builtin_nontemporal_load(p + i);
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
-    }
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
     if (acc == never) sink[0] = acc;
 }
 

@@ -1,0 +1,154 @@
+"""Summaries of rocprofv3 output for the projection kernels.
+
+    python -m shape_specialised_bf16_amd.profile_summary stats <dir-or-db> [--match S] [--stream last]
+        per-kernel dispatch count and mean/min/max duration (us) from a
+        ``--kernel-trace`` run (rocpd ``*_results.db`` or ``*_kernel_trace.csv``);
+        ``--stream last`` keeps only the stream of the last dispatch (the timed
+        loop), dropping the load-time tuner's launches.
+
+    python -m shape_specialised_bf16_amd.profile_summary traffic --fetch <dir> --write <dir>
+            --kernel NAME --calib NAME --calib-bytes B [--out profiles/traffic.json --key KEY]
+        HBM bytes per launch of kernel NAME from two ``--pmc FETCH_SIZE`` /
+        ``--pmc WRITE_SIZE`` runs.  Each counter (KiB per dispatch) is scaled by
+        the ratio of the known bytes of a plain copy kernel (``--calib``, which
+        reads and writes ``--calib-bytes``) to what the same counter reports for
+        it.  With ``--out`` the result is merged into a JSON file keyed by KEY,
+        together with the hash of the kernel sources it was measured on.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_sha(kernel: str) -> str:
+    """Hash of the device sources a kernel is built from (the shared helpers and
+    its family's file), to tell whether a stored measurement is still current."""
+    fam = "gemv.hip" if kernel.startswith("gemv") else "gemm.hip"
+    h = hashlib.sha256()
+    for f in ("device_common.hip", fam):
+        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _dispatches(path: str):
+    """(name, stream, start, end, dispatch_id, grid) of every kernel dispatch."""
+    dbs = [path] if path.endswith(".db") else glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True)
+    if dbs:
+        db = sqlite3.connect(dbs[0])
+        return [tuple(r) for r in db.execute(
+            "select name, stream_id, start, end, dispatch_id, grid_x * grid_y from kernels order by start")]
+    csvs = glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True)
+    if not csvs:
+        raise SystemExit(f"no kernel trace under {path}")
+    out = []
+    for r in csv.DictReader(open(csvs[0])):
+        grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0) * int(r.get("Grid_Size_Y", 1) or 1)
+        out.append((r["Kernel_Name"], int(r.get("Stream_Id", 0) or 0), int(r["Start_Timestamp"]),
+                    int(r["End_Timestamp"]), int(r["Dispatch_Id"]), grid))
+    return sorted(out, key=lambda t: t[2])
+
+
+def stats(path: str, match: str = "", stream: str = "all"):
+    rows = _dispatches(path)
+    if stream == "last" and rows:
+        s = rows[-1][1]
+        rows = [r for r in rows if r[1] == s]
+    by = {}
+    for name, _, a, b, _, grid in rows:
+        if match and match not in name:
+            continue
+        by.setdefault((name, grid), []).append((b - a) / 1e3)   # one entry per kernel and launch size
+    out = []
+    for (name, grid), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        out.append(dict(kernel=name, grid=grid, calls=len(d), mean_us=statistics.mean(d), min_us=min(d),
+                        max_us=max(d), total_us=sum(d)))
+    return out
+
+
+def _counter(path: str, counter: str):
+    """{dispatch_id: (kernel name, value)} for one counter of a --pmc run."""
+    csvs = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    out = {}
+    if csvs:
+        for r in csv.DictReader(open(csvs[0])):
+            if r["Counter_Name"] == counter:
+                out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+        return out
+    dbs = glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no counter output under {path}")
+    db = sqlite3.connect(dbs[0])
+    for did, name, val in db.execute(
+            "select dispatch_id, kernel_name, value from counters_collection where counter_name = ?", (counter,)):
+        out[int(did)] = (name, float(val))
+    return out
+
+
+def _per_launch(vals, name):
+    v = [x for n, x in vals.values() if name in n]
+    if not v:
+        raise SystemExit(f"kernel {name!r} not found in counter output")
+    return statistics.median(v)
+
+
+def traffic(fetch_dir, write_dir, kernel, calib, calib_bytes):
+    f = _counter(fetch_dir, "FETCH_SIZE")
+    w = _counter(write_dir, "WRITE_SIZE")
+    f_k, w_k = _per_launch(f, kernel), _per_launch(w, kernel)
+    # the calibration copy is the largest dispatch of its name (small copies of the
+    # same blit kernel also occur while plans are built)
+    f_c = max(x for n, x in f.values() if calib in n)
+    w_c = max(x for n, x in w.values() if calib in n)
+    f_scale = calib_bytes / f_c
+    w_scale = calib_bytes / w_c
+    return dict(fetch_bytes=f_k * f_scale, write_bytes=w_k * w_scale,
+                bytes_per_launch=f_k * f_scale + w_k * w_scale,
+                raw_fetch_kib=f_k, raw_write_kib=w_k, calib_fetch_kib=f_c, calib_write_kib=w_c,
+                fetch_scale=f_scale, write_scale=w_scale, calib_kernel=calib, calib_bytes=calib_bytes)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("path")
+    s.add_argument("--match", default="")
+    s.add_argument("--stream", default="all", choices=["all", "last"])
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--calib", required=True)
+    t.add_argument("--calib-bytes", type=float, required=True)
+    t.add_argument("--out")
+    t.add_argument("--key")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        for r in stats(a.path, a.match, a.stream):
+            print(f"{r['kernel'][:48]:48s} grid {r['grid']:10d} calls {r['calls']:5d}  mean {r['mean_us']:9.3f} us  "
+                  f"min {r['min_us']:10.3f}  max {r['max_us']:10.3f}  total {r['total_us']:12.1f}")
+    else:
+        r = traffic(a.fetch, a.write, a.kernel, a.calib, a.calib_bytes)
+        r["source_sha"] = kernel_source_sha(a.kernel)
+        print(json.dumps(r, indent=1))
+        if a.out:
+            d = json.load(open(a.out)) if os.path.exists(a.out) else {}
+            d[a.key or a.kernel] = r
+            with open(a.out, "w") as fh:
+                json.dump(d, fh, indent=1, sort_keys=True)
+                fh.write("\n")
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -85,10 +85,11 @@ def test_candidates_tile_the_shape(N, K):
             S, U, _ = map(int, m.groups())
             assert N % (16 * (4 // S)) == 0 and K % (32 * U * S) == 0
             continue
-        m = re.match(r"gemm_(\d+)x(\d+)_w(\d+)x(\d+)_sk(\d+)_g(\d+)", n)
+        m = re.match(r"gemm_(\d+)x(\d+)x(\d+)_st(\d+)_w(\d+)x(\d+)_sw(\d+)_g(\d+)_sk(\d+)", n)
         if m:
-            BM, BN, WM, WN, SK, _ = map(int, m.groups())
-            assert N % BN == 0 and K % (64 * SK) == 0
+            BM, BN, BK, ST, WM, WN, SWZ, GM, SK = map(int, m.groups())
+            assert N % BN == 0 and K % (BK * SK) == 0
+            assert ST * (BM + BN) * BK * 2 <= 160 * 1024     # LDS of one workgroup
             continue
         assert n == "gemm_plain", n
 

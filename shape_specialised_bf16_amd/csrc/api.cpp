@@ -136,7 +136,8 @@ int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* bu
         return set_error(PROJ_EINVAL, "invalid shape N=%lld K=%lld", (long long)N, (long long)K);
     if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16) return set_error(PROJ_EINVAL, "invalid dtype %d", dtype);
     const std::string a = (arch && *arch) ? arch : "gfx950";
-    return copy_text(emit_source(N, K, dtype, a, enumerate_candidates(N, K)), buf, cap, needed);
+    return copy_text(emit_source(N, K, dtype, a, kDefaultCUs, enumerate_candidates(N, K, kDefaultCUs)), buf, cap,
+                     needed);
 }
 
 int proj_plan_describe(const proj_plan* plan, char* buf, size_t cap, size_t* needed)
@@ -164,8 +165,10 @@ int64_t proj_plan_candidate_max_m(const proj_plan* plan, int idx)
     if (idx < 0 || idx >= (int)plan->cands.size()) return set_error(PROJ_EINVAL, "candidate %d out of range", idx);
     const Candidate& c = plan->cands[idx];
     int64_t m = c.max_m;
-    if (c.needs_ws()) m = std::min<int64_t>(m, (int64_t)(plan->ws_bytes / ((size_t)c.SK * plan->N * sizeof(float))));
-    return m;
+    if (c.SK > 1) m = std::min<int64_t>(m, (int64_t)(plan->ws_bytes / ((size_t)c.SK * plan->N * sizeof(float))));
+    if (c.TAILS > 1)  // largest row count whose whole range fits the workspace
+        while (m > 0 && c.ws_bound(m, plan->N) > plan->ws_bytes) m -= c.BM;
+    return std::max<int64_t>(m, 0);
 }
 
 int proj_run_candidate(const proj_plan* plan, int idx, const void* X, const void* W, void* Y, int64_t M,

@@ -34,7 +34,7 @@ static std::string fmt(const char* f, ...)
     return buf;
 }
 
-std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K)
+std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus)
 {
     std::vector<Candidate> out;
     const int64_t CH = K / 8;  // 16-byte chunks per row
@@ -85,32 +85,41 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K)
     //      banks) at a time, so the 16 rows one operand read touches must land on
     //      distinct bank groups: XOR period 2 rows for 128-byte rows (BK = 64),
     //      4 rows for 64-byte rows (BK = 32).
-    struct GT { int BM, BN, BK, ST, WM, WN, SWZ; int maxSK; int GM = 8; };
+    //      Each entry also lists the K-split factors of its split-tail variants
+    //      (whole tiles for all full rounds of workgroups, the remaining tiles
+    //      split along K so the last round is not mostly idle).
+    struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[2]; };
     const GT gts[] = {
-        {256, 256, 64, 2, 2, 4, 1, 1}, {256, 256, 64, 2, 2, 4, 1, 1, 4}, {256, 256, 64, 2, 2, 4, 1, 1, 16},
-        {256, 256, 64, 2, 4, 2, 1, 1}, {256, 256, 32, 4, 2, 4, 2, 1},  {256, 256, 32, 3, 2, 4, 2, 1},
-        {256, 128, 64, 3, 4, 2, 1, 1, 4}, {128, 256, 64, 3, 2, 4, 1, 1, 4},
-        {256, 128, 32, 2, 2, 2, 2, 2}, {128, 256, 32, 2, 2, 2, 2, 2},
-        {128, 128, 64, 2, 2, 2, 1, 4}, {128, 128, 32, 3, 2, 2, 2, 4},
-        {64, 128, 64, 2, 1, 2, 1, 4}};
+        {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 0}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2, 0}},
+        {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {0, 0}}, {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {0, 0}},
+        {128, 128, 64, 2, 2, 2, 1, 4, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {0, 0}},
+        {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {0, 0}}, {64, 128, 64, 2, 1, 2, 1, 4, 8, 1, {0, 0}}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
         const int cpr = g.BK / 8, rpi = 64 * g.WM * g.WN / cpr;
         if ((rpi >> g.SWZ) % cpr) continue;  // the copy slots' swizzled column must not vary per copy
-        for (int SK : {1, 2, 4}) {
-            if (SK > g.maxSK) continue;
-            if (K % (g.BK * SK)) continue;
+        const int lds = g.ST * (g.BM + g.BN) * g.BK * 2;
+        const int per_cu = std::max(1, std::min(2, 160 * 1024 / lds));
+        auto add = [&](int SK, int TL) {
             Candidate c;
             c.fam = Family::Gemm;
             c.BM = g.BM; c.BN = g.BN; c.BK = g.BK; c.ST = g.ST; c.WM = g.WM; c.WN = g.WN;
-            c.SK = SK; c.GM = g.GM; c.SWZ = g.SWZ;
+            c.SK = SK; c.GM = g.GM; c.SWZ = g.SWZ; c.DMA = g.DMA;
+            c.TAILS = TL;
+            c.ROUND = TL > 1 ? cus * per_cu : 0;
             c.threads = 64 * g.WM * g.WN;
             c.max_m = kMaxBlockRows;
-            c.name = fmt("gemm_%dx%dx%d_st%d_w%dx%d_sw%d_g%d_sk%d", c.BM, c.BN, c.BK, c.ST, c.WM, c.WN, c.SWZ, c.GM,
-                         c.SK);
+            c.name = fmt("gemm_%dx%dx%d_st%d_w%dx%d_sw%d_g%d_sk%d%s", c.BM, c.BN, c.BK, c.ST, c.WM, c.WN, c.SWZ,
+                         c.GM, c.SK, c.DMA ? "" : "_reg");
+            if (TL > 1) c.name += fmt("_tail%d_r%d", TL, c.ROUND);
             if (SK > 1) c.reduce_name = fmt("splitk_reduce_sk%d", SK);
+            if (TL > 1) c.reduce_name = c.name + "_reduce";
             out.push_back(c);
-        }
+        };
+        for (int SK : {1, 2, 4})
+            if (SK <= g.maxSK && K % (g.BK * SK) == 0) add(SK, 1);
+        for (int TL : g.tails)
+            if (TL > 1 && (K / g.BK) % TL == 0) add(1, TL);
     }
 
     // ---- plain kernel, any shape (K % 8 == 0)
@@ -133,7 +142,7 @@ std::string emit_support_source()
     return s;
 }
 
-std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch,
+std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
                         const std::vector<Candidate>& cands)
 {
     const char* out = dtype == 1 ? "OUT_BF16" : "OUT_F32";
@@ -145,7 +154,8 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
     s << "constexpr long K = " << K << ";            // row length (bf16 values)\n";
     s << "constexpr long K_BLOCKS16 = " << K / 8 << ";    // 16-byte (8 x bf16) blocks per weight row\n";
     s << "constexpr long N_LAST = " << N - 1 << ";       // last output row index\n";
-    s << "constexpr long ROW_BYTES = " << 2 * K << ";    // stride between weight rows\n\n";
+    s << "constexpr long ROW_BYTES = " << 2 * K << ";    // stride between weight rows\n";
+    s << "constexpr int DEVICE_CUS = " << cus << ";     // compute units of the device the code is for\n\n";
     s << kDeviceCommonSrc << "\n";
     s << kKernelsHeadSrc << "\n";
     s << kGemvSrc << "\n";
@@ -188,7 +198,15 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
             s << "static_assert(K / " << c.SK << " / " << c.BK << " == " << kt << ", \"trip count\");\n";
             s << "extern \"C\" __global__ __launch_bounds__(" << c.threads << ") void " << c.name << sig
               << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.BK << ", " << c.ST << ", " << c.WM << ", "
-              << c.WN << ", " << c.SK << ", " << c.GM << ", " << c.SWZ << ", " << out << ">(X, W, Y, ws, M); }\n";
+              << c.WN << ", " << c.SK << ", " << c.GM << ", " << c.SWZ << ", " << out << ", " << c.DMA << ", "
+              << c.TAILS << ", " << c.ROUND << ">(X, W, Y, ws, M); }\n";
+            if (c.TAILS > 1) {
+                s << "// " << c.reduce_name << ": tail tiles of " << c.name << ", " << c.TAILS
+                  << " pieces each, rounds of " << c.ROUND << " workgroups\n";
+                s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.reduce_name
+                  << "(const float* __restrict__ ws, void* __restrict__ Y, int M)\n{ tail_reduce<" << c.BM << ", "
+                  << c.BN << ", " << c.TAILS << ", " << c.ROUND << ", " << c.GM << ", " << out << ">(ws, Y, M); }\n";
+            }
             if (c.SK > 1 && !reduce_emitted[c.SK]) {
                 reduce_emitted[c.SK] = true;
                 s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.reduce_name

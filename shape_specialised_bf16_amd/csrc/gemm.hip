@@ -5,12 +5,13 @@
 //
 // Both operands are K-contiguous ("TN").  Each k-tile of X (BM x BK) and W
 // (BN x BK) goes straight from global memory into LDS with
-// global_load_lds_dwordx4 (no trip through VGPRs): the wave's 64 lanes fill 64
-// consecutive 16-byte LDS slots, and each lane fetches from global memory the
-// chunk that belongs in its slot.  LDS rows are BK*2 bytes (CPR 16-byte
-// chunks); chunk c of row r lives in slot c ^ ((r >> SWZ) & (CPR-1)) of the
-// row, so that the 32 rows read by one MFMA operand load spread over all LDS
-// banks (SWZ picks the period that matches the bank count).
+// global_load_lds_dwordx4 (DMA = 1; no trip through VGPRs): the wave's 64
+// lanes fill 64 consecutive 16-byte LDS slots, and each lane fetches from
+// global memory the chunk that belongs in its slot.  With DMA = 0 the same
+// chunks go through registers (loaded before the tile's MFMAs, written to LDS
+// after them).  LDS rows are BK*2 bytes (CPR 16-byte chunks); chunk c of row r
+// lives in slot c ^ ((r >> SWZ) & (CPR-1)) of the row, so that the 16 rows one
+// operand read serves at a time hit distinct banks.
 //
 // STAGES buffers form a ring: while the waves run MFMAs on tile kt, the copies
 // of tiles kt+1 .. kt+STAGES-1 are in flight.  Each wave waits only for its own
@@ -25,14 +26,24 @@
 // steps of a tile.  Rows of X at or past M are clamped to M-1 on load and never
 // stored.
 //
-// Split-K (SK > 1): block (tile, z) sums k in [z*K/SK, (z+1)*K/SK) and writes
-// an f32 partial into ws[z][M][N]; splitk_reduce then adds the SK partials in
-// ascending z, so the result does not depend on which block finishes first.
+// Work split, one of:
+//  * SK > 1 (split-K): block (tile, z) sums k in [z*K/SK, (z+1)*K/SK) and
+//    writes an f32 partial into ws[z][M][N]; splitk_reduce adds the SK partials
+//    in ascending z.
+//  * TAILS > 1 (data-parallel with a split tail): of the T tiles, the largest
+//    multiple of ROUND (the workgroups the device runs at once) that leaves a
+//    remainder runs as whole tiles; each of the rem remaining tiles is split
+//    TAILS ways along K, so the last round is filled with rem*TAILS shorter
+//    pieces instead of rem long ones.  Pieces write f32 partials into
+//    ws[piece][BM*BN]; tail_reduce adds them in ascending split order.
+// Both reductions use a fixed order, so results do not depend on which block
+// finishes first.
 //
 // Tile order: the hardware deals consecutive workgroup ids round-robin to the
-// 8 XCDs, each with its own L2.  The id is first remapped so that each XCD gets
-// a contiguous range of ids, then that range walks the tiles GROUP_M tile-rows
-// at a time, so tiles sharing X rows and W rows run together under one L2.
+// 8 XCDs, each with its own L2.  Whole-tile ids are first remapped so that
+// each XCD gets a contiguous range, then tile ids walk the tile grid GROUP_M
+// tile-rows at a time, so tiles sharing X rows and W rows run together under
+// one L2.
 // ---------------------------------------------------------------------------
 namespace gemm_detail {
 
@@ -60,9 +71,42 @@ __device__ __forceinline__ void barrier_lds()
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+template <long V> struct ic { static constexpr long value = V; };
+
+// Whole tiles and split tail tiles of a launch: T tiles, ROUND workgroups at
+// once.  With T >= ROUND the tail is T % ROUND tiles; below one round every
+// tile is a tail tile.  (The host computes the same split for the launch.)
+__device__ __forceinline__ void tail_split(long T, long round, long* n_full, long* rem)
+{
+    *rem = T >= round ? T % round : T;
+    *n_full = T - *rem;
+}
+
+// Tile id -> (tile-row, tile-column): GROUP_M tile-rows at a time.
+template <int GROUP_M>
+__device__ __forceinline__ void group_order(long pid, long tiles_m, long tiles_n, long* tm, long* tn)
+{
+    const long in_group = (long)GROUP_M * tiles_n;
+    const long group = pid / in_group;
+    const long first_m = group * GROUP_M;
+    const long gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+    *tm = first_m + (pid % in_group) % gsz;
+    *tn = (pid % in_group) / gsz;
+}
+
+// Workgroup id -> tile id such that each XCD (ids dealt round-robin over 8)
+// gets a contiguous range of tile ids.  A bijection on [0, nblk).
+__device__ __forceinline__ long xcd_remap(long pid0, long nblk)
+{
+    const long q = nblk / 8, rem = nblk % 8;
+    const long xcd = pid0 % 8, local = pid0 / 8;
+    return (xcd < rem) ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+}
+
 }  // namespace gemm_detail
 
-template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SK, int GROUP_M, int SWZ, int OUT>
+template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SK, int GROUP_M, int SWZ, int OUT, int DMA = 1,
+          int TAILS = 1, int ROUND = 0>
 __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* __restrict__ W,
                                           void* __restrict__ Y, float* __restrict__ ws, int M)
 {
@@ -72,8 +116,10 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
     static_assert(STAGES >= 2 && STAGES <= 4, "2..4 buffers");
     static_assert(K % (SK * BK) == 0, "K splits are whole k-tiles");
+    static_assert(TAILS == 1 || (SK == 1 && ROUND > 0 && (K / BK) % TAILS == 0), "tail pieces are whole k-tiles");
     constexpr long KS = K / SK;
-    constexpr long KT = KS / BK;                      // k-tiles per split (trip count)
+    constexpr long KT = KS / BK;                      // k-tiles of a whole (split-K) tile
+    constexpr long KT_TAIL = KT / TAILS;              // k-tiles of a tail piece
     constexpr int WTM = BM / WM, WTN = BN / WN;       // wave sub-tile
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -98,22 +144,28 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    // ---- tile index: XCD-contiguous remap, then grouped ordering
+    // ---- which tile (and which K range) this workgroup computes
     const long tiles_m = (M + BM - 1) / BM;
-    const long nblk = tiles_m * TILES_N;
-    const long pid0 = blockIdx.x;
-    const long q = nblk / 8, rem = nblk % 8;
-    const long xcd = pid0 % 8, local = pid0 / 8;
-    const long pid = (xcd < rem) ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
-    const long in_group = (long)GROUP_M * TILES_N;
-    const long group = pid / in_group;
-    const long first_m = group * GROUP_M;
-    const long gsz = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
-    const long tm = first_m + (pid % in_group) % gsz;
-    const long tn = (pid % in_group) / gsz;
+    const long T = tiles_m * TILES_N;
+    long n_full = T, rem_t = 0;
+    if constexpr (TAILS > 1) tail_split(T, ROUND, &n_full, &rem_t);
+    const bool tail = TAILS > 1 && (long)blockIdx.x >= n_full;
+    long pid, piece = 0;
+    int z;
+    long kbeg;
+    if (tail) {
+        piece = (long)blockIdx.x - n_full;
+        pid = n_full + piece / TAILS;
+        z = (int)(piece % TAILS);
+        kbeg = (long)z * (K / TAILS);
+    } else {
+        pid = xcd_remap(blockIdx.x, n_full);
+        z = blockIdx.y;
+        kbeg = (long)z * KS;
+    }
+    long tm, tn;
+    group_order<GROUP_M>(pid, tiles_m, TILES_N, &tm, &tn);
     const long m0 = tm * BM, n0 = tn * BN;
-    const int z = blockIdx.y;
-    const long kbeg = (long)z * KS;
 
     // ---- global sources of the copy slots.  Copy instruction i of thread t fills
     //      slot i*NTHR + t, i.e. row i*RPI + t/CPR of the buffer; the chunk's column
@@ -147,6 +199,22 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
             __builtin_amdgcn_global_load_lds((const void*)(b + boff0 + (unsigned)(i * RPI * K)),
                                              (lds_void*)(dst + CA + i * NTHR + wave * 64), 16, 0, 0);
     };
+    u32x4 ra[DMA ? 1 : IA], rb[DMA ? 1 : IB];
+    auto gload = [&](long kt) {
+        const u16* a = abase + kt * BK;
+        const u16* b = bbase + kt * BK;
+#pragma unroll
+        for (int i = 0; i < IA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a + aoff[i]);
+#pragma unroll
+        for (int i = 0; i < IB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b + boff0 + (unsigned)(i * RPI * K));
+    };
+    auto lstore = [&](u32x4* dst) {
+#pragma unroll
+        for (int i = 0; i < IA; ++i) dst[i * NTHR + tid] = ra[i];
+#pragma unroll
+        for (int i = 0; i < IB; ++i) dst[CA + i * NTHR + tid] = rb[i];
+    };
+    static_assert(DMA || STAGES == 2, "register-staged copies use two buffers");
 
     // ---- operand fragment addressing (slot of lane's row/chunk within a buffer)
     const int lrow = lane & 31;
@@ -170,77 +238,113 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // ---- prologue: tiles 0 .. STAGES-2 in flight
+    // ---- the k loop over NKT k-tiles (a compile-time count: KT for a whole
+    //      tile, KT_TAIL for a tail piece).
+    auto kloop = [&](auto nkt) {
+        constexpr long NKT = decltype(nkt)::value;
+        // prologue: tiles 0 .. STAGES-2 in flight (or tile 0 in buffer 0)
+        if constexpr (DMA) {
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(buf(s), s < KT ? s : KT - 1);
-
-    // One k-tile: wait for its copies, barrier, start the copy of the tile
-    // STAGES-1 ahead into the buffer freed by the previous tile, then the MFMAs.
-    // Past the last tile the copy re-reads tile KT-1 into a free buffer, so every
-    // step issues the same number of copies and the vmcnt bound stays exact
-    // without branches (branches here hide from the compiler which buffer a copy
-    // writes, and it then drains every copy before each LDS read).
-    auto step = [&](const u32x4* b, u32x4* nxt, long kt) {
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm_lds<(STAGES - 2) * PER_TILE>();
-        barrier_lds();
-        const long ahead = kt + STAGES - 1;
-        issue(nxt, ahead < KT ? ahead : KT - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 fa[2][TM], fb[2][TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[0][i] = frag_a(b, i, 0);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[0][j] = frag_b(b, j, 0);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int cur = kk & 1;
-            if (kk + 1 < KK) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = frag_a(b, i, kk + 1);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = frag_b(b, j, kk + 1);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+            for (int s = 0; s < STAGES - 1; ++s) issue(buf(s), s < NKT ? s : NKT - 1);
+        } else {
+            gload(0);
+            lstore(lds0);
         }
-        // Instruction order for the scheduler: the first step's operand reads,
-        // then, for each step, its MFMAs with the next step's reads slotted in
-        // between them, so those reads are in flight while the MFMA pipe works
-        // (left to itself the scheduler keeps one set of operand registers and
-        // waits on every read).
-        constexpr int NMF = TM * TN, NRD = TM + TN;
-        constexpr int PAIRS = NMF < NRD ? NMF : NRD;
-        __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+        // One k-tile: wait for its copies, barrier, start the copy of the tile
+        // STAGES-1 ahead into the buffer freed by the previous tile, then the
+        // MFMAs.  Past the last tile the copy re-reads tile NKT-1 into a free
+        // buffer, so every step issues the same number of copies and the vmcnt
+        // bound stays exact without branches (branches here hide from the
+        // compiler which buffer a copy writes, and it then drains every copy
+        // before each LDS read).  With DMA == 0 the step loads tile kt+1 into
+        // registers before its MFMAs and writes them to the free buffer after.
+        auto step = [&](const u32x4* b, u32x4* nxt, long kt) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lds<DMA ? (STAGES - 2) * PER_TILE : 0>();
+            barrier_lds();
+            const long ahead = kt + STAGES - 1;
+            if constexpr (DMA) issue(nxt, ahead < NKT ? ahead : NKT - 1);
+            else gload(ahead < NKT ? ahead : NKT - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
-        for (int kk = 0; kk + 1 < KK; ++kk) {
+            for (int i = 0; i < TM; ++i) fa[0][i] = frag_a(b, i, 0);
 #pragma unroll
-            for (int r = 0; r < PAIRS; ++r) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int j = 0; j < TN; ++j) fb[0][j] = frag_b(b, j, 0);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const int cur = kk & 1;
+                if (kk + 1 < KK) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = frag_a(b, i, kk + 1);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = frag_b(b, j, kk + 1);
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
+                                                                            0, 0, 0);
             }
-            if constexpr (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
-            if constexpr (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
+            // Instruction order for the scheduler: the first step's operand reads,
+            // then, for each step, its MFMAs with the next step's reads slotted in
+            // between them, so those reads are in flight while the MFMA pipe works
+            // (left to itself the scheduler keeps one set of operand registers and
+            // waits on every read).
+            constexpr int NMF = TM * TN, NRD = TM + TN;
+            constexpr int PAIRS = NMF < NRD ? NMF : NRD;
+            __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+            for (int kk = 0; kk + 1 < KK; ++kk) {
+#pragma unroll
+                for (int r = 0; r < PAIRS; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                if constexpr (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+                if constexpr (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+            if constexpr (!DMA) {
+                __builtin_amdgcn_sched_barrier(0);
+                lstore(nxt);
+            }
+        };
+        constexpr long KMAIN = NKT - NKT % STAGES;
+        for (long kt = 0; kt < KMAIN; kt += STAGES) {
+            step(lds0, buf(STAGES - 1), kt);
+            step(lds1, lds0, kt + 1);
+            if constexpr (STAGES > 2) step(lds2, lds1, kt + 2);
+            if constexpr (STAGES > 3) step(lds3, lds2, kt + 3);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+        if constexpr (NKT % STAGES > 0) step(lds0, buf(STAGES - 1), KMAIN);
+        if constexpr (NKT % STAGES > 1) step(lds1, lds0, KMAIN + 1);
+        if constexpr (NKT % STAGES > 2) step(lds2, lds1, KMAIN + 2);
+        wait_vm_lds<0>();   // no copy may still write LDS when the block ends
     };
-    constexpr long KMAIN = KT - KT % STAGES;
-    for (long kt = 0; kt < KMAIN; kt += STAGES) {
-        step(lds0, buf(STAGES - 1), kt);
-        step(lds1, lds0, kt + 1);
-        if constexpr (STAGES > 2) step(lds2, lds1, kt + 2);
-        if constexpr (STAGES > 3) step(lds3, lds2, kt + 3);
-    }
-    if constexpr (KT % STAGES > 0) step(lds0, buf(STAGES - 1), KMAIN);
-    if constexpr (KT % STAGES > 1) step(lds1, lds0, KMAIN + 1);
-    if constexpr (KT % STAGES > 2) step(lds2, lds1, KMAIN + 2);
-    wait_vm_lds<0>();   // no copy may still write LDS when the block ends
 
     // ---- epilogue.  acc[i][j][e] of lane l is C[row][col] of its 32x32 block with
     //      row = 8*(e>>2) + 4*(l>>5) + (e&3), col = l & 31.
+    if constexpr (TAILS > 1) {
+        if (tail) {
+            kloop(ic<KT_TAIL>{});
+            float* part = ws + piece * ((long)BM * BN);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lhalf + (e & 3);
+                        if (m0 + row < M) part[row * BN + col] = acc[i][j][e];
+                    }
+                }
+            return;
+        }
+    }
+    kloop(ic<KT>{});
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -272,6 +376,32 @@ __device__ __forceinline__ void splitk_reduce(const float* __restrict__ ws, void
     dev::store4<OUT>(Y, i * 4, t);
 }
 
+// Sum of the TAILS partials of each tail tile (ascending split order), then the
+// epilogue.  One thread per 4 consecutive outputs of a tail tile; the tile ids
+// and their positions follow gemm_mfma's split and order exactly.
+template <int BM, int BN, int TAILS, int ROUND, int GROUP_M, int OUT>
+__device__ __forceinline__ void tail_reduce(const float* __restrict__ ws, void* __restrict__ Y, int M)
+{
+    using namespace gemm_detail;
+    constexpr long TILES_N = N / BN;
+    constexpr long PER_TILE4 = (long)BM * BN / 4;
+    const long tiles_m = (M + BM - 1) / BM;
+    long n_full, rem_t;
+    tail_split(tiles_m * TILES_N, ROUND, &n_full, &rem_t);
+    const long g = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= rem_t * PER_TILE4) return;
+    const long t = g / PER_TILE4, e4 = g % PER_TILE4;
+    long tm, tn;
+    group_order<GROUP_M>(n_full + t, tiles_m, TILES_N, &tm, &tn);
+    const long row = tm * BM + (e4 * 4) / BN, col = tn * BN + (e4 * 4) % BN;
+    if (row >= M) return;
+    const f32x4* p = reinterpret_cast<const f32x4*>(ws + t * TAILS * ((long)BM * BN)) + e4;
+    f32x4 s = p[0];
+#pragma unroll
+    for (int z = 1; z < TAILS; ++z) s += p[z * PER_TILE4];
+    dev::store4<OUT>(Y, row * N + col, s);
+}
+
 // ---------------------------------------------------------------------------
 // Plain kernel for any shape: one thread per output, k ascending, f32 FMA.
 // Serves shapes no tiled candidate divides.
@@ -289,4 +419,3 @@ __device__ __forceinline__ void gemm_plain(const u16* __restrict__ X, const u16*
     for (long c = 0; c < K / 8; ++c) acc = dev::dot8(wp[c], xp[c], acc);
     dev::store1<OUT>(Y, idx, acc);
 }
-

@@ -138,6 +138,11 @@ static LaunchGeom geom(const Candidate& c, int64_t N, int64_t M)
     case Family::GemvValu: return {(unsigned)(N / (c.R * (4 / c.S))), 1u, 256u};
     case Family::GemvMfma: return {(unsigned)(N / (16 * (4 / c.S))), 1u, 256u};
     case Family::Gemm: {
+        if (c.TAILS > 1) {
+            int64_t T, n_full, rem;
+            c.tail_split(M, N, &T, &n_full, &rem);
+            return {(unsigned)(n_full + rem * c.TAILS), 1u, (unsigned)c.threads};
+        }
         const int64_t tm = (M + c.BM - 1) / c.BM;
         return {(unsigned)(tm * (N / c.BN)), (unsigned)c.SK, (unsigned)c.threads};
     }
@@ -164,11 +169,18 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
     void* args[] = {&x, &w, &y, &ws, &m};
     HIP_TRY(hipModuleLaunchKernel(c.fn, g.gx, g.gy, 1, g.threads, 1, 1, 0, stream, args, nullptr));
     if (c.needs_ws()) {
-        const int64_t total4 = M * p->N / 4;
-        const unsigned gx = (unsigned)((total4 + 255) / 256);
-        const float* wsc = ws;
-        void* rargs[] = {&wsc, &y, &m};
-        HIP_TRY(hipModuleLaunchKernel(c.reduce_fn, gx, 1, 1, 256, 1, 1, 0, stream, rargs, nullptr));
+        int64_t total4 = M * p->N / 4;              // split-K: every output
+        if (c.TAILS > 1) {                          // split tail: the tail tiles only
+            int64_t T, n_full, rem;
+            c.tail_split(M, p->N, &T, &n_full, &rem);
+            total4 = rem * c.BM * c.BN / 4;
+        }
+        if (total4 > 0) {
+            const unsigned gx = (unsigned)((total4 + 255) / 256);
+            const float* wsc = ws;
+            void* rargs[] = {&wsc, &y, &m};
+            HIP_TRY(hipModuleLaunchKernel(c.reduce_fn, gx, 1, 1, 256, 1, 1, 0, stream, rargs, nullptr));
+        }
     }
     return PROJ_OK;
 }
@@ -378,7 +390,9 @@ static bool applies(const Candidate& c, int b, const proj_plan* p)
 {
     const BucketRange br = kBuckets[b];
     if (c.max_m < br.hi) return false;
-    if (c.ws_bytes(br.hi, p->N) > p->ws_bytes) return false;
+    // every M of the bucket must fit the workspace (a split tail's need is not
+    // monotonic in M, so its bound over the bucket is used)
+    if (c.ws_bound(br.hi, p->N) > p->ws_bytes) return false;
     switch (c.fam) {
     case Family::GemvValu:
         if (b == 0) return c.MMAX == 1;
@@ -411,7 +425,7 @@ int tune_plan(proj_plan* p)
     // split-K workspace: enough for every split-K candidate at the largest block,
     // capped; a candidate then runs up to the row count the workspace holds.
     size_t need = 0;
-    for (const Candidate& c : p->cands) need = std::max(need, c.ws_bytes(kMaxBlockRows, p->N));
+    for (const Candidate& c : p->cands) need = std::max(need, c.ws_bound(kMaxBlockRows, p->N));
     need = std::min(need, ws_cap);
     if (need) {
         if (hipMalloc(&p->ws, need) != hipSuccess)
@@ -546,11 +560,12 @@ int create_plan(int64_t N, int64_t K, int dtype, proj_plan** out)
     p->dtype = dtype;
     HIP_TRY(hipGetDevice(&p->device));
     int rc;
-    if ((rc = device_arch(p->device, &p->arch, nullptr))) return rc;
+    int cus = kDefaultCUs;
+    if ((rc = device_arch(p->device, &p->arch, &cus))) return rc;
     for (int b = 0; b < kNumBuckets; ++b) p->choice[b] = -1, p->choice_us[b] = -1;
 
-    p->cands = enumerate_candidates(N, K);
-    const std::string src = emit_source(N, K, dtype, p->arch, p->cands);
+    p->cands = enumerate_candidates(N, K, cus);
+    const std::string src = emit_source(N, K, dtype, p->arch, cus, p->cands);
     const double t0 = now_s();
     std::shared_ptr<std::vector<char>> code;
     char name[96];

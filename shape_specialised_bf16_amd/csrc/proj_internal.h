@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <string>
+#include <algorithm>
 #include <vector>
 
 namespace proj {
@@ -28,6 +29,9 @@ struct Candidate {
     // GEMM parameters: block tile, k-tile, LDS buffers, wave grid, split-K,
     // tile-row group, LDS swizzle period
     int BM = 0, BN = 0, BK = 64, ST = 2, WM = 0, WN = 0, SK = 1, GM = 8, SWZ = 0;
+    int DMA = 1;  // 1: global->LDS copies; 0: copies staged through registers
+    int TAILS = 1;   // >1: whole tiles plus a tail split TAILS ways along K
+    int ROUND = 0;   // workgroups the device runs at once (CU count x blocks per CU)
 
     std::string name;          // extern "C" wrapper name in the generated module
     std::string reduce_name;   // split-K reduce kernel (empty if SK == 1)
@@ -36,21 +40,49 @@ struct Candidate {
     hipFunction_t fn = nullptr;
     hipFunction_t reduce_fn = nullptr;
 
-    bool needs_ws() const { return fam == Family::Gemm && SK > 1; }
+    bool needs_ws() const { return fam == Family::Gemm && (SK > 1 || TAILS > 1); }
+    // Tiles, whole tiles and split tail tiles of a launch at M rows (the same
+    // split as tail_split() in the device code).
+    void tail_split(int64_t M, int64_t N, int64_t* T, int64_t* n_full, int64_t* rem) const
+    {
+        *T = ((M + BM - 1) / BM) * (N / BN);
+        *rem = *T >= ROUND ? *T % ROUND : *T;
+        *n_full = *T - *rem;
+    }
     size_t ws_bytes(int64_t M, int64_t N) const
     {
-        return needs_ws() ? (size_t)SK * (size_t)M * (size_t)N * sizeof(float) : 0;
+        if (fam != Family::Gemm) return 0;
+        if (SK > 1) return (size_t)SK * (size_t)M * (size_t)N * sizeof(float);
+        if (TAILS > 1) {
+            int64_t T, nf, rem;
+            tail_split(M, N, &T, &nf, &rem);
+            return (size_t)rem * TAILS * BM * BN * sizeof(float);
+        }
+        return 0;
+    }
+    // Largest workspace any M up to max_rows can need.
+    size_t ws_bound(int64_t max_rows, int64_t N) const
+    {
+        if (TAILS > 1) {
+            const int64_t T = ((max_rows + BM - 1) / BM) * (N / BN);
+            return (size_t)std::min<int64_t>(T, ROUND) * TAILS * BM * BN * sizeof(float);
+        }
+        return ws_bytes(max_rows, N);
     }
 };
 
 // Enumerate the candidates that tile (N, K) exactly.  Always ends with the
 // plain kernel, which fits any shape.
-std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K);
+// `cus` is the device's compute-unit count (it sets the tail split's round size).
+std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus);
 
 // The full translation unit for (N, K, dtype): prelude with the shape as
 // literals, device helpers, kernel templates, one wrapper per candidate.
-std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch,
+std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
                         const std::vector<Candidate>& cands);
+
+// Compute units assumed when no device is queried (MI355X).
+constexpr int kDefaultCUs = 256;
 
 // Shape-independent support module (probe, rounding check).
 std::string emit_support_source();

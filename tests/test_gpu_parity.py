@@ -76,6 +76,34 @@ def test_every_candidate_bit_exact_on_integer_probe(N, K, dtype):
         G.log(f"  {N}x{K} {dtype} {name}: bit-exact")
 
 
+@pytest.mark.parametrize("M", [2048 + 64, 4100])
+def test_split_tail_candidates_with_whole_and_tail_tiles(M):
+    """Split-tail GEMMs at row counts where some tiles run whole and the rest as
+    K pieces: every output written (NaN-prefilled Y has no NaN left), the
+    first and the last 600 rows bit-exact on the integer probe (the tail tiles
+    are the last ones in tile order, i.e. the bottom tile-rows)."""
+    import torch
+    N, K, dtype = 7168, 1024, "f32"
+    p = G.plan(N, K, dtype)
+    W = synth.int_bf16(70, (N, K))
+    X = synth.int_bf16(71, (M, K))
+    rows = list(range(64)) + list(range(M - 600, M))
+    want = oracle.round_f32(oracle.matmul_rows(X, rows, W))
+    Xd, Wd = G.dev(X), G.dev(W)
+    names = [n for n in p.candidates() if "_tail" in n and not n.endswith("_reduce")]
+    assert names, "no split-tail candidate for this shape"
+    for name in names:
+        idx = p.candidates().index(name)
+        if p.candidate_max_m(idx) < M:
+            continue
+        Y = G.empty_out(M, N, dtype, extra_rows=1)
+        p.run_candidate(idx, Xd, Wd, Y)
+        assert int(torch.isnan(Y[:M]).sum()) == 0, f"{name}: unwritten outputs"
+        assert np.array_equal(G.host(Y)[rows], want), f"{name} M={M}"
+        assert np.all(G.host(Y)[M:].view(np.uint32) == 0x7FC00001), f"{name} wrote past M"
+        G.log(f"  {name} M={M}: bit-exact on sampled rows, all rows written")
+
+
 @pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16")])
 def test_every_candidate_within_tolerance_on_random_inputs(N, K, dtype):
     p = G.plan(N, K, dtype)

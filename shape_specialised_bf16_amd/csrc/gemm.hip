@@ -4,8 +4,8 @@
 // Prefill GEMM on MFMA (any M; block tile BM x BN, k-tile BK).
 //
 // Both operands are K-contiguous ("TN").  Each k-tile of X (BM x BK) and W
-// (BN x BK) goes straight from global memory into LDS with
-// global_load_lds_dwordx4 (DMA = 1; no trip through VGPRs): the wave's 64
+// (BN x BK) goes straight from global memory into LDS with MUBUF
+// buffer_load_dwordx4 ... lds (DMA = 1; no trip through VGPRs): the wave's 64
 // lanes fill 64 consecutive 16-byte LDS slots, and each lane fetches from
 // global memory the chunk that belongs in its slot.  With DMA = 0 the same
 // chunks go through registers (loaded before the tile's MFMAs, written to LDS
@@ -14,11 +14,12 @@
 // operand read serves at a time hit distinct banks.
 //
 // STAGES buffers form a ring: while the waves run MFMAs on tile kt, the copies
-// of tiles kt+1 .. kt+STAGES-1 are in flight.  Each wave waits only for its own
-// copies of tile kt (s_waitcnt vmcnt with the count of younger copies), then a
-// barrier makes every wave's part visible and also tells that tile kt-1's
-// buffer is free for tile kt+STAGES-1.  Each buffer is its own __shared__
-// array so the compiler can see which copy writes which buffer.
+// of tiles kt+1 .. kt+STAGES-1 are in flight.  Before the last 16-wide k step
+// of tile kt, each wave waits only for its own copies of tile kt+1 (s_waitcnt
+// vmcnt with the count of younger copies), then a barrier makes every wave's
+// part visible and also tells that tile kt's buffer is free once that step's
+// operands are in registers.  Each buffer is its own __shared__ array so the
+// compiler can see which copy writes which buffer.
 //
 // WM x WN waves; each wave owns a (BM/WM) x (BN/WN) sub-tile of 32 x 32 MFMA
 // blocks (v_mfma_f32_32x32x16_bf16, X as the A operand, W as the B operand),
@@ -187,17 +188,34 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
         aoff[i] = (unsigned)(r * K + ccol * 8);
     }
     const unsigned boff0 = (unsigned)(r0 * K + ccol * 8);
+    // The copies are MUBUF loads into LDS (buffer_load_dwordx4 ... lds) over a
+    // raw buffer descriptor per operand (gfx9 layout: base, stride 0, size in
+    // bytes, word 3 = 0x00020000) that starts at the tile's first row and
+    // covers exactly the bytes the tile reads.  Each lane's byte offset is
+    // fixed; the k-tile advances in the scalar offset.  (The global_ form of
+    // the same copy is a FLAT instruction, and while one is outstanding the
+    // compiler can only wait for all LDS reads at once.)
+    static_assert((long)(BM > BN ? BM : BN) * K * 2 < (1L << 31), "tile rows fit a 32-bit buffer size");
+    const long rows_a = (long)M - m0 < BM ? (long)M - m0 : BM;
+    const __amdgpu_buffer_rsrc_t rsa =
+        __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, (int)((rows_a * K - kbeg) * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)(((long)BN * K - kbeg) * 2), 0x00020000);
+    unsigned abyte[IA], bbyte[IB];
+#pragma unroll
+    for (int i = 0; i < IA; ++i) abyte[i] = aoff[i] * 2;
+#pragma unroll
+    for (int i = 0; i < IB; ++i) bbyte[i] = (boff0 + (unsigned)(i * RPI * K)) * 2;
     auto issue = [&](u32x4* dst, long kt) {
-        const u16* a = abase + kt * BK;
-        const u16* b = bbase + kt * BK;
+        const unsigned koff = (unsigned)(kt * BK * 2);
 #pragma unroll
         for (int i = 0; i < IA; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(a + aoff[i]),
-                                             (lds_void*)(dst + i * NTHR + wave * 64), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(dst + i * NTHR + wave * 64), 16, abyte[i],
+                                                     koff, 0, 0);
 #pragma unroll
         for (int i = 0; i < IB; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(b + boff0 + (unsigned)(i * RPI * K)),
-                                             (lds_void*)(dst + CA + i * NTHR + wave * 64), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(dst + CA + i * NTHR + wave * 64), 16,
+                                                     bbyte[i], koff, 0, 0);
     };
     u32x4 ra[DMA ? 1 : IA], rb[DMA ? 1 : IB];
     auto gload = [&](long kt) {
@@ -239,10 +257,44 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     // ---- the k loop over NKT k-tiles (a compile-time count: KT for a whole
-    //      tile, KT_TAIL for a tail piece).
+    //      tile, KT_TAIL for a tail piece).  Tile t lives in buffer t % STAGES.
+    //      The barrier that publishes tile kt+1 (and frees tile kt's buffer)
+    //      sits before the last 16-wide k step of tile kt: after it, each wave
+    //      reads the first operand fragments of tile kt+1 while the MFMAs of
+    //      that last k step, whose operands are already in registers, keep the
+    //      matrix pipe busy.  Neither the barrier nor the first operand reads of
+    //      a tile then find the pipe empty.  Operand fragments alternate between
+    //      two register slots: k step kk of a tile uses slot kk & 1.
+    bf16x8 fa[2][TM], fb[2][TN];
+    // W fragments first: the first MFMAs of a step then wait only for the reads
+    // of their own operands, not for the whole set.
+    auto read_frags = [&](const u32x4* b, int kk, int slot) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[slot][j] = frag_b(b, j, kk);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[slot][i] = frag_a(b, i, kk);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+    };
+    // Instruction order for the scheduler, per k step: the next step's operand
+    // reads first, then this step's MFMAs, so the reads have a whole step of
+    // MFMAs to land.  (While copies into LDS are in flight the compiler can
+    // only wait for all outstanding LDS reads at once, so reads slotted late
+    // between the MFMAs would stall the next step's first MFMA.)
+    auto interleave = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+    };
+
     auto kloop = [&](auto nkt) {
         constexpr long NKT = decltype(nkt)::value;
-        // prologue: tiles 0 .. STAGES-2 in flight (or tile 0 in buffer 0)
+        // prologue: tiles 0 .. STAGES-2 in flight (DMA) or tile 0 in buffer 0,
+        // then tile 0 published and its first fragments read.
         if constexpr (DMA) {
 #pragma unroll
             for (int s = 0; s < STAGES - 1; ++s) issue(buf(s), s < NKT ? s : NKT - 1);
@@ -250,77 +302,58 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
             gload(0);
             lstore(lds0);
         }
-        // One k-tile: wait for its copies, barrier, start the copy of the tile
-        // STAGES-1 ahead into the buffer freed by the previous tile, then the
-        // MFMAs.  Past the last tile the copy re-reads tile NKT-1 into a free
-        // buffer, so every step issues the same number of copies and the vmcnt
-        // bound stays exact without branches (branches here hide from the
-        // compiler which buffer a copy writes, and it then drains every copy
-        // before each LDS read).  With DMA == 0 the step loads tile kt+1 into
-        // registers before its MFMAs and writes them to the free buffer after.
-        auto step = [&](const u32x4* b, u32x4* nxt, long kt) {
+        wait_vm_lds<DMA ? (STAGES - 2) * PER_TILE : 0>();
+        barrier_lds();
+        read_frags(lds0, 0, 0);
+        // One k-tile kt in buffer b: start the copy of tile kt+STAGES-1 into
+        // buffer bd (tile kt-1's, which every wave finished reading before the
+        // previous barrier), the MFMAs of all but the last k step, then wait for
+        // this wave's copies of tile kt+1, barrier, and the last k step's MFMAs
+        // beside the reads of tile kt+1's first fragments from buffer bn.  Past
+        // the last tile the copy re-reads tile NKT-1 into a free buffer, so
+        // every step issues the same number of copies and the vmcnt bound stays
+        // exact without branches (branches here hide from the compiler which
+        // buffer a copy writes, and it then drains every copy before each LDS
+        // read).  With DMA == 0, tile kt+1 is loaded into registers before the
+        // MFMAs and written to buffer bn after them.
+        auto step = [&](const u32x4* b, u32x4* bn, u32x4* bd, long kt) {
+            const long ahead = kt + STAGES - 1;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (DMA) issue(bd, ahead < NKT ? ahead : NKT - 1);
+            else gload(ahead < NKT ? ahead : NKT - 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk + 1 < KK; ++kk) {
+                read_frags(b, kk + 1, (kk + 1) & 1);
+                mfmas(kk & 1);
+            }
+#pragma unroll
+            for (int kk = 0; kk + 1 < KK; ++kk) interleave();
+            if constexpr (!DMA) {
+                __builtin_amdgcn_sched_barrier(0);
+                lstore(bn);
+            }
             __builtin_amdgcn_sched_barrier(0);
             wait_vm_lds<DMA ? (STAGES - 2) * PER_TILE : 0>();
             barrier_lds();
-            const long ahead = kt + STAGES - 1;
-            if constexpr (DMA) issue(nxt, ahead < NKT ? ahead : NKT - 1);
-            else gload(ahead < NKT ? ahead : NKT - 1);
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 fa[2][TM], fb[2][TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) fa[0][i] = frag_a(b, i, 0);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb[0][j] = frag_b(b, j, 0);
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const int cur = kk & 1;
-                if (kk + 1 < KK) {
-#pragma unroll
-                    for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = frag_a(b, i, kk + 1);
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = frag_b(b, j, kk + 1);
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j],
-                                                                            0, 0, 0);
-            }
-            // Instruction order for the scheduler: the first step's operand reads,
-            // then, for each step, its MFMAs with the next step's reads slotted in
-            // between them, so those reads are in flight while the MFMA pipe works
-            // (left to itself the scheduler keeps one set of operand registers and
-            // waits on every read).
-            constexpr int NMF = TM * TN, NRD = TM + TN;
-            constexpr int PAIRS = NMF < NRD ? NMF : NRD;
-            __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-#pragma unroll
-            for (int kk = 0; kk + 1 < KK; ++kk) {
-#pragma unroll
-                for (int r = 0; r < PAIRS; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                if constexpr (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
-                if constexpr (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
-            if constexpr (!DMA) {
-                __builtin_amdgcn_sched_barrier(0);
-                lstore(nxt);
-            }
+            read_frags(bn, 0, 0);
+            mfmas((KK - 1) & 1);
+            interleave();
+        };
+        auto ring = [&](auto r, long kt) {
+            constexpr int R = decltype(r)::value;
+            step(buf(R), buf((R + 1) % STAGES), buf((R + STAGES - 1) % STAGES), kt);
         };
         constexpr long KMAIN = NKT - NKT % STAGES;
         for (long kt = 0; kt < KMAIN; kt += STAGES) {
-            step(lds0, buf(STAGES - 1), kt);
-            step(lds1, lds0, kt + 1);
-            if constexpr (STAGES > 2) step(lds2, lds1, kt + 2);
-            if constexpr (STAGES > 3) step(lds3, lds2, kt + 3);
+            ring(ic<0>{}, kt);
+            ring(ic<1>{}, kt + 1);
+            if constexpr (STAGES > 2) ring(ic<2>{}, kt + 2);
+            if constexpr (STAGES > 3) ring(ic<3>{}, kt + 3);
         }
-        if constexpr (NKT % STAGES > 0) step(lds0, buf(STAGES - 1), KMAIN);
-        if constexpr (NKT % STAGES > 1) step(lds1, lds0, KMAIN + 1);
-        if constexpr (NKT % STAGES > 2) step(lds2, lds1, KMAIN + 2);
+        if constexpr (NKT % STAGES > 0) ring(ic<0>{}, KMAIN);
+        if constexpr (NKT % STAGES > 1) ring(ic<1>{}, KMAIN + 1);
+        if constexpr (NKT % STAGES > 2) ring(ic<2>{}, KMAIN + 2);
         wait_vm_lds<0>();   // no copy may still write LDS when the block ends
     };
 

@@ -59,10 +59,10 @@ def traffic_for(key: str):
     return round(e["bytes_per_launch"])
 
 
-def profile_mode(which: str, launches: int = 30):
+def profile_mode(which: str, prefill_m: int = 2048, launches: int = 30):
     """Only the dominant kernel of one bench leg at its bench configuration --
     the decode head GEMV (151936x1024, M=1, f32 out, rotating weight copies) or
-    the prefill gate/up GEMM (18432x2560, M=2048, bf16 out) -- then a 1 GiB
+    the prefill gate/up GEMM (18432x2560, M=prefill_m, bf16 out) -- then a 1 GiB
     device copy of known size that calibrates the FETCH_SIZE / WRITE_SIZE
     counters; for rocprofv3 counter runs."""
     import torch
@@ -73,7 +73,7 @@ def profile_mode(which: str, launches: int = 30):
     if which == "decode":
         cfg, pi, M, dt = synth.CONFIGS[1], len(synth.CONFIGS[1].projections) - 1, 1, "f32"
     else:
-        cfg, pi, M, dt = synth.CONFIGS[2], 2, 2048, "bf16"
+        cfg, pi, M, dt = synth.CONFIGS[2], 2, prefill_m, "bf16"
     p = cfg.projections[pi]
     plan = Plan(p.N, p.K, dt)
     W = upload(synth.weights(cfg, pi))
@@ -256,6 +256,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-m", type=int, default=2048, choices=[512, 2048],
+                    help="row count of the prefill GEMM in --mode profile-prefill")
     ap.add_argument("--mode", default="full", choices=["full", "profile-decode", "profile-prefill"],
                     help="profile-*: only that leg's dominant kernel and a calibration copy, for rocprofv3 "
                          "counter runs")
@@ -265,7 +267,7 @@ def main():
               "by output rows across GPUs but no multi-GPU path is built", file=sys.stderr)
         sys.exit(2)
     if args.mode != "full":
-        profile_mode(args.mode.split("-")[1])
+        profile_mode(args.mode.split("-")[1], args.prefill_m)
         return
 
     import torch

@@ -95,17 +95,21 @@ def _counter(path: str, counter: str):
     return out
 
 
-def _per_launch(vals, name):
-    v = [x for n, x in vals.values() if name in n]
+def _per_launch(vals, name, last):
+    """Median over the last `last` dispatches of kernel `name` (the profiled
+    loop's own launches; the load-time tuner runs the same kernel earlier, at
+    other row counts).  The name must match exactly: a split-tail GEMM's second
+    pass is named after it ("<name>_reduce")."""
+    v = [vals[d][1] for d in sorted(vals) if vals[d][0].strip() == name][-last:]
     if not v:
         raise SystemExit(f"kernel {name!r} not found in counter output")
     return statistics.median(v)
 
 
-def traffic(fetch_dir, write_dir, kernel, calib, calib_bytes):
+def traffic(fetch_dir, write_dir, kernel, calib, calib_bytes, last=5):
     f = _counter(fetch_dir, "FETCH_SIZE")
     w = _counter(write_dir, "WRITE_SIZE")
-    f_k, w_k = _per_launch(f, kernel), _per_launch(w, kernel)
+    f_k, w_k = _per_launch(f, kernel, last), _per_launch(w, kernel, last)
     # the calibration copy is the largest dispatch of its name (small copies of the
     # same blit kernel also occur while plans are built)
     f_c = max(x for n, x in f.values() if calib in n)
@@ -133,13 +137,14 @@ def main(argv=None):
     t.add_argument("--calib-bytes", type=float, required=True)
     t.add_argument("--out")
     t.add_argument("--key")
+    t.add_argument("--last", type=int, default=5, help="dispatches of the kernel to use, counted from the end")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         for r in stats(a.path, a.match, a.stream):
             print(f"{r['kernel'][:48]:48s} grid {r['grid']:10d} calls {r['calls']:5d}  mean {r['mean_us']:9.3f} us  "
                   f"min {r['min_us']:10.3f}  max {r['max_us']:10.3f}  total {r['total_us']:12.1f}")
     else:
-        r = traffic(a.fetch, a.write, a.kernel, a.calib, a.calib_bytes)
+        r = traffic(a.fetch, a.write, a.kernel, a.calib, a.calib_bytes, a.last)
         r["source_sha"] = kernel_source_sha(a.kernel)
         print(json.dumps(r, indent=1))
         if a.out:

@@ -10,6 +10,10 @@ total) so that no step finds them in the 256 MB last-level cache -- a decode
 step re-reads every weight, as in the pages' "Ce que coute un token" ("#001 un
 compilateur pour moteur de LLM").
 
+The timed steps launch the five proj_run calls one by one on torch's current
+stream; the same steps recorded as a HIP graph and replayed are timed after
+them and reported under "graph".
+
 Reported (one JSON line on stdout):
   value      decode HBM GB/s = algorithmic bytes of the step / step time
   roofline   the head GEMV (the step's dominant kernel): its algorithmic bytes
@@ -126,44 +130,70 @@ def time_decode(steps: int, warmup: int):
     sh = __import__("ctypes").c_void_p(stream.cuda_stream)
     head = len(projs) - 1
     head_bytes = 2 * projs[head].N * projs[head].K + 2 * projs[head].K + 4 * projs[head].N
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
 
-    def step(s, record):
+    def step(s, h):
         c = s % copies
         for i in range(len(projs)):
-            if record and i == head:
-                ev[s][0].record(stream)
-            plans[i].run_ptr(Xs[i].data_ptr(), Wrot[i][c].data_ptr(), Ys[i].data_ptr(), 1, sh)
-            if record and i == head:
-                ev[s][1].record(stream)
+            plans[i].run_ptr(Xs[i].data_ptr(), Wrot[i][c].data_ptr(), Ys[i].data_ptr(), 1, h)
+
+    def elapsed_us(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for s in range(n):
+            fn(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
 
     for s in range(warmup):
-        step(s, False)
+        step(s, sh)
     torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for s in range(steps):
-        step(s, True)
-    t_end.record(stream)
+    # the timed region: exactly `steps` steps, five proj_run calls each, nothing else
+    ms_per_step = elapsed_us(lambda s: step(s, sh), steps) / steps / 1e3
+
+    # Diagnostics, untimed: (1) the head inside the step, with an event pair
+    # around it (the events themselves lengthen the step, which is why the timed
+    # loop has none); (2) the head alone, back to back (the roofline figure);
+    # (3) the same steps recorded as one HIP graph per rotation of the weight
+    # copies (proj_run only enqueues kernels -- no allocation, synchronisation
+    # or memset -- so it records), replayed.
+    n_in = 200
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_in)]
+    for s in range(n_in):
+        c = s % copies
+        for i in range(len(projs)):
+            if i == head:
+                ev[s][0].record(stream)
+            plans[i].run_ptr(Xs[i].data_ptr(), Wrot[i][c].data_ptr(), Ys[i].data_ptr(), 1, sh)
+            if i == head:
+                ev[s][1].record(stream)
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    in_step_us = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
-    ms_per_step = ms_total / steps
-    # The head alone, back to back on the same stream (rotating weight copies):
-    # with no other kernel between launches the event pair brackets kernel time
-    # plus the per-launch dispatch gap only.
+    in_step_us = sum(a.elapsed_time(b) for a, b in ev) / n_in * 1e3
     reps = 100
-    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    h0.record(stream)
-    for s in range(reps):
-        plans[head].run_ptr(Xs[head].data_ptr(), Wrot[head][s % copies].data_ptr(), Ys[head].data_ptr(), 1, sh)
-    h1.record(stream)
+    head_us = elapsed_us(lambda s: plans[head].run_ptr(Xs[head].data_ptr(), Wrot[head][s % copies].data_ptr(),
+                                                       Ys[head].data_ptr(), 1, sh), reps) / reps
+    gs = torch.cuda.Stream()
+    gh = __import__("ctypes").c_void_p(gs.cuda_stream)
+    g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
-    head_us = h0.elapsed_time(h1) / reps * 1e3
-    # correctness of what was timed: the last step's head output vs the oracle (sampled)
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(g, stream=gs):
+            for c in range(copies):
+                step(c, gh)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, steps // copies)
+    graph_ms_per_step = elapsed_us(lambda s: g.replay(), n_rep) / (n_rep * copies) / 1e3
+    # the last work on Ys was a graph replay of a whole rotation; rerun one eager
+    # step so the checked outputs are the timed path's own
+    step(0, sh)
+    torch.cuda.synchronize()
+    # correctness of what was timed: the last replay's outputs are checked against the oracle
     return dict(plans=plans, projs=projs, host=host, Ys=Ys, step_bytes=step_bytes, ms_per_step=ms_per_step,
-                head_us=head_us, in_step_us=in_step_us, head_bytes=head_bytes,
-                head_kernel=plans[head].choice(1), copies=copies)
+                graph_ms_per_step=graph_ms_per_step, graph_steps=n_rep * copies, head_us=head_us,
+                in_step_us=in_step_us, head_bytes=head_bytes, head_kernel=plans[head].choice(1), copies=copies,
+                graph=g)
 
 
 def time_prefill(reps: int = 20):
@@ -279,9 +309,11 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
     d = time_decode(args.steps, args.warmup)
     value = d["step_bytes"] / (d["ms_per_step"] * 1e-3) / 1e9
+    graph_value = d["step_bytes"] / (d["graph_ms_per_step"] * 1e-3) / 1e9
     achieved = d["head_bytes"] / (d["head_us"] * 1e-6) / 1e9
-    log(f"decode: {d['ms_per_step'] * 1e3:.2f} us/step, {value:.0f} GB/s; head {d['head_kernel']} "
-        f"{d['head_us']:.2f} us = {achieved:.0f} GB/s")
+    log(f"decode: {d['ms_per_step'] * 1e3:.2f} us/step, {value:.0f} GB/s; as HIP graph replays "
+        f"{d['graph_ms_per_step'] * 1e3:.2f} us/step, {graph_value:.0f} GB/s; "
+        f"head {d['head_kernel']} {d['head_us']:.2f} us = {achieved:.0f} GB/s")
     # check the timed outputs (last step) against the oracle on the head row sample
     for (X, W), Y, p in zip(d["host"], d["Ys"], d["projs"]):
         ref = oracle.matmul(X, W, threads=min(16, os.cpu_count() or 1))
@@ -309,8 +341,13 @@ def main():
             "M": 1,
             "bytes_per_step": d["step_bytes"],
             "weight_copies_rotated": d["copies"],
+            "launch": "five proj_run calls per step on torch's current stream",
             "parallelism": "single GPU",
         },
+        "graph": {"ms_per_step": round(d["graph_ms_per_step"], 5), "value": round(graph_value, 1),
+                  "steps": d["graph_steps"],
+                  "launch": f"one HIP graph recording {d['copies']} steps (a rotation of the weight copies), "
+                            "replayed"},
         "roofline": {
             "bound": "hbm",
             "kernel": d["head_kernel"],
@@ -321,10 +358,13 @@ def main():
             "traffic": traffic_for(d["head_kernel"] + "@151936x1024"),
             "bytes_per_launch": d["head_bytes"],
             "mean_launch_us": round(d["head_us"], 3),
-            "timing": "HIP events around 100 back-to-back launches on the launch stream, after the timed steps",
+            "timing": "HIP events around 100 back-to-back launches on the launch stream, after the timed steps; "
+                      "in_step_launch_us: an event pair around the head inside 200 further steps",
             "in_step_launch_us": round(d["in_step_us"], 3),
         },
     }
+    del d["graph"]
+    torch.cuda.synchronize()
     for p in d["plans"]:
         p.close()
     torch.cuda.synchronize()

@@ -83,6 +83,13 @@ proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
  * misaligned pointers, or a current device other than the plan's give
  * PROJ_EINVAL; a failed launch gives PROJ_EDEVICE.  M above 8192 is processed
  * as consecutive blocks of at most 8192 rows.
+ *
+ * Only kernel launches are enqueued (one, or two for split-K and split-tail
+ * kernels whose second pass sums f32 partials kept in the plan's workspace):
+ * no allocation, no synchronisation, no memset, so the call may be recorded
+ * into a HIP graph by stream capture.  Calls on one plan share its workspace:
+ * they must not run concurrently (different streams without ordering, or
+ * overlapping graph replays).
  */
 int proj_run(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M,
              hipStream_t stream);

@@ -1,0 +1,85 @@
+"""proj_run recorded into a HIP graph and replayed.
+
+A decode step (the GEMV path) and prefill launches that use the plan's
+workspace (a split-K GEMM and a split-tail GEMM, both with their second pass)
+are captured once, then the graph is replayed several times with the program's
+own eager work -- the same plans run eagerly on other buffers, which reuses the
+same workspace, torch ops, synchronisations -- between the replays.  Every
+replay must reproduce the eager result bit for bit.
+"""
+import pytest
+
+import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _pick(p, pattern, M):
+    for idx, name in enumerate(p.candidates()):
+        if pattern(name) and p.candidate_max_m(idx) >= M:
+            return idx, name
+    pytest.skip(f"no candidate for {pattern} at M={M}")
+
+
+def test_graph_replay_matches_eager():
+    import torch
+
+    # decode: two GEMV projections at M=1 through the tuned choice
+    dec = []
+    for i, (N, K) in enumerate([(2048, 1024), (1024, 3072)]):
+        p = G.plan(N, K, "f32")
+        W = G.dev(synth.normal_bf16(80, 2 * i, (N, K), 0.02))
+        X = G.dev(synth.normal_bf16(80, 2 * i + 1, (1, K), 1.0))
+        dec.append((p, X, W, N))
+    # prefill: a split-K and a split-tail candidate of one plan (both use the workspace)
+    N, K = 7168, 1024
+    pg = G.plan(N, K, "f32")
+    Wg = G.dev(synth.normal_bf16(81, 0, (N, K), 0.02))
+    Xg = G.dev(synth.normal_bf16(81, 1, (2112, K), 1.0))
+    sk_idx, sk_name = _pick(pg, lambda n: "_sk2" in n or "_sk4" in n, 300)
+    tl_idx, tl_name = _pick(pg, lambda n: "_tail" in n and not n.endswith("_reduce"), 2112)
+
+    def launch(outs):
+        for (p, X, W, _), Y in zip(dec, outs[:2]):
+            p.run(X, W, Y)
+        pg.run_candidate(sk_idx, Xg[:300], Wg, outs[2])
+        pg.run_candidate(tl_idx, Xg, Wg, outs[3])
+
+    def fresh():
+        return [G.empty_out(1, n, "f32") for (_, _, _, n) in dec] + \
+               [G.empty_out(300, N, "f32"), G.empty_out(2112, N, "f32")]
+
+    ref = fresh()
+    launch(ref)
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ref]
+
+    outs = fresh()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    launch(outs)                          # warm-up on the eager stream before capture
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            launch(outs)
+    torch.cuda.synchronize()
+
+    scratch = fresh()
+    for rep in range(4):
+        for y in outs:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), \
+                f"replay {rep}: output {k} ({sk_name if k == 2 else tl_name if k == 3 else 'decode'}) differs"
+        # eager work between replays: same plans, other buffers, same workspace
+        launch(scratch)
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(scratch, ref)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"eager run {rep}: output {k} differs"
+        for y in scratch:
+            y.zero_()
+    G.log(f"  graph of 2 GEMVs + {sk_name} + {tl_name}: 4 replays bit-identical to eager")

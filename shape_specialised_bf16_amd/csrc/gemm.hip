@@ -17,9 +17,10 @@
 // of tiles kt+1 .. kt+STAGES-1 are in flight.  Before the last 16-wide k step
 // of tile kt, each wave waits only for its own copies of tile kt+1 (s_waitcnt
 // vmcnt with the count of younger copies), then a barrier makes every wave's
-// part visible and also tells that tile kt's buffer is free once that step's
-// operands are in registers.  Each buffer is its own __shared__ array so the
-// compiler can see which copy writes which buffer.
+// part visible and also tells that every wave has read all of tile kt (the
+// last step's operands are in registers), so the copy of tile kt+STAGES goes
+// into tile kt's buffer at once.  Each buffer is its own __shared__ array so
+// the compiler can see which copy writes which buffer.
 //
 // WM x WN waves; each wave owns a (BM/WM) x (BN/WN) sub-tile of 32 x 32 MFMA
 // blocks (v_mfma_f32_32x32x16_bf16, X as the A operand, W as the B operand),
@@ -129,7 +130,11 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     static_assert(CA % NTHR == 0 && CB % NTHR == 0, "copies split evenly over threads");
     constexpr int IA = CA / NTHR, IB = CB / NTHR;     // copy instructions per thread per tile
     constexpr int PER_TILE = IA + IB;
-    static_assert((STAGES - 2) * PER_TILE <= 63, "younger copies fit the vmcnt counter");
+    // EARLY: the copy of tile kt+STAGES is issued right after the barrier inside
+    // step kt; otherwise that of tile kt+STAGES-1 at the start of step kt.
+    constexpr bool EARLY = DMA && STAGES == 2;
+    constexpr int LEAD = EARLY ? STAGES : STAGES - 1;   // tiles in flight after the prologue
+    static_assert((LEAD - 1) * PER_TILE <= 63, "younger copies fit the vmcnt counter");
     constexpr int STAGE = CA + CB;                    // 16-byte slots per buffer
     constexpr long TILES_N = N / BN;
     constexpr int KK = BK / 16;                       // MFMA k-steps per tile
@@ -237,15 +242,20 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     // ---- operand fragment addressing (slot of lane's row/chunk within a buffer)
     const int lrow = lane & 31;
     const int lhalf = lane >> 5;
+    // The swizzle of a row does not change in 32-row steps, so each lane's
+    // chunk for k step kk is (2*kk) ^ q with a per-lane q, and the 32-row steps
+    // of a fragment are constant offsets (immediates of the LDS read).
+    static_assert((32 >> SWZ) % CPR == 0, "32-row steps keep the swizzle");
+    const int rowa0 = wm * WTM + lrow, rowb0 = wn * WTN + lrow;
+    const int qa = lhalf ^ ((rowa0 >> SWZ) & (CPR - 1));
+    const int qb = lhalf ^ ((rowb0 >> SWZ) & (CPR - 1));
     auto frag_a = [&](const u32x4* b, int i, int kk) -> bf16x8 {
-        const int row = wm * WTM + i * 32 + lrow;
-        const int c = kk * 2 + lhalf;
-        return __builtin_bit_cast(bf16x8, b[row * CPR + (c ^ ((row >> SWZ) & (CPR - 1)))]);
+        const u32x4* p = b + rowa0 * CPR + ((kk * 2) ^ qa);
+        return __builtin_bit_cast(bf16x8, p[i * 32 * CPR]);
     };
     auto frag_b = [&](const u32x4* b, int j, int kk) -> bf16x8 {
-        const int row = wn * WTN + j * 32 + lrow;
-        const int c = kk * 2 + lhalf;
-        return __builtin_bit_cast(bf16x8, b[CA + row * CPR + (c ^ ((row >> SWZ) & (CPR - 1)))]);
+        const u32x4* p = b + CA + rowb0 * CPR + ((kk * 2) ^ qb);
+        return __builtin_bit_cast(bf16x8, p[j * 32 * CPR]);
     };
 
     f32x16 acc[TM][TN];
@@ -293,34 +303,36 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 
     auto kloop = [&](auto nkt) {
         constexpr long NKT = decltype(nkt)::value;
-        // prologue: tiles 0 .. STAGES-2 in flight (DMA) or tile 0 in buffer 0,
-        // then tile 0 published and its first fragments read.
+        // prologue: tiles 0 .. LEAD-1 in flight, one per buffer (DMA), or tile 0
+        // in buffer 0; then tile 0 published and its first fragments read.
         if constexpr (DMA) {
 #pragma unroll
-            for (int s = 0; s < STAGES - 1; ++s) issue(buf(s), s < NKT ? s : NKT - 1);
+            for (int s = 0; s < LEAD; ++s) issue(buf(s), s < NKT ? s : NKT - 1);
         } else {
             gload(0);
             lstore(lds0);
         }
-        wait_vm_lds<DMA ? (STAGES - 2) * PER_TILE : 0>();
+        wait_vm_lds<DMA ? (LEAD - 1) * PER_TILE : 0>();
         barrier_lds();
         read_frags(lds0, 0, 0);
-        // One k-tile kt in buffer b: start the copy of tile kt+STAGES-1 into
-        // buffer bd (tile kt-1's, which every wave finished reading before the
-        // previous barrier), the MFMAs of all but the last k step, then wait for
-        // this wave's copies of tile kt+1, barrier, and the last k step's MFMAs
-        // beside the reads of tile kt+1's first fragments from buffer bn.  Past
-        // the last tile the copy re-reads tile NKT-1 into a free buffer, so
-        // every step issues the same number of copies and the vmcnt bound stays
-        // exact without branches (branches here hide from the compiler which
-        // buffer a copy writes, and it then drains every copy before each LDS
-        // read).  With DMA == 0, tile kt+1 is loaded into registers before the
-        // MFMAs and written to buffer bn after them.
-        auto step = [&](const u32x4* b, u32x4* bn, u32x4* bd, long kt) {
-            const long ahead = kt + STAGES - 1;
+        // One k-tile kt in buffer b: the MFMAs of all but the last k step, then
+        // wait for this wave's copies of tile kt+1, barrier -- every wave has
+        // now read all of tile kt and written its part of tile kt+1 -- then the
+        // last k step's MFMAs beside the reads of tile kt+1's first fragments
+        // from buffer bn.  The copy of the next tile to fetch goes out right
+        // after that barrier into buffer b (EARLY: two buffers, so a copy gets
+        // a whole step between issue and wait) or at the start of the step into
+        // buffer bd, tile kt-1's (three or more buffers: already STAGES-1.75
+        // steps ahead).  Past the last tile the copy re-reads tile NKT-1 into
+        // the free buffer, so every step issues the same number of copies and
+        // the vmcnt bound stays exact without branches (branches here hide from
+        // the compiler which buffer a copy writes, and it then drains every copy
+        // before each LDS read).  With DMA == 0, tile kt+1 is loaded into
+        // registers before the MFMAs and written to buffer bn after them.
+        auto step = [&](u32x4* b, u32x4* bn, u32x4* bd, long kt) {
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (DMA) issue(bd, ahead < NKT ? ahead : NKT - 1);
-            else gload(ahead < NKT ? ahead : NKT - 1);
+            if constexpr (!DMA) gload(kt + 1 < NKT ? kt + 1 : NKT - 1);
+            else if constexpr (!EARLY) issue(bd, kt + LEAD < NKT ? kt + LEAD : NKT - 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk + 1 < KK; ++kk) {
@@ -337,8 +349,23 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
             wait_vm_lds<DMA ? (STAGES - 2) * PER_TILE : 0>();
             barrier_lds();
             read_frags(bn, 0, 0);
+            if constexpr (EARLY) issue(b, kt + LEAD < NKT ? kt + LEAD : NKT - 1);
             mfmas((KK - 1) & 1);
-            interleave();
+            // the reads first, then the MFMAs with any copies slotted between them
+            __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+            if constexpr (EARLY) {
+                constexpr int NMF = TM * TN;
+                constexpr int PAIRS = NMF < PER_TILE ? NMF : PER_TILE;
+#pragma unroll
+                for (int r = 0; r < PAIRS; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+                if constexpr (NMF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+                if constexpr (PER_TILE > PAIRS) __builtin_amdgcn_sched_group_barrier(0x020, PER_TILE - PAIRS, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+            }
         };
         auto ring = [&](auto r, long kt) {
             constexpr int R = decltype(r)::value;

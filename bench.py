@@ -243,6 +243,160 @@ def time_prefill(reps: int = 20):
     return out
 
 
+def _check_rows(Y, X, W, rows, dtype, label):
+    """Sampled rows of a timed output against the oracle (tolerance of its dtype)."""
+    import numpy as np
+
+    import oracle
+    from oracle import tolerance
+    ref = oracle.matmul_rows(X, rows, W)
+    got = Y[rows].cpu()
+    if dtype == "bf16":
+        rep = tolerance.check_bf16(got.view(__import__("torch").int16).numpy().view(np.uint16), ref)
+    else:
+        rep = tolerance.check_f32(got.numpy(), ref)
+    if not rep.ok:
+        raise SystemExit(f"bench: {label} does not match the oracle: {rep}")
+
+
+def time_long_prompt(reps: int = 5):
+    """The caller-side prompt-block driver: 8192 prompt rows through each 4B-like
+    projection as 8 blocks of 1024 (block-major: every projection of block b,
+    then block b+1), then the 151936 x 2560 head on the last row only."""
+    import torch
+
+    import synth
+    from shape_specialised_bf16_amd import Plan
+
+    cfg = synth.CONFIGS[3]
+    rows_total, block = cfg.extra["prompt_rows"], cfg.extra["block"]
+    layer = [p for p in cfg.projections if p.name != "head"]
+    head = [p for p in cfg.projections if p.name == "head"][0]
+    hi = cfg.projections.index(head)
+    plans = [Plan(p.N, p.K, "bf16") for p in layer]
+    hplan = Plan(head.N, head.K, "f32")
+    host = [(synth.activations(cfg, i, rows_total), synth.weights(cfg, i)) for i in range(len(layer))]
+    Xs = [upload(x) for x, _ in host]
+    Ws = [upload(w) for _, w in host]
+    Ys = [torch.empty((rows_total, p.N), dtype=torch.bfloat16, device="cuda") for p in layer]
+    hx, hw = synth.activations(cfg, hi, 1), synth.weights(cfg, hi)
+    HX, HW = upload(hx), upload(hw)
+    logits = torch.empty((1, head.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = __import__("ctypes").c_void_p(stream.cuda_stream)
+
+    def prompt():
+        for b in range(rows_total // block):
+            for i, p in enumerate(layer):
+                plans[i].run_ptr(Xs[i].data_ptr() + b * block * p.K * 2, Ws[i].data_ptr(),
+                                 Ys[i].data_ptr() + b * block * p.N * 2, block, sh)
+        hplan.run_ptr(HX.data_ptr(), HW.data_ptr(), logits.data_ptr(), 1, sh)
+
+    prompt()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        prompt()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    for i, p in enumerate(layer):
+        _check_rows(Ys[i], *host[i], [0, block - 1, block, rows_total - 1], "bf16", f"long prompt {p.name}")
+    _check_rows(logits, hx, hw, [0], "f32", "long prompt head")
+    flops = 2.0 * rows_total * sum(p.N * p.K for p in layer) + 2.0 * head.N * head.K
+    out = dict(workload=f"long_prompt_4b: {rows_total} rows as {rows_total // block} blocks of {block} through "
+                        "QKV 2560->5120, out 4096->2560, gate/up 2560->18432, down 9216->2560 (bf16 Y), then the "
+                        "head 2560->151936 on the last row (f32 Y)",
+               value=round(flops / us / 1e6, 1), unit="TFLOP/s", prompt_us=round(us, 1),
+               pct_peak=round(100 * flops / us / 1e6 / MFMA_BF16_PEAK_TFS, 1),
+               kernels={p.name: plans[i].choice(block) for i, p in enumerate(layer)} | {"head": hplan.choice(1)})
+    log(f"  long prompt: {out['value']} TFLOP/s ({us:.0f} us per 8192-row prompt)")
+    for pl in plans + [hplan]:
+        pl.close()
+    return out
+
+
+def time_27b(steps: int = 500, warmup: int = 20, reps: int = 5):
+    """27B-like layer (weights with 1 % outliers x10, bf16 Y): the four
+    projections at M = 1 (rotating weight copies, as the decode leg) and at
+    M = 8192."""
+    import torch
+
+    import synth
+    from shape_specialised_bf16_amd import Plan
+
+    cfg = synth.CONFIGS[4]
+    projs = cfg.projections
+    plans = [Plan(p.N, p.K, "bf16") for p in projs]
+    Wh = [synth.weights(cfg, i) for i in range(len(projs))]
+    Ws = [upload(w) for w in Wh]
+    layer_bytes = sum(w.numel() * 2 for w in Ws)
+    copies = max(2, -(-ROTATE_BYTES // layer_bytes))
+    Wrot = [[w] + [w.clone() for _ in range(copies - 1)] for w in Ws]
+    stream = torch.cuda.current_stream()
+    sh = __import__("ctypes").c_void_p(stream.cuda_stream)
+    out = {"workload": "layer_27b: QKV 5120->10240, out 8192->5120, gate/up 5120->34816, down 17408->5120, "
+                       "weights ~N(0, 0.01) with 1 % outliers x10, bf16 Y"}
+    # M = 1
+    X1h = [synth.activations(cfg, i, 1) for i in range(len(projs))]
+    X1 = [upload(x) for x in X1h]
+    Y1 = [torch.empty((1, p.N), dtype=torch.bfloat16, device="cuda") for p in projs]
+
+    def step(s):
+        c = s % copies
+        for i in range(len(projs)):
+            plans[i].run_ptr(X1[i].data_ptr(), Wrot[i][c].data_ptr(), Y1[i].data_ptr(), 1, sh)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    step_bytes = sum(2 * p.N * p.K + 2 * p.K + 2 * p.N for p in projs)
+    for i, p in enumerate(projs):
+        _check_rows(Y1[i], X1h[i], Wh[i], [0], "bf16", f"27b {p.name} M=1")
+    out["decode_m1"] = dict(value=round(step_bytes / us / 1e3, 1), unit="GB/s", step_us=round(us, 2),
+                            pct_peak=round(100 * step_bytes / us / 1e3 / HBM_PEAK_GBS, 1),
+                            bytes_per_step=step_bytes, weight_copies_rotated=copies,
+                            kernels={p.name: plans[i].choice(1) for i, p in enumerate(projs)})
+    log(f"  27B decode M=1: {out['decode_m1']['value']} GB/s ({us:.1f} us per layer)")
+    del Wrot, X1, Y1
+    # M = 8192
+    M = 8192
+    per, flops = [], 0.0
+    for i, p in enumerate(projs):
+        xh = synth.activations(cfg, i, M)
+        X = upload(xh)
+        Y = torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda")
+        plans[i].run(X, Ws[i], Y)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            plans[i].run(X, Ws[i], Y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e3
+        f = 2.0 * M * p.N * p.K
+        flops += f
+        _check_rows(Y, xh, Wh[i], [0, 4095, M - 1], "bf16", f"27b {p.name} M={M}")
+        per.append(dict(proj=p.name, N=p.N, K=p.K, kernel=plans[i].choice(M), us=round(t, 1),
+                        tflops=round(f / t / 1e6, 1)))
+        del X, Y
+    tot = sum(x["us"] for x in per)
+    out["prefill_m8192"] = dict(value=round(flops / tot / 1e6, 1), unit="TFLOP/s", layer_us=round(tot, 1),
+                                pct_peak=round(100 * flops / tot / 1e6 / MFMA_BF16_PEAK_TFS, 1), projections=per)
+    log(f"  27B prefill M=8192: {out['prefill_m8192']['value']} TFLOP/s ({tot:.0f} us per layer)")
+    for pl in plans:
+        pl.close()
+    return out
+
+
 def probe_bandwidth():
     import torch
     import shape_specialised_bf16_amd as ssb
@@ -286,6 +440,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-prompt and 27B-layer legs")
     ap.add_argument("--prefill-m", type=int, default=2048, choices=[512, 2048],
                     help="row count of the prefill GEMM in --mode profile-prefill")
     ap.add_argument("--mode", default="full", choices=["full", "profile-decode", "profile-prefill"],
@@ -373,6 +528,11 @@ def main():
     if not args.no_prefill:
         result["prefill"] = {"workload": "prefill_4b_layer: QKV 2560->5120, out 4096->2560, gate/up "
                                          "2560->18432, down 9216->2560, Y bf16", **time_prefill()}
+    if not args.no_extra:
+        result["long_prompt"] = time_long_prompt()
+        torch.cuda.empty_cache()
+        result["layer_27b"] = time_27b()
+        torch.cuda.empty_cache()
     result["cpu_baseline"] = None if args.no_cpu else cpu_baseline(d["host"], d["step_bytes"])
     print(json.dumps(result), flush=True)
 

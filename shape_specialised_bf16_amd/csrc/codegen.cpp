@@ -61,6 +61,19 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus)
         c.max_m = v.MMAX;
         c.name = fmt("gemv_valu_r%d_s%d_m%d_u%d_nt%d", c.R, c.S, c.MMAX, c.U, c.NT);
         out.push_back(c);
+        // the same with pipelined batches: the largest U that still leaves a
+        // wave two batches or more
+        if (v.MMAX == 1 && v.NT == 1) {
+            int Up = 0;
+            for (int u : {4, 2, 1})
+                if (trips > 0 && trips % u == 0 && u * v.R <= 8 && trips / u >= 2) { Up = u; break; }
+            if (Up) {
+                c.U = Up;
+                c.P = 1;
+                c.name = fmt("gemv_valu_r%d_s%d_m%d_u%d_nt%d_p", c.R, c.S, c.MMAX, c.U, c.NT);
+                out.push_back(c);
+            }
+        }
     }
 
     // ---- MFMA skinny GEMV for M <= 16: (S waves splitting K, U MFMA steps per load batch)
@@ -176,8 +189,8 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
               << " tail lanes, weight row stride " << 2 * K << " B\n";
             s << "static_assert(K_BLOCKS16 / " << c.S << " / 64 == " << chs / 64 << ", \"trip count\");\n";
             s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_valu<"
-              << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out
-              << ">(X, W, Y, M); }\n";
+              << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out << ", "
+              << c.P << ">(X, W, Y, M); }\n";
             break;
         }
         case Family::GemvMfma: {

@@ -11,10 +11,16 @@
 // sur un GPU", section "Emettre pour un GPU").  The S waves of a row group
 // split K and combine through LDS in a fixed order.
 //
+// With P = 1 (M = 1 only) the batches of U trips are software-pipelined: the
+// loads of batch b+1 (weights and the matching X chunks) are issued before the
+// dot products of batch b, so a wave keeps a batch in flight from its first
+// load to its last instead of waiting out one memory round trip per batch --
+// what long rows (K of several thousand) need.
+//
 // Block: 256 threads = 4 waves = (4/S) row groups x S K-slices.
 // Grid:  N / (R * 4/S) blocks.
 // ---------------------------------------------------------------------------
-template <int R, int S, int MMAX, int U, int NT, int OUT>
+template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0>
 __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* __restrict__ W,
                                           void* __restrict__ Y, int M)
 {
@@ -43,7 +49,35 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
 
-    for (long t0 = 0; t0 < TRIPS; t0 += U) {
+    constexpr long NB = TRIPS / U;              // batches of U trips
+    static_assert(P == 0 || (MMAX == 1 && NB >= 2), "pipelined batches: M = 1, two batches or more");
+    if constexpr (P) {
+        u32x4 w[2][U][R], xv[2][U];
+        auto ld = [&](int slot, long t0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) w[slot][u][r] = dev::load16<NT>(Wp + r * CH + (t0 + u) * 64);
+                xv[slot][u] = Xp[(t0 + u) * 64];
+            }
+        };
+        auto dot = [&](int slot) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = dev::dot8(w[slot][u][r], xv[slot][u], acc[r]);
+        };
+        ld(0, 0);
+#pragma unroll
+        for (long b = 0; b + 1 < NB; b += 2) {
+            ld(1, (b + 1) * U);
+            dot(0);
+            if (b + 2 < NB) ld(0, (b + 2) * U);
+            dot(1);
+        }
+        if constexpr (NB % 2) dot(0);
+    }
+    for (long t0 = 0; t0 < (P ? 0 : TRIPS); t0 += U) {
         u32x4 w[U][R];
 #pragma unroll
         for (int u = 0; u < U; ++u)

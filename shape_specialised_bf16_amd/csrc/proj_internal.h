@@ -26,6 +26,7 @@ struct Candidate {
     Family fam = Family::Plain;
     // GEMV parameters
     int R = 1, S = 1, MMAX = 1, U = 1, NT = 1;
+    int P = 0;       // 1: software-pipelined batches of U trips (vector GEMV, M = 1)
     // GEMM parameters: block tile, k-tile, LDS buffers, wave grid, split-K,
     // tile-row group, LDS swizzle period
     int BM = 0, BN = 0, BK = 64, ST = 2, WM = 0, WN = 0, SK = 1, GM = 8, SWZ = 0;

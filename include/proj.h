@@ -43,6 +43,9 @@ typedef struct proj_plan proj_plan; /* opaque; owned by the library */
 /* Storage type of Y.  X and W are always bf16. */
 enum { PROJ_OUT_F32 = 0, PROJ_OUT_BF16 = 1 };
 
+/* Epilogue fused into a plan's kernels (proj_plan_create_ex). */
+enum { PROJ_EPI_NONE = 0, PROJ_EPI_SWIGLU = 1 };
+
 enum {
     PROJ_OK = 0,
     PROJ_EINVAL = -1,   /* bad argument: null or misaligned pointer, bad size or dtype, wrong device */
@@ -76,6 +79,32 @@ enum {
  * PROJ_DUMP_DIR=<dir> writes the generated source and code object there.
  */
 proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
+
+/*
+ * Like proj_plan_create, with an epilogue folded into every kernel of the plan.
+ *
+ * PROJ_EPI_SWIGLU: W is a fused gate_up matrix, rows [0, N/2) the gate
+ * projection and rows [N/2, N) the up projection (N even), and the plan's Y is
+ * [M, N/2] with
+ *     Y[m, j] = silu(g) * u,   silu(g) = g / (1 + exp(-g)),
+ *     g = (X . W^T)[m, j],  u = (X . W^T)[m, N/2 + j],
+ * evaluated in f32 on the f32 sums; with PROJ_OUT_BF16, g and u are first
+ * rounded to bf16 (the values a plain plan would store) and the product is
+ * rounded to bf16 once.  The result is bit-identical to the unfused path -- a
+ * plain plan running the same kernel variant, then proj_swiglu on its output --
+ * while writing N/2 columns instead of N and skipping one launch and the round
+ * trip of the N-column intermediate: the SwiGLU folded into the gate_up
+ * projection of "#004 the same compiler on Apple's chips", section "Decode"
+ * (each fusion gives the same bits as the kernels it replaces), and of "#002
+ * le meme compilateur sur un GPU", section "Emettre pour un GPU" (the
+ * activation fused with the projection that produces its input).  Only the
+ * kernel families that have the fused epilogue are candidates (vector GEMVs
+ * with an even row count per wave, whole-tile MFMA GEMMs, the plain kernel).
+ *
+ * epilogue outside the enum, or an odd N with PROJ_EPI_SWIGLU, returns NULL
+ * with PROJ_EINVAL in proj_last_error.  PROJ_EPI_NONE is proj_plan_create.
+ */
+proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int epilogue);
 
 /*
  * Enqueue Y[0:M, :] = X[0:M, :] . W^T on `stream`.  Rows of Y at or past M are
@@ -115,6 +144,9 @@ const char* proj_last_error(void);
  */
 int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* buf, size_t cap,
                      size_t* needed);
+/* The same for a plan with an epilogue (proj_plan_create_ex). */
+int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int epilogue, const char* arch, char* buf, size_t cap,
+                        size_t* needed);
 
 /* JSON text (host buffer) describing the plan: shape, candidates, per-bucket
  * choice and timings, the tuner log, compile and tuning seconds.  Same size
@@ -141,6 +173,20 @@ int proj_run_candidate(const proj_plan* plan, int idx, const void* X, const void
 
 /* Index of the candidate proj_run uses for M rows (M >= 1), or a negative error. */
 int proj_plan_choice(const proj_plan* plan, int64_t M);
+
+/* ---- the unfused activation (shape-independent) ---- */
+
+/*
+ * Enqueue H[m, j] = silu(G[m, j]) * G[m, N/2 + j] for m < M, j < N/2: the
+ * SwiGLU of a plain gate_up projection's output G [M, N] into H [M, N/2], both
+ * of storage type dtype (f32, or bf16 read and written as bit patterns), dense
+ * row-major device buffers owned by the caller, H not overlapping G.  The
+ * same f32 operations and roundings as the PROJ_EPI_SWIGLU epilogue -- the
+ * separate kernel that epilogue replaces ("#004 the same compiler on Apple's
+ * chips", section "Decode").  N must be even; M == 0 or N == 0 is a no-op;
+ * negative sizes, odd N, a bad dtype or null pointers give PROJ_EINVAL.
+ */
+int proj_swiglu(const void* G, void* H, int64_t M, int64_t N, int dtype, hipStream_t stream);
 
 /* ---- measurement support (shape-independent) ---- */
 

@@ -72,6 +72,8 @@ def _load():
         lib.oracle_round_bf16.restype = None
         lib.oracle_round_f32_to_bf16.argtypes = [_p, _p, _i64, ctypes.c_int]
         lib.oracle_round_f32_to_bf16.restype = None
+        lib.oracle_swiglu.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_swiglu.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -115,6 +117,19 @@ def matmul_rows(X: np.ndarray, rows, W: np.ndarray, threads: int = 0) -> np.ndar
         _load().oracle_matmul_rows(X.ctypes.data, rows.ctypes.data, rows.size,
                                    W.ctypes.data, N, K, Y.ctypes.data, threads)
     return Y
+
+
+def swiglu(Y: np.ndarray) -> np.ndarray:
+    """H[m, j] = silu(Y[m, j]) * Y[m, N/2 + j] in fp64 for an fp64 gate_up
+    product Y [M, N] (gate columns first, then up), N even; see oracle.c."""
+    Y = np.ascontiguousarray(Y, dtype=np.float64)
+    if Y.ndim != 2 or Y.shape[1] % 2:
+        raise ValueError("swiglu: Y must be [M, N] with N even")
+    M, N = Y.shape
+    H = np.empty((M, N // 2), dtype=np.float64)
+    if H.size:
+        _load().oracle_swiglu(Y.ctypes.data, M, N, H.ctypes.data)
+    return H
 
 
 def round_f32(Y: np.ndarray) -> np.ndarray:

@@ -170,6 +170,28 @@ void oracle_round_f32_to_bf16(const float *in, uint16_t *out, int64_t n,
         out[i] = oracle_f64_to_bf16((double)in[i]);
 }
 
+/*
+ * SwiGLU of a gate_up projection, in fp64 ("#004 the same compiler on Apple's
+ * chips", section "Decode": the SwiGLU folded into the gate_up projection;
+ * "#002 le meme compilateur sur un GPU", section "Emettre pour un GPU": the
+ * activation fused with the projection that feeds it).  Reading of the layout
+ * (the pages name the fused matrix, not its row order): rows [0, N/2) of W are
+ * the gate projection and rows [N/2, N) the up projection, so with Y the fp64
+ * product [M, N]:
+ *     H[m][j] = silu(Y[m][j]) * Y[m][N/2 + j],   silu(g) = g / (1 + exp(-g)),
+ * for j < N/2, computed in double from the (unrounded) double sums.
+ */
+void oracle_swiglu(const double *Y, int64_t M, int64_t N, double *H)
+{
+    const int64_t half = N / 2;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < half; ++j) {
+            const double g = Y[m * N + j];
+            const double u = Y[m * N + half + j];
+            H[m * half + j] = g / (1.0 + exp(-g)) * u;
+        }
+}
+
 /* Number of threads an OpenMP parallel region would use. */
 int oracle_max_threads(void)
 {

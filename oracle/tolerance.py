@@ -105,3 +105,46 @@ def check_bf16(y_bits: np.ndarray, ref: np.ndarray) -> Report:
                   n_second_clause=int((~first & second).sum()),
                   worst_excess=float(excess[wi]) if y.size else 0.0,
                   gate_ratio=_gate_ratio(y, ref), worst_index=wi)
+
+
+SILU_LIPSCHITZ = 1.1      # max over x of |d/dx x*sigmoid(x)| = 1.0998...
+
+
+def check_swiglu(y: np.ndarray, g: np.ndarray, u: np.ndarray, dtype: str) -> Report:
+    """A fused SwiGLU output ``y`` [.., N/2] against the oracle's fp64 gate and
+    up sums ``g``, ``u`` (``oracle.matmul`` columns [0, N/2) and [N/2, N)).
+
+    Derivation (an allowance per element, from the rules above): the device's
+    f32 sums g', u' each meet the projection's f32 rule, |g' - g| <= eg =
+    1e-3 (|g| + 1) and likewise eu.  With bf16 storage the epilogue first
+    rounds g' and u' to bf16 (relative error <= 2^-9, 2^-8 taken), widening
+    eg and eu by 2^-8 of their size.  silu is Lipschitz with constant 1.1, so
+    |silu(g')u' - silu(g)u| <= 1.1 eg (|u| + eu) + |silu(g)| eu.  The f32
+    evaluation of silu(g')u' adds a few f32 ulps (2^-20 |h| allowed) and a
+    bf16 store one more rounding (one bf16 ulp of |h| + the bound).  The
+    allowance is of order 1e-3 of the operands: it catches every structural
+    mistake (a swapped gate and up, a wrong row pairing, a missing activation
+    -- all O(1) changes), while the bit-exactness of the fused result against
+    the unfused path is checked separately."""
+    y = np.asarray(y, dtype=np.float64).ravel()
+    g = np.asarray(g, dtype=np.float64).ravel()
+    u = np.asarray(u, dtype=np.float64).ravel()
+    if not (y.shape == g.shape == u.shape):
+        raise ValueError(f"shape mismatch {y.shape} {g.shape} {u.shape}")
+    silu = g / (1.0 + np.exp(-g))
+    h = silu * u
+    eg = F32_RTOL * (np.abs(g) + 1.0)
+    eu = F32_RTOL * (np.abs(u) + 1.0)
+    if dtype == "bf16":
+        eg = eg + 2.0 ** -8 * (np.abs(g) + eg)
+        eu = eu + 2.0 ** -8 * (np.abs(u) + eu)
+    allowed = SILU_LIPSCHITZ * eg * (np.abs(u) + eu) + np.abs(silu) * eu + 2.0 ** -20 * np.abs(h)
+    if dtype == "bf16":
+        allowed = allowed + bf16_ulp(np.abs(h) + allowed)
+    err = np.abs(y - h)
+    bad = ~(err <= allowed)
+    excess = np.where(np.isfinite(err), err / allowed, np.inf)
+    wi = int(np.argmax(excess)) if y.size else -1
+    return Report(n=y.size, n_bad=int(bad.sum()), n_second_clause=0,
+                  worst_excess=float(excess[wi]) if y.size else 0.0,
+                  gate_ratio=_gate_ratio(y, h), worst_index=wi)

@@ -24,6 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libproj.so")
 
 OUT_F32 = 0
 OUT_BF16 = 1
+EPI_NONE = 0
+EPI_SWIGLU = 1
 _ERRORS = {-1: "PROJ_EINVAL", -2: "PROJ_EDEVICE", -3: "PROJ_ECOMPILE", -4: "PROJ_ENOCAND", -5: "PROJ_ENOMEM"}
 
 # Every function declared in include/proj.h.
@@ -31,7 +33,7 @@ EXPORTED_SYMBOLS = (
     "proj_plan_create", "proj_run", "proj_plan_destroy", "proj_last_error", "proj_emit_source",
     "proj_plan_describe", "proj_plan_num_candidates", "proj_plan_candidate_name",
     "proj_plan_candidate_max_m", "proj_run_candidate", "proj_plan_choice", "proj_probe_read",
-    "proj_round_bf16",
+    "proj_round_bf16", "proj_plan_create_ex", "proj_emit_source_ex", "proj_swiglu",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -49,6 +51,13 @@ _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _lib.proj_plan_create.argtypes = [_i64, _i64, ctypes.c_int]
 _lib.proj_plan_create.restype = _p
+_lib.proj_plan_create_ex.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int]
+_lib.proj_plan_create_ex.restype = _p
+_lib.proj_emit_source_ex.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_char_p, ctypes.c_char_p,
+                                     ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+_lib.proj_emit_source_ex.restype = ctypes.c_int
+_lib.proj_swiglu.argtypes = [_p, _p, _i64, _i64, ctypes.c_int, _p]
+_lib.proj_swiglu.restype = ctypes.c_int
 _lib.proj_run.argtypes = [_p, _p, _p, _p, _i64, _p]
 _lib.proj_run.restype = ctypes.c_int
 _lib.proj_plan_destroy.argtypes = [_p]
@@ -97,9 +106,17 @@ def _text(fn, *args) -> str:
     return buf.value.decode()
 
 
-def emit_source(N: int, K: int, dtype: str = "f32", arch: str = "gfx950") -> str:
-    """The HIP source a plan for (N, K, dtype) compiles (no GPU needed)."""
-    return _text(_lib.proj_emit_source, N, K, _dtype_code(dtype), arch.encode())
+def _epi_code(epilogue) -> int:
+    if epilogue in (None, "none", EPI_NONE):
+        return EPI_NONE
+    if epilogue in ("swiglu", EPI_SWIGLU):
+        return EPI_SWIGLU
+    raise ValueError(f"unsupported epilogue {epilogue!r} (None or 'swiglu')")
+
+
+def emit_source(N: int, K: int, dtype: str = "f32", arch: str = "gfx950", epilogue=None) -> str:
+    """The HIP source a plan for (N, K, dtype[, epilogue]) compiles (no GPU needed)."""
+    return _text(_lib.proj_emit_source_ex, N, K, _dtype_code(dtype), _epi_code(epilogue), arch.encode())
 
 
 def _dtype_code(dtype) -> int:
@@ -136,14 +153,19 @@ def _bf16_2d(t, name: str, cols: int):
 
 
 class Plan:
-    """A compiled, tuned projection plan for fixed (N, K) and output dtype."""
+    """A compiled, tuned projection plan for fixed (N, K) and output dtype.
 
-    def __init__(self, N: int, K: int, dtype="f32"):
+    epilogue="swiglu": W is a gate_up matrix (gate rows then up rows) and the
+    plan writes Y[M, N/2] = silu(gate) * up (see proj_plan_create_ex)."""
+
+    def __init__(self, N: int, K: int, dtype="f32", epilogue=None):
         self.N, self.K = int(N), int(K)
         self.dtype_code = _dtype_code(dtype)
-        h = _lib.proj_plan_create(self.N, self.K, self.dtype_code)
+        self.epi_code = _epi_code(epilogue)
+        self.NO = self.N // 2 if self.epi_code == EPI_SWIGLU else self.N
+        h = _lib.proj_plan_create_ex(self.N, self.K, self.dtype_code, self.epi_code)
         if not h:
-            raise ProjError(-1, f"proj_plan_create({N}, {K}, {dtype})")
+            raise ProjError(-1, f"proj_plan_create_ex({N}, {K}, {dtype}, {epilogue})")
         self._h = ctypes.c_void_p(h)
 
     @property
@@ -176,10 +198,10 @@ class Plan:
             raise ValueError(f"W must be [{self.N}, {self.K}], got {tuple(W.shape)}")
         M = X.shape[0]
         if Y is None:
-            Y = torch.empty((M, self.N), dtype=self.out_dtype, device=X.device)
-        elif (Y.dtype != self.out_dtype or Y.dim() != 2 or Y.shape[1] != self.N or Y.shape[0] < M
+            Y = torch.empty((M, self.NO), dtype=self.out_dtype, device=X.device)
+        elif (Y.dtype != self.out_dtype or Y.dim() != 2 or Y.shape[1] != self.NO or Y.shape[0] < M
               or not Y.is_contiguous()):
-            raise ValueError(f"Y must be a contiguous [>= {M}, {self.N}] {self.out_dtype} matrix")
+            raise ValueError(f"Y must be a contiguous [>= {M}, {self.NO}] {self.out_dtype} matrix")
         return M, Y
 
     def run(self, X, W, Y=None, stream=None):
@@ -225,6 +247,22 @@ def probe_read(buf, sink, never: int = 0x9E3779B9, stream=None) -> None:
     nbytes = buf.numel() * buf.element_size()
     _check(_lib.proj_probe_read(buf.data_ptr(), nbytes, never, sink.data_ptr(), _stream_handle(stream)),
            "proj_probe_read")
+
+
+def swiglu(G, H=None, stream=None):
+    """H = silu(G[:, :N/2]) * G[:, N/2:] with the library's kernel (the unfused
+    path of the SwiGLU epilogue); G is f32 or bf16 [M, N] on the device."""
+    import torch
+    if G.dim() != 2 or G.shape[1] % 2 or not G.is_contiguous() or G.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("swiglu: G must be a contiguous f32 or bf16 [M, N] matrix with N even")
+    M, N = G.shape
+    if H is None:
+        H = torch.empty((M, N // 2), dtype=G.dtype, device=G.device)
+    elif H.dtype != G.dtype or tuple(H.shape) != (M, N // 2) or not H.is_contiguous():
+        raise ValueError(f"swiglu: H must be a contiguous [{M}, {N // 2}] {G.dtype} matrix")
+    _check(_lib.proj_swiglu(G.data_ptr(), H.data_ptr(), M, N, _dtype_code(G.dtype), _stream_handle(stream)),
+           "proj_swiglu")
+    return H
 
 
 def round_bf16(inp, out, stream=None) -> None:

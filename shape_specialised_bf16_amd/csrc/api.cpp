@@ -16,7 +16,7 @@ int set_error(int code, const char* f, ...);
 int compile_source(const std::string& src, const std::string& arch, const char* name,
                    std::shared_ptr<std::vector<char>>* code);
 int device_arch(int dev, std::string* arch, int* cus);
-int create_plan(int64_t N, int64_t K, int dtype, proj_plan** out);
+int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out);
 void destroy_plan(proj_plan* p);
 int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream);
 int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M);
@@ -26,7 +26,7 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
 // Shape-independent support module, one per device, loaded on first use.
 struct SupportModule {
     hipModule_t mod = nullptr;
-    hipFunction_t probe = nullptr, round = nullptr;
+    hipFunction_t probe = nullptr, round = nullptr, swiglu_f32 = nullptr, swiglu_bf16 = nullptr;
     int cus = 256;
 };
 static std::mutex g_support_mu;
@@ -49,7 +49,9 @@ static int support_module(SupportModule** out)
         if ((e = hipModuleLoadData(&sm.mod, code->data())) != hipSuccess)
             return set_error(PROJ_EDEVICE, "hipModuleLoadData(support): %s", hipGetErrorString(e));
         if ((e = hipModuleGetFunction(&sm.probe, sm.mod, "proj_probe_read")) != hipSuccess ||
-            (e = hipModuleGetFunction(&sm.round, sm.mod, "proj_round_bf16")) != hipSuccess)
+            (e = hipModuleGetFunction(&sm.round, sm.mod, "proj_round_bf16")) != hipSuccess ||
+            (e = hipModuleGetFunction(&sm.swiglu_f32, sm.mod, "proj_swiglu_f32")) != hipSuccess ||
+            (e = hipModuleGetFunction(&sm.swiglu_bf16, sm.mod, "proj_swiglu_bf16")) != hipSuccess)
             return set_error(PROJ_EDEVICE, "hipModuleGetFunction(support): %s", hipGetErrorString(e));
     }
     *out = &sm;
@@ -81,7 +83,8 @@ static std::string json_escape(const std::string& s)
 static std::string describe(const proj_plan* p)
 {
     std::ostringstream s;
-    s << "{\"N\": " << p->N << ", \"K\": " << p->K << ", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
+    s << "{\"N\": " << p->N << ", \"K\": " << p->K << ", \"NO\": " << p->NO << ", \"epilogue\": \""
+      << (p->epi ? "swiglu" : "none") << "\", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
       << "\", \"arch\": \"" << p->arch << "\", \"device\": " << p->device << ", \"compile_s\": " << p->compile_s
       << ", \"tune_s\": " << p->tune_s << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
       << ",\n \"candidates\": [";
@@ -115,9 +118,14 @@ extern "C" {
 
 proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype)
 {
+    return proj_plan_create_ex(N, K, dtype, PROJ_EPI_NONE);
+}
+
+proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int epilogue)
+{
     g_last_error.clear();
     proj_plan* p = nullptr;
-    if (create_plan(N, K, dtype, &p) != PROJ_OK) return nullptr;
+    if (create_plan(N, K, dtype, epilogue, &p) != PROJ_OK) return nullptr;
     return p;
 }
 
@@ -132,12 +140,23 @@ const char* proj_last_error(void) { return g_last_error.c_str(); }
 
 int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* buf, size_t cap, size_t* needed)
 {
+    return proj_emit_source_ex(N, K, dtype, PROJ_EPI_NONE, arch, buf, cap, needed);
+}
+
+int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int epilogue, const char* arch, char* buf, size_t cap,
+                        size_t* needed)
+{
     if (N < 1 || K < 8 || K % 8 != 0)
         return set_error(PROJ_EINVAL, "invalid shape N=%lld K=%lld", (long long)N, (long long)K);
     if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16) return set_error(PROJ_EINVAL, "invalid dtype %d", dtype);
+    if (epilogue != PROJ_EPI_NONE && epilogue != PROJ_EPI_SWIGLU)
+        return set_error(PROJ_EINVAL, "invalid epilogue %d", epilogue);
+    if (epilogue == PROJ_EPI_SWIGLU && N % 2)
+        return set_error(PROJ_EINVAL, "the SwiGLU epilogue needs an even N, got N=%lld", (long long)N);
     const std::string a = (arch && *arch) ? arch : "gfx950";
-    return copy_text(emit_source(N, K, dtype, a, kDefaultCUs, enumerate_candidates(N, K, kDefaultCUs)), buf, cap,
-                     needed);
+    return copy_text(emit_source(N, K, dtype, a, kDefaultCUs, enumerate_candidates(N, K, kDefaultCUs, epilogue),
+                                 epilogue),
+                     buf, cap, needed);
 }
 
 int proj_plan_describe(const proj_plan* plan, char* buf, size_t cap, size_t* needed)
@@ -206,6 +225,27 @@ int proj_probe_read(const void* buf, int64_t bytes, uint32_t never, void* sink, 
     const unsigned gx = (unsigned)((n16 + 2047) / 2048);  // one 32 KiB span per block
     hipError_t e = hipModuleLaunchKernel(sm->probe, gx, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
     if (e != hipSuccess) return set_error(PROJ_EDEVICE, "probe launch: %s", hipGetErrorString(e));
+    return PROJ_OK;
+}
+
+int proj_swiglu(const void* G, void* H, int64_t M, int64_t N, int dtype, hipStream_t stream)
+{
+    if (M < 0 || N < 0) return set_error(PROJ_EINVAL, "M and N must not be negative");
+    if (N % 2) return set_error(PROJ_EINVAL, "N=%lld must be even (gate and up halves)", (long long)N);
+    if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16) return set_error(PROJ_EINVAL, "invalid dtype %d", dtype);
+    if (M == 0 || N == 0) return PROJ_OK;
+    if (!G || !H) return set_error(PROJ_EINVAL, "null pointer");
+    SupportModule* sm = nullptr;
+    int rc = support_module(&sm);
+    if (rc) return rc;
+    const void* g = G;
+    void* h = H;
+    long mm = (long)M, nn = (long)N;
+    void* args[] = {&g, &h, &mm, &nn};
+    const unsigned gx = (unsigned)std::min<int64_t>(65536, (M * (N / 2) + 255) / 256);
+    hipError_t e = hipModuleLaunchKernel(dtype == PROJ_OUT_BF16 ? sm->swiglu_bf16 : sm->swiglu_f32, gx, 1, 1, 256, 1,
+                                         1, 0, stream, args, nullptr);
+    if (e != hipSuccess) return set_error(PROJ_EDEVICE, "swiglu launch: %s", hipGetErrorString(e));
     return PROJ_OK;
 }
 

@@ -34,7 +34,7 @@ static std::string fmt(const char* f, ...)
     return buf;
 }
 
-std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus)
+std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int epi)
 {
     std::vector<Candidate> out;
     const int64_t CH = K / 8;  // 16-byte chunks per row
@@ -47,6 +47,7 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus)
                       {1, 4, 1, 1}, {2, 4, 1, 1}, {1, 1, 16, 1}, {2, 1, 16, 1}, {1, 4, 16, 1}};
     for (const VG& v : vgs) {
         if (CH % v.S) continue;
+        if (epi && v.R % 2) continue;   // the fused epilogue pairs gate and up rows in a wave
         const int RG = 4 / v.S;
         if (N % (v.R * RG)) continue;
         const int64_t trips = CH / v.S / 64;
@@ -78,6 +79,7 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus)
 
     // ---- MFMA skinny GEMV for M <= 16: (S waves splitting K, U MFMA steps per load batch)
     for (int S : {1, 2, 4}) {
+        if (epi) break;                 // no fused epilogue in the MFMA GEMV
         for (int U : {2, 4}) {
             const int RG = 4 / S;
             if (N % (16 * RG)) continue;
@@ -130,6 +132,10 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus)
             if (TL > 1) c.reduce_name = c.name + "_reduce";
             out.push_back(c);
         };
+        if (epi) {                      // fused epilogue: whole tiles, gate/up halves per wave
+            if ((g.BN / g.WN) % 64 == 0 && K % g.BK == 0) add(1, 1);
+            continue;
+        }
         for (int SK : {1, 2, 4})
             if (SK <= g.maxSK && K % (g.BK * SK) == 0) add(SK, 1);
         for (int TL : g.tails)
@@ -157,19 +163,23 @@ std::string emit_support_source()
 }
 
 std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
-                        const std::vector<Candidate>& cands)
+                        const std::vector<Candidate>& cands, int epi)
 {
     const char* out = dtype == 1 ? "OUT_BF16" : "OUT_F32";
     std::ostringstream s;
     s << "// Generated by libproj for Y[M," << N << "] = X[M," << K << "] . W[" << N << "," << K
-      << "]^T, output " << (dtype == 1 ? "bf16" : "f32") << ", target " << arch << ".\n";
+      << "]^T, output " << (dtype == 1 ? "bf16" : "f32") << ", target " << arch
+      << (epi ? ", SwiGLU epilogue: Y[M, N/2] = silu(gate) * up" : "") << ".\n";
     s << "// Every constant below is an immediate of the kernels; M is the only run-time size.\n";
     s << "constexpr long N = " << N << ";            // output rows = rows of W\n";
     s << "constexpr long K = " << K << ";            // row length (bf16 values)\n";
     s << "constexpr long K_BLOCKS16 = " << K / 8 << ";    // 16-byte (8 x bf16) blocks per weight row\n";
     s << "constexpr long N_LAST = " << N - 1 << ";       // last output row index\n";
     s << "constexpr long ROW_BYTES = " << 2 * K << ";    // stride between weight rows\n";
-    s << "constexpr int DEVICE_CUS = " << cus << ";     // compute units of the device the code is for\n\n";
+    s << "constexpr int DEVICE_CUS = " << cus << ";     // compute units of the device the code is for\n";
+    s << "constexpr int EPI = " << epi << ";            // epilogue: 0 none, 1 SwiGLU of gate rows [0, N/2) and up rows [N/2, N)\n";
+    s << "constexpr long NOUT = " << (epi ? N / 2 : N) << ";         // columns of Y\n";
+    s << "constexpr int OUT_SEL = " << dtype << ";        // storage type of Y: 0 f32, 1 bf16\n\n";
     s << kDeviceCommonSrc << "\n";
     s << kKernelsHeadSrc << "\n";
     s << kGemvSrc << "\n";

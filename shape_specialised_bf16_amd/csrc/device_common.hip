@@ -51,6 +51,25 @@ __device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc)
     return acc;
 }
 
+// SwiGLU of one gate/up pair, silu(g) * u with silu(g) = g / (1 + e^-g), in
+// f32 ("#004 the same compiler on Apple's chips", section "Decode": the SwiGLU
+// folded into the gate_up projection gives the same bits as the separate
+// kernels).  With a bf16 output, g and u are first rounded to bf16 -- the
+// values the projection alone would store -- and the store rounds the product
+// once more; so the fused epilogue and the separate activation kernel run the
+// same operations on the same values.
+template <int OUT>
+__device__ __forceinline__ float swiglu(float g, float u)
+{
+    if constexpr (OUT == OUT_BF16) {
+        g = __builtin_bit_cast(float, (u32)to_bf16(g) << 16);
+        u = __builtin_bit_cast(float, (u32)to_bf16(u) << 16);
+    }
+    const float e = expf(-g);
+    const float s = g / (1.0f + e);
+    return s * u;
+}
+
 template <int OUT>
 __device__ __forceinline__ void store1(void* Y, long idx, float v)
 {

@@ -34,6 +34,22 @@ extern "C" __global__ __launch_bounds__(256) void proj_ref_rows(const u16* __res
         if (j < nrows) ref[(long)j * N + n] = acc[j];
 }
 
+// The plan's epilogue applied to the reference rows, in place: with the SwiGLU
+// epilogue, column n < NOUT of each listed row becomes dev::swiglu(ref[n],
+// ref[NOUT + n]) -- the value the fused candidate computes from its own f32
+// sums (rounded by the check like the candidate's store).  No-op otherwise.
+extern "C" __global__ __launch_bounds__(256) void proj_ref_epilogue(float* __restrict__ ref, int nrows)
+{
+    if constexpr (EPI) {
+        for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < (long)nrows * NOUT;
+             i += (long)gridDim.x * blockDim.x) {
+            const long j = i / NOUT, n = i % NOUT;
+            float* r = ref + j * N;
+            r[n] = dev::swiglu<OUT_SEL>(r[n], r[NOUT + n]);
+        }
+    }
+}
+
 // Counter-based generator for probe inputs (SplitMix-style mixer of seed and
 // index).  kind 0: uniform in [-scale, scale) rounded to bf16; kind 1: integers
 // uniform in [-4, 4] (exact in bf16).
@@ -99,11 +115,11 @@ __device__ __forceinline__ void check_body(const void* __restrict__ Y, long rows
                                            const float* __restrict__ ref, const int* __restrict__ rows,
                                            int nrows, int exact, CheckStats* __restrict__ st)
 {
-    const long total = rows_alloc * N;
+    const long total = rows_alloc * NOUT;
     u32 bad = 0, unw = 0, grd = 0;
     float merr = 0.f, mref = 0.f;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
-        const long row = i / N, col = i % N;
+        const long row = i / NOUT, col = i % NOUT;
         const bool sent = is_sentinel<OUT>(Y, i);
         if (row < M) unw += sent ? 1u : 0u;
         else grd += sent ? 0u : 1u;

@@ -126,6 +126,8 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(N % BN == 0, "tiles cover N exactly");
+    static_assert(EPI == 0 || (SK == 1 && TAILS == 1 && (BN / WN) % 64 == 0),
+                  "fused SwiGLU: whole tiles, gate and up halves of every wave's columns");
     constexpr int CA = BM * CPR, CB = BN * CPR;       // chunks per buffer
     static_assert(CA % NTHR == 0 && CB % NTHR == 0, "copies split evenly over threads");
     constexpr int IA = CA / NTHR, IB = CB / NTHR;     // copy instructions per thread per tile
@@ -171,7 +173,11 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     }
     long tm, tn;
     group_order<GROUP_M>(pid, tiles_m, TILES_N, &tm, &tn);
-    const long m0 = tm * BM, n0 = tn * BN;
+    const long m0 = tm * BM;
+    // first weight row of the tile (with the SwiGLU epilogue: its first gate row,
+    // which is also its first output column; the tile reads BN/2 gate rows and
+    // the BN/2 up rows NOUT below them)
+    const long n0 = tn * (EPI ? BN / 2 : BN);
 
     // ---- global sources of the copy slots.  Copy instruction i of thread t fills
     //      slot i*NTHR + t, i.e. row i*RPI + t/CPR of the buffer; the chunk's column
@@ -192,7 +198,17 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
         r = r < mlast ? r : mlast;
         aoff[i] = (unsigned)(r * K + ccol * 8);
     }
-    const unsigned boff0 = (unsigned)(r0 * K + ccol * 8);
+    // weight row (relative to the tile's first) held in B-tile row rr: with the
+    // SwiGLU epilogue each wave's WTN columns are WTN/2 gate rows followed by
+    // the matching up rows, so both halves of a pair land in the same lane
+    auto wrow = [&](int rr) -> long {
+        if constexpr (EPI) {
+            const int wv = rr / WTN, c = rr % WTN;
+            return c < WTN / 2 ? (long)wv * (WTN / 2) + c : NOUT + (long)wv * (WTN / 2) + c - WTN / 2;
+        } else {
+            return rr;
+        }
+    };
     // The copies are MUBUF loads into LDS (buffer_load_dwordx4 ... lds) over a
     // raw buffer descriptor per operand (gfx9 layout: base, stride 0, size in
     // bytes, word 3 = 0x00020000) that starts at the tile's first row and
@@ -200,17 +216,18 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     // fixed; the k-tile advances in the scalar offset.  (The global_ form of
     // the same copy is a FLAT instruction, and while one is outstanding the
     // compiler can only wait for all LDS reads at once.)
-    static_assert((long)(BM > BN ? BM : BN) * K * 2 < (1L << 31), "tile rows fit a 32-bit buffer size");
+    constexpr long B_ROWS = EPI ? NOUT + BN / 2 : BN;   // weight rows spanned by the B descriptor
+    static_assert((long)(BM > B_ROWS ? BM : B_ROWS) * K * 2 < (1L << 31), "tile rows fit a 32-bit buffer size");
     const long rows_a = (long)M - m0 < BM ? (long)M - m0 : BM;
     const __amdgpu_buffer_rsrc_t rsa =
         __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, (int)((rows_a * K - kbeg) * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t rsb =
-        __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)(((long)BN * K - kbeg) * 2), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)((B_ROWS * K - kbeg) * 2), 0x00020000);
     unsigned abyte[IA], bbyte[IB];
 #pragma unroll
     for (int i = 0; i < IA; ++i) abyte[i] = aoff[i] * 2;
 #pragma unroll
-    for (int i = 0; i < IB; ++i) bbyte[i] = (boff0 + (unsigned)(i * RPI * K)) * 2;
+    for (int i = 0; i < IB; ++i) bbyte[i] = (unsigned)((wrow(i * RPI + r0) * K + ccol * 8) * 2);
     auto issue = [&](u32x4* dst, long kt) {
         const unsigned koff = (unsigned)(kt * BK * 2);
 #pragma unroll
@@ -229,7 +246,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 #pragma unroll
         for (int i = 0; i < IA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a + aoff[i]);
 #pragma unroll
-        for (int i = 0; i < IB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b + boff0 + (unsigned)(i * RPI * K));
+        for (int i = 0; i < IB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b + bbyte[i] / 2);
     };
     auto lstore = [&](u32x4* dst) {
 #pragma unroll
@@ -405,6 +422,22 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
         }
     }
     kloop(ic<KT>{});
+    if constexpr (EPI) {
+        // block j < TN/2 holds gate rows, block j + TN/2 the matching up rows
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN / 2; ++j) {
+                const long col = n0 + wn * (WTN / 2) + j * 32 + (lane & 31);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const long row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lhalf + (e & 3);
+                    if (row < M)
+                        dev::store1<OUT>(Y, row * NOUT + col, dev::swiglu<OUT>(acc[i][j][e], acc[i][j + TN / 2][e]));
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -471,11 +504,17 @@ __device__ __forceinline__ void gemm_plain(const u16* __restrict__ X, const u16*
                                            void* __restrict__ Y, int M)
 {
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long)M * N) return;
-    const long m = idx / N, n = idx % N;
+    if (idx >= (long)M * NOUT) return;
+    const long m = idx / NOUT, n = idx % NOUT;
     const u32x4* xp = reinterpret_cast<const u32x4*>(X + m * K);
     const u32x4* wp = reinterpret_cast<const u32x4*>(W + n * K);
     float acc = 0.f;
     for (long c = 0; c < K / 8; ++c) acc = dev::dot8(wp[c], xp[c], acc);
+    if constexpr (EPI) {           // the up row of output column n is W row NOUT + n
+        const u32x4* up = reinterpret_cast<const u32x4*>(W + (NOUT + n) * K);
+        float au = 0.f;
+        for (long c = 0; c < K / 8; ++c) au = dev::dot8(up[c], xp[c], au);
+        acc = dev::swiglu<OUT>(acc, au);
+    }
     dev::store1<OUT>(Y, idx, acc);
 }

@@ -17,6 +17,10 @@
 // load to its last instead of waiting out one memory round trip per batch --
 // what long rows (K of several thousand) need.
 //
+// With the SwiGLU epilogue (EPI == 1) a wave's R rows are R/2 gate rows j..
+// and their up rows NOUT + j..; after the reduction the up sum of a gate value
+// sits 32 lanes above it, and the wave stores silu(gate) * up in column j.
+//
 // Block: 256 threads = 4 waves = (4/S) row groups x S K-slices.
 // Grid:  N / (R * 4/S) blocks.
 // ---------------------------------------------------------------------------
@@ -35,12 +39,15 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
     static_assert(N % (R * RG) == 0, "blocks tile N exactly");
     constexpr int V = R * MMAX;
     constexpr int LV = dev::log2_of<V>::value;
+    static_assert(EPI == 0 || R % 2 == 0, "gate/up pairs: an even row count per wave");
+    // weight row of the wave's row r, relative to the wave's first row
+    auto rowoff = [](int r) -> long { return (EPI && r >= R / 2) ? NOUT - R / 2 + r : r; };
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int s = wave % S;
     const int rg = wave / S;
-    const long n0 = ((long)blockIdx.x * RG + rg) * R;
+    const long n0 = ((long)blockIdx.x * RG + rg) * (EPI ? R / 2 : R);   // first weight row = first output column
 
     const u32x4* __restrict__ Wp = reinterpret_cast<const u32x4*>(W) + n0 * CH + s * CHS + lane;
     const u32x4* __restrict__ Xp = reinterpret_cast<const u32x4*>(X) + s * CHS + lane;
@@ -57,7 +64,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) w[slot][u][r] = dev::load16<NT>(Wp + r * CH + (t0 + u) * 64);
+                for (int r = 0; r < R; ++r) w[slot][u][r] = dev::load16<NT>(Wp + rowoff(r) * CH + (t0 + u) * 64);
                 xv[slot][u] = Xp[(t0 + u) * 64];
             }
         };
@@ -83,7 +90,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                w[u][r] = dev::load16<NT>(Wp + r * CH + (t0 + u) * 64);
+                w[u][r] = dev::load16<NT>(Wp + rowoff(r) * CH + (t0 + u) * 64);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -101,7 +108,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
         if (lane < TAIL) {
             u32x4 w[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) w[r] = dev::load16<NT>(Wp + r * CH + TRIPS * 64);
+            for (int r = 0; r < R; ++r) w[r] = dev::load16<NT>(Wp + rowoff(r) * CH + TRIPS * 64);
 #pragma unroll
             for (int m = 0; m < MMAX; ++m) {
                 if (m < M) {
@@ -120,16 +127,27 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
     const int r = idx / MMAX, m = idx % MMAX;
 
     if constexpr (S == 1) {
-        if (writer && m < M) dev::store1<OUT>(Y, (long)m * N + n0 + r, sum);
+        if constexpr (EPI) {
+            const float up = __shfl_down(sum, 32);      // value idx + (R/2)*MMAX
+            if (writer && r < R / 2 && m < M) dev::store1<OUT>(Y, (long)m * NOUT + n0 + r, dev::swiglu<OUT>(sum, up));
+        } else {
+            if (writer && m < M) dev::store1<OUT>(Y, (long)m * NOUT + n0 + r, sum);
+        }
     } else {
         __shared__ float red[4][V];
         if (writer) red[wave][idx] = sum;
         __syncthreads();
-        if (s == 0 && writer && m < M) {
+        if (s == 0 && writer && m < M && (!EPI || r < R / 2)) {
             float t = red[wave][idx];
 #pragma unroll
             for (int j = 1; j < S; ++j) t += red[wave + j][idx];
-            dev::store1<OUT>(Y, (long)m * N + n0 + r, t);
+            if constexpr (EPI) {
+                float tu = red[wave][idx + (R / 2) * MMAX];
+#pragma unroll
+                for (int j = 1; j < S; ++j) tu += red[wave + j][idx + (R / 2) * MMAX];
+                t = dev::swiglu<OUT>(t, tu);
+            }
+            dev::store1<OUT>(Y, (long)m * NOUT + n0 + r, t);
         }
     }
 }
@@ -158,6 +176,7 @@ __device__ __forceinline__ void gemv_mfma(const u16* __restrict__ X, const u16* 
     constexpr int RG = 4 / S;
     static_assert(N % (16 * RG) == 0, "blocks tile N exactly");
     static_assert(K % (32 * U * S) == 0, "K slices are whole batches");
+    static_assert(EPI == 0, "no fused epilogue in the MFMA GEMV");
     constexpr long KS = K / S;
     constexpr long BATCHES = KS / (32 * U);
 

@@ -132,7 +132,7 @@ struct LaunchGeom {
     unsigned gx, gy, threads;
 };
 
-static LaunchGeom geom(const Candidate& c, int64_t N, int64_t M)
+static LaunchGeom geom(const Candidate& c, int64_t N, int64_t NO, int64_t M)
 {
     switch (c.fam) {
     case Family::GemvValu: return {(unsigned)(N / (c.R * (4 / c.S))), 1u, 256u};
@@ -147,7 +147,7 @@ static LaunchGeom geom(const Candidate& c, int64_t N, int64_t M)
         return {(unsigned)(tm * (N / c.BN)), (unsigned)c.SK, (unsigned)c.threads};
     }
     case Family::Plain:
-    default: return {(unsigned)((M * N + 255) / 256), 1u, 256u};
+    default: return {(unsigned)((M * NO + 255) / 256), 1u, 256u};
     }
 }
 
@@ -160,7 +160,7 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
     if (c.ws_bytes(M, p->N) > p->ws_bytes)
         return set_error(PROJ_EINVAL, "%s needs %zu bytes of split-K workspace at M=%lld, plan has %zu",
                          c.name.c_str(), c.ws_bytes(M, p->N), (long long)M, p->ws_bytes);
-    const LaunchGeom g = geom(c, p->N, M);
+    const LaunchGeom g = geom(c, p->N, p->NO, M);
     const void* x = X;
     const void* w = W;
     void* y = Y;
@@ -203,8 +203,8 @@ static float bf16_to_f(uint16_t b) { return bits_f((uint32_t)b << 16); }
 struct Tuner {
     proj_plan* p;
     hipStream_t st = nullptr;
-    hipFunction_t f_fill_probe = nullptr, f_fill_u32 = nullptr, f_ref = nullptr, f_check = nullptr,
-                  f_probe = nullptr;
+    hipFunction_t f_fill_probe = nullptr, f_fill_u32 = nullptr, f_ref = nullptr, f_ref_epi = nullptr,
+                  f_check = nullptr, f_probe = nullptr;
     void *Xr = nullptr, *Xi = nullptr, *Wr = nullptr, *Wi = nullptr, *Y = nullptr;
     float *ref_r = nullptr, *ref_i = nullptr;
     int* rows_d = nullptr;
@@ -237,7 +237,7 @@ struct Tuner {
 
     int fill_sentinel(int64_t rows)
     {
-        const int64_t bytes = rows * p->N * (int64_t)ysize();
+        const int64_t bytes = rows * p->NO * (int64_t)ysize();
         long n32 = (long)(bytes / 4);
         uint32_t v = p->dtype == PROJ_OUT_BF16 ? 0x7FBA7FBAu : 0x7FBADBADu;
         unsigned gx = (unsigned)std::min<int64_t>((n32 + 255) / 256, 65536);
@@ -256,11 +256,12 @@ struct Tuner {
         HIP_TRY(hipModuleGetFunction(&f_fill_probe, p->module, "proj_fill_probe"));
         HIP_TRY(hipModuleGetFunction(&f_fill_u32, p->module, "proj_fill_u32"));
         HIP_TRY(hipModuleGetFunction(&f_ref, p->module, "proj_ref_rows"));
+        HIP_TRY(hipModuleGetFunction(&f_ref_epi, p->module, "proj_ref_epilogue"));
         HIP_TRY(hipModuleGetFunction(&f_probe, p->module, "proj_probe_read"));
         HIP_TRY(hipModuleGetFunction(&f_check, p->module,
                                      p->dtype == PROJ_OUT_BF16 ? "proj_check_bf16" : "proj_check_f32"));
         const size_t xb = (size_t)mmax * p->K * 2, wb = (size_t)p->N * p->K * 2;
-        const size_t yb = (size_t)(mmax + kGuardRows) * p->N * ysize();
+        const size_t yb = (size_t)(mmax + kGuardRows) * p->NO * ysize();
         if (hipMalloc(&Xr, xb) != hipSuccess || hipMalloc(&Xi, xb) != hipSuccess ||
             hipMalloc(&Wr, wb) != hipSuccess || hipMalloc(&Wi, wb) != hipSuccess ||
             hipMalloc(&Y, yb) != hipSuccess || hipMalloc(&ref_r, 8 * p->N * 4) != hipSuccess ||
@@ -299,6 +300,22 @@ struct Tuner {
             int* rd = rows_d;
             void* args[] = {&x, &w, &rd, &nr, &r};
             HIP_TRY(hipModuleLaunchKernel(f_ref, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
+        }
+        HIP_TRY(hipStreamSynchronize(st));
+        return PROJ_OK;
+    }
+
+    // The plan's epilogue applied to the reference rows of both probes (after the
+    // self-check, which compares the plain sums).
+    int reference_epilogue(int nrows)
+    {
+        if (!p->epi) return PROJ_OK;
+        unsigned gx = (unsigned)std::min<int64_t>((nrows * p->NO + 255) / 256, 4096);
+        for (int pass = 0; pass < 2; ++pass) {
+            float* r = pass ? ref_i : ref_r;
+            int nr = nrows;
+            void* args[] = {&r, &nr};
+            HIP_TRY(hipModuleLaunchKernel(f_ref_epi, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
         }
         HIP_TRY(hipStreamSynchronize(st));
         return PROJ_OK;
@@ -461,6 +478,7 @@ int tune_plan(proj_plan* p)
             ref_checked = true;
         }
         const int nrows = (int)rows.size();
+        if ((rc = T.reference_epilogue(nrows))) return rc;
 
         std::vector<int> ok;
         auto validate = [&](int ci) -> int {
@@ -546,7 +564,7 @@ int tune_plan(proj_plan* p)
     return PROJ_OK;
 }
 
-int create_plan(int64_t N, int64_t K, int dtype, proj_plan** out)
+int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out)
 {
     *out = nullptr;
     if (N < 1 || K < 8 || K % 8 != 0 || N > (int64_t)1 << 30 || K > (int64_t)1 << 24)
@@ -554,22 +572,30 @@ int create_plan(int64_t N, int64_t K, int dtype, proj_plan** out)
                          (long long)N, (long long)K);
     if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16)
         return set_error(PROJ_EINVAL, "invalid dtype %d (PROJ_OUT_F32=0 or PROJ_OUT_BF16=1)", dtype);
+    if (epi != PROJ_EPI_NONE && epi != PROJ_EPI_SWIGLU)
+        return set_error(PROJ_EINVAL, "invalid epilogue %d (PROJ_EPI_NONE=0 or PROJ_EPI_SWIGLU=1)", epi);
+    if (epi == PROJ_EPI_SWIGLU && N % 2)
+        return set_error(PROJ_EINVAL, "the SwiGLU epilogue needs an even N (gate and up halves), got N=%lld",
+                         (long long)N);
     std::unique_ptr<proj_plan> p(new proj_plan());
     p->N = N;
     p->K = K;
     p->dtype = dtype;
+    p->epi = epi;
+    p->NO = epi == PROJ_EPI_SWIGLU ? N / 2 : N;
     HIP_TRY(hipGetDevice(&p->device));
     int rc;
     int cus = kDefaultCUs;
     if ((rc = device_arch(p->device, &p->arch, &cus))) return rc;
     for (int b = 0; b < kNumBuckets; ++b) p->choice[b] = -1, p->choice_us[b] = -1;
 
-    p->cands = enumerate_candidates(N, K, cus);
-    const std::string src = emit_source(N, K, dtype, p->arch, cus, p->cands);
+    p->cands = enumerate_candidates(N, K, cus, epi);
+    const std::string src = emit_source(N, K, dtype, p->arch, cus, p->cands, epi);
     const double t0 = now_s();
     std::shared_ptr<std::vector<char>> code;
     char name[96];
-    snprintf(name, sizeof name, "proj_%lldx%lld_%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32");
+    snprintf(name, sizeof name, "proj_%lldx%lld_%s%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32",
+             epi ? "_swiglu" : "");
     if ((rc = compile_source(src, p->arch, name, &code))) return rc;
     p->compile_s = now_s() - t0;
     p->code_bytes = code->size();
@@ -637,7 +663,7 @@ int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t 
     for (int64_t off = 0; off < M; off += kMaxBlockRows) {
         const int64_t m = std::min<int64_t>(kMaxBlockRows, M - off);
         const Candidate& c = p->cands[p->choice[bucket_of(m)]];
-        rc = launch_candidate(p, c, (const char*)X + (size_t)off * p->K * 2, W, (char*)Y + (size_t)off * p->N * ysz,
+        rc = launch_candidate(p, c, (const char*)X + (size_t)off * p->K * 2, W, (char*)Y + (size_t)off * p->NO * ysz,
                               m, stream);
         if (rc) return rc;
     }

@@ -75,12 +75,13 @@ struct Candidate {
 // Enumerate the candidates that tile (N, K) exactly.  Always ends with the
 // plain kernel, which fits any shape.
 // `cus` is the device's compute-unit count (it sets the tail split's round size).
-std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus);
+// epi: 0 plain projection, 1 fused SwiGLU epilogue (only the families that have it)
+std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int epi = 0);
 
 // The full translation unit for (N, K, dtype): prelude with the shape as
 // literals, device helpers, kernel templates, one wrapper per candidate.
 std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
-                        const std::vector<Candidate>& cands);
+                        const std::vector<Candidate>& cands, int epi = 0);
 
 // Compute units assumed when no device is queried (MI355X).
 constexpr int kDefaultCUs = 256;
@@ -104,6 +105,8 @@ int bucket_of(int64_t M);
 struct proj_plan {
     int64_t N = 0, K = 0;
     int dtype = 0;
+    int epi = 0;        // PROJ_EPI_NONE or PROJ_EPI_SWIGLU
+    int64_t NO = 0;     // columns of Y: N, or N/2 with the SwiGLU epilogue
     int device = -1;
     std::string arch;
     hipModule_t module = nullptr;

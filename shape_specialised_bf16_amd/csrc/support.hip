@@ -40,3 +40,35 @@ extern "C" __global__ __launch_bounds__(256) void proj_round_bf16(const float* _
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
         out[i] = dev::to_bf16(in[i]);
 }
+
+// The SwiGLU activation as a kernel of its own -- the unfused path that the
+// projection's fused epilogue must reproduce bit for bit: G [M, N] holds the
+// gate_up projection (gate in columns [0, N/2), up in [N/2, N)), H [M, N/2]
+// receives dev::swiglu(gate, up) stored with the same rounding.
+template <int OUT>
+__device__ __forceinline__ void swiglu_rows(const void* __restrict__ G, void* __restrict__ H, long M, long N)
+{
+    const long half = N / 2;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < M * half; i += (long)gridDim.x * blockDim.x) {
+        const long m = i / half, j = i % half;
+        float g, u;
+        if constexpr (OUT == OUT_F32) {
+            g = reinterpret_cast<const float*>(G)[m * N + j];
+            u = reinterpret_cast<const float*>(G)[m * N + half + j];
+        } else {
+            g = dev::lo_bf16(reinterpret_cast<const u16*>(G)[m * N + j]);
+            u = dev::lo_bf16(reinterpret_cast<const u16*>(G)[m * N + half + j]);
+        }
+        dev::store1<OUT>(H, i, dev::swiglu<OUT>(g, u));
+    }
+}
+
+extern "C" __global__ __launch_bounds__(256) void proj_swiglu_f32(const void* G, void* H, long M, long N)
+{
+    swiglu_rows<OUT_F32>(G, H, M, N);
+}
+
+extern "C" __global__ __launch_bounds__(256) void proj_swiglu_bf16(const void* G, void* H, long M, long N)
+{
+    swiglu_rows<OUT_BF16>(G, H, M, N);
+}

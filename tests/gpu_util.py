@@ -16,13 +16,13 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def plan(N: int, K: int, dtype: str = "f32"):
+def plan(N: int, K: int, dtype: str = "f32", epilogue=None):
     from shape_specialised_bf16_amd import Plan
 
-    key = (N, K, dtype)
+    key = (N, K, dtype, epilogue)
     if key not in _plans:
-        log(f"[plan] creating {N}x{K} {dtype}")
-        _plans[key] = Plan(N, K, dtype)
+        log(f"[plan] creating {N}x{K} {dtype}" + (f" epilogue {epilogue}" if epilogue else ""))
+        _plans[key] = Plan(N, K, dtype, epilogue=epilogue)
     return _plans[key]
 
 

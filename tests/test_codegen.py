@@ -107,3 +107,42 @@ def test_emitted_source_compiles_for_gfx950(tmp_path):
                         "-std=c++17", "-include", "hip/hip_runtime.h", str(f), "-o", str(f) + ".o"],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
+
+
+def test_swiglu_module_constants_and_families():
+    """A SwiGLU plan's module carries the epilogue and the halved output width
+    as literals, and compiles only the kernel families that have the fused
+    epilogue: vector GEMVs with an even row count per wave, whole-tile GEMMs
+    whose waves hold gate and up halves (no split-K, no split tail), and the
+    plain kernel -- no MFMA GEMV."""
+    src = ssb.emit_source(6144, 1024, "f32", epilogue="swiglu")
+    assert "constexpr int EPI = 1;" in src
+    assert "constexpr long NOUT = 3072;" in src
+    names = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\(', src)
+    assert "gemm_plain" in names and any(n.startswith("gemv_valu") for n in names)
+    for n in names:
+        assert not n.startswith("gemv_mfma"), n
+        m = re.match(r"gemv_valu_r(\d+)_", n)
+        if m:
+            assert int(m.group(1)) % 2 == 0, n
+        m = re.match(r"gemm_(\d+)x(\d+)x(\d+)_st(\d+)_w(\d+)x(\d+)_sw(\d+)_g(\d+)_sk(\d+)", n)
+        if m:
+            BM, BN, BK, ST, WM, WN, SWZ, GM, SK = map(int, m.groups())
+            assert SK == 1 and "_tail" not in n and (BN // WN) % 64 == 0, n
+    plain = ssb.emit_source(6144, 1024, "f32")
+    assert "constexpr int EPI = 0;" in plain and "constexpr long NOUT = 6144;" in plain
+
+
+def test_swiglu_odd_n_rejected():
+    with pytest.raises(ssb.ProjError, match="even"):
+        ssb.emit_source(1001, 1024, "f32", epilogue="swiglu")
+
+
+def test_swiglu_source_compiles_for_gfx950(tmp_path):
+    src = ssb.emit_source(1000, 520, "bf16", epilogue="swiglu")
+    f = tmp_path / "proj_1000x520_swiglu.hip"
+    f.write_text(src)
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-device-only", "-c", "-O3",
+                        "-std=c++17", "-include", "hip/hip_runtime.h", str(f), "-o", str(f) + ".o"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]

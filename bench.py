@@ -21,6 +21,10 @@ Reported (one JSON line on stdout):
              stream), against 8 TB/s
   prefill    the 4B-like layer at M = 512 and 2048 (bf16 out): TFLOP/s against
              the 2.5 PFLOP/s dense bf16 MFMA peak, with its dominant kernel
+  swiglu_epilogue  the gate/up projection with the fused SwiGLU epilogue
+             against the plain plan + the separate activation kernel
+  long_prompt, layer_27b  the caller-side prompt-block driver (8192 rows in
+             blocks of 1024, then the head) and the 27B-like layer
   cpu_baseline  the fp64 CPU oracle on the same decode step, all host cores
   probe      HBM read-probe bandwidth on the same device (the pages' denominator)
 Progress goes to stderr.
@@ -397,6 +401,87 @@ def time_27b(steps: int = 500, warmup: int = 20, reps: int = 5):
     return out
 
 
+def time_swiglu(steps: int = 1000, reps: int = 20):
+    """The SwiGLU epilogue folded into the gate_up projection against the
+    unfused path (the plain plan, then proj_swiglu on its N-column output):
+    the 0.8B-like gate/up at M = 1 (f32, rotating weight copies) and the
+    4B-like gate/up at M = 2048 (bf16)."""
+    import numpy as np
+    import torch
+
+    import shape_specialised_bf16_amd as ssb
+    import synth
+
+    stream = torch.cuda.current_stream()
+    sh = __import__("ctypes").c_void_p(stream.cuda_stream)
+    out = {}
+    for key, cfg_no, M, dt in (("decode_gate_up_08b_m1", 1, 1, "f32"), ("prefill_gate_up_4b_m2048", 2, 2048, "bf16")):
+        cfg = synth.CONFIGS[cfg_no]
+        pi = [p.name for p in cfg.projections].index("gate_up")
+        p = cfg.projections[pi]
+        fused = ssb.Plan(p.N, p.K, dt, epilogue="swiglu")
+        plain = ssb.Plan(p.N, p.K, dt)
+        Wh, Xh = synth.weights(cfg, pi), synth.activations(cfg, pi, M)
+        W, X = upload(Wh), upload(Xh)
+        copies = max(1, -(-ROTATE_BYTES // (W.numel() * 2))) if M == 1 else 1
+        Wrot = [W] + [W.clone() for _ in range(copies - 1)]
+        odt = torch.bfloat16 if dt == "bf16" else torch.float32
+        Gb = torch.empty((M, p.N), dtype=odt, device="cuda")
+        Hu = torch.empty((M, p.N // 2), dtype=odt, device="cuda")
+        Hf = torch.empty((M, p.N // 2), dtype=odt, device="cuda")
+        n = steps if M == 1 else reps
+
+        # raw C-ABI calls on precomputed pointers, so that host overhead does not
+        # weigh on the two-launch path more than on the one-launch path
+        xp, wps, gp, hup, hfp = X.data_ptr(), [w.data_ptr() for w in Wrot], Gb.data_ptr(), Hu.data_ptr(), \
+            Hf.data_ptr()
+        swiglu_c, code = ssb._lib.proj_swiglu, (1 if dt == "bf16" else 0)
+
+        def unfused(s):
+            plain.run_ptr(xp, wps[s % copies], gp, M, sh)
+            swiglu_c(gp, hup, M, p.N, code, sh)
+
+        def fused_(s):
+            fused.run_ptr(xp, wps[s % copies], hfp, M, sh)
+
+        res = {}
+        for name, fn in (("unfused", unfused), ("fused", fused_)):
+            for s in range(20):
+                fn(s)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s in range(n):
+                fn(s)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / n * 1e3
+        rows = [0] if M == 1 else [0, 1023, M - 1]
+        import oracle
+        from oracle import tolerance
+        ref = oracle.matmul_rows(Xh, rows, Wh)
+        half = p.N // 2
+        got = Hf[rows].float().cpu().numpy().astype(np.float64) if dt == "f32" else \
+            oracle.bf16_bits_to_f64(Hf[rows].view(torch.int16).cpu().numpy().view(np.uint16))
+        rep = tolerance.check_swiglu(got, ref[:, :half], ref[:, half:], dt)
+        if not rep.ok:
+            raise SystemExit(f"bench: fused SwiGLU {key} does not match the oracle: {rep}")
+        o = dict(shape=f"{p.N}x{p.K}", M=M, dtype=dt, fused_us=round(res["fused"], 3),
+                 unfused_us=round(res["unfused"], 3), speedup=round(res["unfused"] / res["fused"], 3),
+                 fused_kernel=fused.choice(M), plain_kernel=plain.choice(M))
+        if M == 1:
+            o["weight_copies_rotated"] = copies
+            o["fused_GBps"] = round((2 * p.N * p.K + 2 * p.K + 4 * half) / res["fused"] / 1e3, 1)
+        else:
+            o["fused_TFLOPs"] = round(2.0 * M * p.N * p.K / res["fused"] / 1e6, 1)
+        out[key] = o
+        log(f"  SwiGLU {key}: fused {res['fused']:.2f} us, unfused {res['unfused']:.2f} us")
+        fused.close()
+        plain.close()
+        del Wrot, W, X, Gb, Hu, Hf
+    return out
+
+
 def probe_bandwidth():
     import torch
     import shape_specialised_bf16_amd as ssb
@@ -529,6 +614,7 @@ def main():
         result["prefill"] = {"workload": "prefill_4b_layer: QKV 2560->5120, out 4096->2560, gate/up "
                                          "2560->18432, down 9216->2560, Y bf16", **time_prefill()}
     if not args.no_extra:
+        result["swiglu_epilogue"] = time_swiglu()
         result["long_prompt"] = time_long_prompt()
         torch.cuda.empty_cache()
         result["layer_27b"] = time_27b()

@@ -76,7 +76,16 @@ enum {
  * PROJ_TUNE=0 skips timing and takes the first candidate that validates;
  * PROJ_TUNE_REPS=<n> sets timed launches per candidate; PROJ_FORCE=<name>
  * keeps only that candidate (plus the plain kernel) where it applies;
- * PROJ_DUMP_DIR=<dir> writes the generated source and code object there.
+ * PROJ_DUMP_DIR=<dir> writes the generated source and code object there;
+ * PROJ_CACHE_DIR=<dir> turns on the persistent tuning cache: the choices of a
+ * tuned plan are written to <dir>/proj-<key>.txt, where the key hashes the
+ * device (architecture name, CU count), the HIP runtime and driver versions
+ * and the complete generated source; a later plan with the same key runs
+ * every cached choice through the same validation gate instead of timing
+ * candidates, and tunes afresh any bucket whose cached choice is unknown or
+ * fails the gate (the cache the pages propose, and doubt because machine state
+ * drifts: "#004 the same compiler on Apple's chips", section "Reproducing at
+ * home").  proj_plan_describe reports "cache": off, miss, hit or stale.
  */
 proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
 

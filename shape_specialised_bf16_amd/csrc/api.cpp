@@ -87,6 +87,7 @@ static std::string describe(const proj_plan* p)
       << (p->epi ? "swiglu" : "none") << "\", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
       << "\", \"arch\": \"" << p->arch << "\", \"device\": " << p->device << ", \"compile_s\": " << p->compile_s
       << ", \"tune_s\": " << p->tune_s << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
+      << ", \"cache\": \"" << p->cache << "\", \"cache_path\": \"" << json_escape(p->cache_path) << "\""
       << ",\n \"candidates\": [";
     for (size_t i = 0; i < p->cands.size(); ++i) s << (i ? ", " : "") << "\"" << p->cands[i].name << "\"";
     s << "],\n \"buckets\": [";

@@ -431,6 +431,73 @@ static void plog(proj_plan* p, const std::string& line)
     if (env_int("PROJ_LOG", 0)) fprintf(stderr, "%s\n", line.c_str());
 }
 
+// ---------------------------------------------------------------- tuning cache
+// The choices of a tuned plan, kept in a text file per key (the persistent
+// tuning cache the pages propose -- and doubt, because the machine's state
+// drifts -- in "#004 the same compiler on Apple's chips", section "Reproducing
+// at home").  The key hashes the device (full architecture name, CU count),
+// the HIP runtime and driver versions and the complete emitted source, which
+// fixes the shape, output type, epilogue and every candidate's code; so a
+// library or driver change is a different key.  On a hit every cached choice
+// still goes through the load-time gate before it is used ("re-validation");
+// a choice that is missing or fails it sends its bucket back to full tuning.
+// Off unless PROJ_CACHE_DIR names a directory.
+static uint64_t fnv1a(uint64_t h, const std::string& s)
+{
+    for (unsigned char c : s) {
+        h ^= c;
+        h *= 0x100000001b3ull;
+    }
+    return h;
+}
+
+static int cache_key(proj_plan* p, const std::string& src)
+{
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, p->device));
+    int rt = 0, drv = 0;
+    HIP_TRY(hipRuntimeGetVersion(&rt));
+    HIP_TRY(hipDriverGetVersion(&drv));
+    char head[512];
+    snprintf(head, sizeof head, "%s|cus=%d|runtime=%d|driver=%d|", prop.gcnArchName, prop.multiProcessorCount, rt,
+             drv);
+    p->key = fnv1a(fnv1a(0xcbf29ce484222325ull, head), src);
+    return PROJ_OK;
+}
+
+// Cached choice names per bucket ("" where absent); false if there is no usable file.
+static bool cache_read(const std::string& path, std::vector<std::string>* names)
+{
+    std::ifstream f(path);
+    if (!f) return false;
+    std::string line;
+    if (!std::getline(f, line) || line != "libproj tuning cache 1") return false;
+    names->assign(kNumBuckets, "");
+    while (std::getline(f, line)) {
+        int b = -1;
+        char name[160] = {0};
+        if (sscanf(line.c_str(), "bucket %d %159s", &b, name) == 2 && b >= 0 && b < kNumBuckets) (*names)[b] = name;
+    }
+    return true;
+}
+
+static void cache_write(proj_plan* p)
+{
+    const std::string tmp = p->cache_path + ".tmp";
+    {
+        std::ofstream f(tmp);
+        if (!f) return;
+        f << "libproj tuning cache 1\n";
+        f << "# N=" << p->N << " K=" << p->K << " dtype=" << (p->dtype ? "bf16" : "f32")
+          << " epilogue=" << (p->epi ? "swiglu" : "none") << " arch=" << p->arch << "\n";
+        for (int b = 0; b < kNumBuckets; ++b)
+            if (p->choice[b] >= 0)
+                f << "bucket " << b << " " << p->cands[p->choice[b]].name << " " << p->choice_us[b] << "\n";
+        if (!f) return;
+    }
+    if (std::rename(tmp.c_str(), p->cache_path.c_str()) != 0) std::remove(tmp.c_str());
+}
+
 int tune_plan(proj_plan* p)
 {
     const double t0 = now_s();
@@ -454,6 +521,18 @@ int tune_plan(proj_plan* p)
     T.p = p;
     int rc;
     if ((rc = T.setup(kBuckets[kNumBuckets - 1].hi))) return rc;
+
+    std::vector<std::string> cached;
+    p->cache = "off";
+    if (const char* dir = getenv("PROJ_CACHE_DIR")) {
+        if (*dir) {
+            char file[64];
+            snprintf(file, sizeof file, "/proj-%016llx.txt", (unsigned long long)p->key);
+            p->cache_path = std::string(dir) + file;
+            p->cache = cache_read(p->cache_path, &cached) ? "hit" : "miss";
+        }
+    }
+    bool retuned = false;
 
     p->timings.assign(kNumBuckets, {});
     p->rejected.assign(kNumBuckets, {});
@@ -506,6 +585,25 @@ int tune_plan(proj_plan* p)
             return 0;
         };
 
+        if (!cached.empty() && !cached[b].empty() && !(force && *force)) {
+            int ci = -1;
+            for (int i = 0; i < (int)p->cands.size(); ++i)
+                if (p->cands[i].name == cached[b]) ci = i;
+            if (ci >= 0 && (applies(p->cands[ci], b, p) || p->cands[ci].fam == Family::Plain)) {
+                const int v = validate(ci);
+                if (v < 0) return v;
+                if (v == 0) {
+                    snprintf(line, sizeof line, "[autotune] proj %lldx%lld %lld..%lld rows: %s (cached, re-validated)",
+                             (long long)p->N, (long long)p->K, (long long)br.lo, (long long)br.hi, cached[b].c_str());
+                    plog(p, line);
+                    p->choice[b] = ci;
+                    p->choice_us[b] = -1;
+                    continue;
+                }
+            }
+            p->cache = "stale";
+        }
+        retuned = true;
         for (int ci = 0; ci < (int)p->cands.size(); ++ci) {
             const Candidate& c = p->cands[ci];
             if (!applies(c, b, p)) continue;
@@ -560,6 +658,7 @@ int tune_plan(proj_plan* p)
         p->choice[b] = best;
         p->choice_us[b] = best_us;
     }
+    if (!p->cache_path.empty() && retuned && do_time && !(force && *force)) cache_write(p);
     p->tune_s = now_s() - t0;
     return PROJ_OK;
 }
@@ -591,6 +690,7 @@ int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out)
 
     p->cands = enumerate_candidates(N, K, cus, epi);
     const std::string src = emit_source(N, K, dtype, p->arch, cus, p->cands, epi);
+    if ((rc = cache_key(p.get(), src))) return rc;
     const double t0 = now_s();
     std::shared_ptr<std::vector<char>> code;
     char name[96];

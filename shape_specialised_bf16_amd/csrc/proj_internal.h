@@ -106,6 +106,9 @@ struct proj_plan {
     int64_t N = 0, K = 0;
     int dtype = 0;
     int epi = 0;        // PROJ_EPI_NONE or PROJ_EPI_SWIGLU
+    uint64_t key = 0;   // tuning-cache key: device, runtime and driver versions, emitted source
+    std::string cache;  // tuning cache: "off", "miss", "hit", "stale" (a cached choice failed the gate)
+    std::string cache_path;
     int64_t NO = 0;     // columns of Y: N, or N/2 with the SwiGLU epilogue
     int device = -1;
     std::string arch;

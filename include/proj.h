@@ -43,8 +43,8 @@ typedef struct proj_plan proj_plan; /* opaque; owned by the library */
 /* Storage type of Y.  X and W are always bf16. */
 enum { PROJ_OUT_F32 = 0, PROJ_OUT_BF16 = 1 };
 
-/* Epilogue fused into a plan's kernels (proj_plan_create_ex). */
-enum { PROJ_EPI_NONE = 0, PROJ_EPI_SWIGLU = 1 };
+/* Work folded into a plan's kernels (flags of proj_plan_create_ex). */
+enum { PROJ_EPI_NONE = 0, PROJ_EPI_SWIGLU = 1, PROJ_PRO_RMSNORM = 2 };
 
 enum {
     PROJ_OK = 0,
@@ -90,7 +90,11 @@ enum {
 proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
 
 /*
- * Like proj_plan_create, with an epilogue folded into every kernel of the plan.
+ * Like proj_plan_create, with work folded into the plan's kernels; `fusion` is
+ * PROJ_EPI_NONE or an OR of the flags below.  The pages fold exactly these two
+ * ("#004 the same compiler on Apple's chips", section "Decode": the norms into
+ * the projection that follows them, the SwiGLU into the gate_up projection),
+ * each with the same bits as the kernels it replaces.
  *
  * PROJ_EPI_SWIGLU: W is a fused gate_up matrix, rows [0, N/2) the gate
  * projection and rows [N/2, N) the up projection (N even), and the plan's Y is
@@ -110,10 +114,24 @@ proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
  * kernel families that have the fused epilogue are candidates (vector GEMVs
  * with an even row count per wave, whole-tile MFMA GEMMs, the plain kernel).
  *
- * epilogue outside the enum, or an odd N with PROJ_EPI_SWIGLU, returns NULL
- * with PROJ_EINVAL in proj_last_error.  PROJ_EPI_NONE is proj_plan_create.
+ * PROJ_PRO_RMSNORM: X is normalised first, row by row, as by proj_rmsnorm with
+ * epsilon `norm_eps` (a constant of the generated code) and the norm weights
+ * `gamma` passed to proj_run_ex; Y is then the projection of the normalised
+ * rows, bit-identical to proj_rmsnorm followed by a plain plan running the
+ * same kernel variant.  Every candidate of the plan can run unfused (the norm
+ * kernel into a workspace of the plan, 8192 x K bf16, then the candidate on
+ * it); the vector GEMVs for M = 1 also come with the norm folded in (each
+ * block normalises the row into LDS first), and the load-time tuner picks
+ * between them by measurement -- the pages find the folded norm faster on
+ * small models and slower from the 4B on, where every workgroup re-reads the
+ * whole row.  proj_run on such a plan fails with PROJ_EINVAL: use proj_run_ex.
+ *
+ * Unknown flags, an odd N with PROJ_EPI_SWIGLU, or a negative or non-finite
+ * norm_eps with PROJ_PRO_RMSNORM return NULL with PROJ_EINVAL in
+ * proj_last_error.  norm_eps is ignored without PROJ_PRO_RMSNORM;
+ * proj_plan_create_ex(N, K, dtype, PROJ_EPI_NONE, 0) is proj_plan_create.
  */
-proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int epilogue);
+proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int fusion, float norm_eps);
 
 /*
  * Enqueue Y[0:M, :] = X[0:M, :] . W^T on `stream`.  Rows of Y at or past M are
@@ -131,6 +149,12 @@ proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int epilogue);
  */
 int proj_run(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M,
              hipStream_t stream);
+
+/* proj_run with the norm weights of a PROJ_PRO_RMSNORM plan: gamma is a device
+ * pointer to K f32 values, 16-byte aligned, owned by the caller (NULL for
+ * plans without the prologue; missing or misaligned for one: PROJ_EINVAL). */
+int proj_run_ex(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, const float* gamma,
+                hipStream_t stream);
 
 /* Free the plan's module and workspace.  NULL-safe.  No launch of this plan may
  * still be pending on the device. */
@@ -153,9 +177,9 @@ const char* proj_last_error(void);
  */
 int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* buf, size_t cap,
                      size_t* needed);
-/* The same for a plan with an epilogue (proj_plan_create_ex). */
-int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int epilogue, const char* arch, char* buf, size_t cap,
-                        size_t* needed);
+/* The same for a plan with fused work (proj_plan_create_ex's fusion flags and epsilon). */
+int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, const char* arch, char* buf,
+                        size_t cap, size_t* needed);
 
 /* JSON text (host buffer) describing the plan: shape, candidates, per-bucket
  * choice and timings, the tuner log, compile and tuning seconds.  Same size
@@ -179,6 +203,9 @@ int64_t proj_plan_candidate_max_m(const proj_plan* plan, int idx);
  */
 int proj_run_candidate(const proj_plan* plan, int idx, const void* X, const void* W, void* Y,
                        int64_t M, hipStream_t stream);
+/* ... with the norm weights of a PROJ_PRO_RMSNORM plan (as proj_run_ex). */
+int proj_run_candidate_ex(const proj_plan* plan, int idx, const void* X, const void* W, void* Y, int64_t M,
+                          const float* gamma, hipStream_t stream);
 
 /* Index of the candidate proj_run uses for M rows (M >= 1), or a negative error. */
 int proj_plan_choice(const proj_plan* plan, int64_t M);
@@ -196,6 +223,22 @@ int proj_plan_choice(const proj_plan* plan, int64_t M);
  * negative sizes, odd N, a bad dtype or null pointers give PROJ_EINVAL.
  */
 int proj_swiglu(const void* G, void* H, int64_t M, int64_t N, int dtype, hipStream_t stream);
+
+/*
+ * Enqueue the RMSNorm of each of the M rows of X [M, K] (bf16 bit patterns)
+ * into Xn [M, K] (bf16): with ss = sum_k x_k^2 in f32 in one fixed order (a
+ * 256-thread block per row: thread t adds k = t, t + 256, ... with FMA, then
+ * pairwise halving of the 256 partials),
+ *     r = 1 / sqrt(ss / K + eps),   Xn[m][k] = bf16((x_k * r) * gamma[k]),
+ * the products in f32, IEEE division and square root, one rounding to bf16.
+ * gamma is K f32 values (pass 1 + w for a norm whose weights are centred on
+ * zero).  The separate kernel that the PROJ_PRO_RMSNORM prologue replaces
+ * ("#004 the same compiler on Apple's chips", section "Decode").  Device
+ * pointers owned by the caller; Xn must not overlap X.  M == 0 or K == 0 is a
+ * no-op; negative sizes, a negative or non-finite eps, M >= 2^31 or null
+ * pointers give PROJ_EINVAL.
+ */
+int proj_rmsnorm(const void* X, const float* gamma, void* Xn, int64_t M, int64_t K, float eps, hipStream_t stream);
 
 /* ---- measurement support (shape-independent) ---- */
 

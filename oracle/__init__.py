@@ -72,6 +72,11 @@ def _load():
         lib.oracle_round_bf16.restype = None
         lib.oracle_round_f32_to_bf16.argtypes = [_p, _p, _i64, ctypes.c_int]
         lib.oracle_round_f32_to_bf16.restype = None
+        lib.oracle_rmsnorm.argtypes = [_p, _p, _i64, _i64, ctypes.c_double, _p]
+        lib.oracle_rmsnorm.restype = None
+        lib.oracle_rmsnorm_matmul.argtypes = [_p, _p, _p, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _p,
+                                              ctypes.c_int]
+        lib.oracle_rmsnorm_matmul.restype = None
         lib.oracle_swiglu.argtypes = [_p, _i64, _i64, _p]
         lib.oracle_swiglu.restype = None
         lib.oracle_max_threads.argtypes = []
@@ -130,6 +135,37 @@ def swiglu(Y: np.ndarray) -> np.ndarray:
     if H.size:
         _load().oracle_swiglu(Y.ctypes.data, M, N, H.ctypes.data)
     return H
+
+
+def rmsnorm(X: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """fp64 RMS-normalised rows of X (bf16 bits [M, K]) with f32 gamma [K]; see oracle.c."""
+    X = _u16(X, "X")
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    M, K = X.shape
+    if g.shape != (K,):
+        raise ValueError("gamma must have K values")
+    out = np.empty((M, K), dtype=np.float64)
+    if out.size:
+        _load().oracle_rmsnorm(X.ctypes.data, g.ctypes.data, M, K, float(eps), out.ctypes.data)
+    return out
+
+
+def rmsnorm_matmul(X: np.ndarray, gamma: np.ndarray, W: np.ndarray, eps: float, absolute: bool = False,
+                   threads: int = 0) -> np.ndarray:
+    """fp64 projection of the RMS-normalised rows (or, with absolute, the sums of
+    the terms' magnitudes); see oracle.c."""
+    X = _u16(X, "X")
+    W = _u16(W, "W")
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    M, K = X.shape
+    N, K2 = W.shape
+    if K != K2 or g.shape != (K,):
+        raise ValueError("shape mismatch")
+    out = np.empty((M, N), dtype=np.float64)
+    if out.size:
+        _load().oracle_rmsnorm_matmul(X.ctypes.data, g.ctypes.data, W.ctypes.data, M, N, K, float(eps),
+                                      1 if absolute else 0, out.ctypes.data, threads)
+    return out
 
 
 def round_f32(Y: np.ndarray) -> np.ndarray:

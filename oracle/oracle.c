@@ -33,6 +33,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -190,6 +191,57 @@ void oracle_swiglu(const double *Y, int64_t M, int64_t N, double *H)
             const double u = Y[m * N + half + j];
             H[m * half + j] = g / (1.0 + exp(-g)) * u;
         }
+}
+
+/*
+ * RMSNorm of each row of X, in double ("#004 the same compiler on Apple's
+ * chips", section "Decode": the norm folded into the projection that follows
+ * it).  Reading of the norm (the pages name it, not its formula): per row,
+ *     r = 1 / sqrt((1/K) sum_k x_k^2 + eps),   xn_k = x_k * r * gamma_k,
+ * gamma given as f32 values; computed here exactly from the inputs (the sum of
+ * squares in ascending k), no rounding to bf16.
+ */
+void oracle_rmsnorm(const uint16_t *X, const float *gamma, int64_t M, int64_t K,
+                    double eps, double *Xn)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double v = oracle_bf16_to_f64(X[m * K + k]);
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            Xn[m * K + k] = oracle_bf16_to_f64(X[m * K + k]) * r * (double)gamma[k];
+    }
+}
+
+/*
+ * The projection of the RMS-normalised rows: Y[m][n] = sum_k xn[m][k] w[n][k]
+ * with xn from oracle_rmsnorm, k ascending, in double.  With absolute != 0 it
+ * returns sum_k |xn[m][k] w[n][k]| instead (the scale of the terms, for
+ * the acceptance rule).
+ */
+void oracle_rmsnorm_matmul(const uint16_t *X, const float *gamma, const uint16_t *W,
+                           int64_t M, int64_t N, int64_t K, double eps, int absolute,
+                           double *Y, int threads)
+{
+    double *Xn = (double *)malloc((size_t)(M > 0 ? M : 1) * (size_t)(K > 0 ? K : 1) * sizeof(double));
+    if (!Xn) return;
+    oracle_rmsnorm(X, gamma, M, K, eps, Xn);
+    set_threads(threads);
+    int64_t total = M * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        const int64_t m = i / N, n = i % N;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double t = Xn[m * K + k] * oracle_bf16_to_f64(W[n * K + k]);
+            acc += absolute ? fabs(t) : t;
+        }
+        Y[i] = acc;
+    }
+    free(Xn);
 }
 
 /* Number of threads an OpenMP parallel region would use. */

@@ -148,3 +148,40 @@ def check_swiglu(y: np.ndarray, g: np.ndarray, u: np.ndarray, dtype: str) -> Rep
     return Report(n=y.size, n_bad=int(bad.sum()), n_second_clause=0,
                   worst_excess=float(excess[wi]) if y.size else 0.0,
                   gate_ratio=_gate_ratio(y, h), worst_index=wi)
+
+
+NORM_REL = 2.0 ** -8    # bf16 rounding of a normalised element (2^-9) plus its f32 scale (taken generously)
+
+
+def check_norm_projection(y: np.ndarray, ref: np.ndarray, terms: np.ndarray, dtype: str) -> Report:
+    """The projection of RMS-normalised rows, ``y`` (f32 values or bf16 bits),
+    against the oracle's fp64 ``ref`` (``oracle.rmsnorm_matmul``) and the sums
+    of the terms' magnitudes ``terms`` (the same with ``absolute``).
+
+    Derivation: the device multiplies bf16(x r' gamma) by w, where the
+    normalised element is rounded to bf16 (relative error <= 2^-9) and r' is
+    the f32 scale (relative error well under 2^-12 at any K used here); each
+    term is therefore within NORM_REL = 2^-8 of its exact value, and the sum
+    within 2^-8 * terms, on top of the projection's own rule (the f32 rule,
+    or the bf16 rule for a bf16 Y) for the f32 accumulation and the store."""
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    extra = NORM_REL * np.asarray(terms, dtype=np.float64).ravel()
+    if dtype == "bf16":
+        yv = bf16_bits_to_f64(np.asarray(y, dtype=np.uint16).ravel())
+    else:
+        yv = np.asarray(y, dtype=np.float64).ravel()
+    if yv.shape != ref.shape:
+        raise ValueError(f"shape mismatch {yv.shape} vs {ref.shape}")
+    a_f32 = F32_RTOL * (np.abs(ref) + 1.0) + extra
+    e_f32 = np.abs(yv - ref)
+    excess = np.where(np.isfinite(e_f32), e_f32 / a_f32, np.inf)
+    if dtype == "bf16":         # within one bf16 ulp of bf16(ref), or the f32 clause
+        R = bf16_bits_to_f64(round_bf16(ref))
+        a_b = bf16_ulp(R) + extra
+        e_b = np.abs(yv - R)
+        excess = np.minimum(excess, np.where(np.isfinite(e_b), e_b / a_b, np.inf))
+    bad = ~(excess <= 1.0)
+    wi = int(np.argmax(excess)) if yv.size else -1
+    return Report(n=yv.size, n_bad=int(bad.sum()), n_second_clause=0,
+                  worst_excess=float(excess[wi]) if yv.size else 0.0,
+                  gate_ratio=_gate_ratio(yv, ref), worst_index=wi)

@@ -26,6 +26,7 @@ OUT_F32 = 0
 OUT_BF16 = 1
 EPI_NONE = 0
 EPI_SWIGLU = 1
+PRO_RMSNORM = 2
 _ERRORS = {-1: "PROJ_EINVAL", -2: "PROJ_EDEVICE", -3: "PROJ_ECOMPILE", -4: "PROJ_ENOCAND", -5: "PROJ_ENOMEM"}
 
 # Every function declared in include/proj.h.
@@ -33,7 +34,8 @@ EXPORTED_SYMBOLS = (
     "proj_plan_create", "proj_run", "proj_plan_destroy", "proj_last_error", "proj_emit_source",
     "proj_plan_describe", "proj_plan_num_candidates", "proj_plan_candidate_name",
     "proj_plan_candidate_max_m", "proj_run_candidate", "proj_plan_choice", "proj_probe_read",
-    "proj_round_bf16", "proj_plan_create_ex", "proj_emit_source_ex", "proj_swiglu",
+    "proj_round_bf16", "proj_plan_create_ex", "proj_emit_source_ex", "proj_swiglu", "proj_run_ex",
+    "proj_run_candidate_ex", "proj_rmsnorm",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -51,10 +53,16 @@ _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _lib.proj_plan_create.argtypes = [_i64, _i64, ctypes.c_int]
 _lib.proj_plan_create.restype = _p
-_lib.proj_plan_create_ex.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int]
+_lib.proj_plan_create_ex.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_float]
 _lib.proj_plan_create_ex.restype = _p
-_lib.proj_emit_source_ex.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_char_p, ctypes.c_char_p,
-                                     ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+_lib.proj_run_ex.argtypes = [_p, _p, _p, _p, _i64, _p, _p]
+_lib.proj_run_ex.restype = ctypes.c_int
+_lib.proj_run_candidate_ex.argtypes = [_p, ctypes.c_int, _p, _p, _p, _i64, _p, _p]
+_lib.proj_run_candidate_ex.restype = ctypes.c_int
+_lib.proj_rmsnorm.argtypes = [_p, _p, _p, _i64, _i64, ctypes.c_float, _p]
+_lib.proj_rmsnorm.restype = ctypes.c_int
+_lib.proj_emit_source_ex.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_char_p,
+                                     ctypes.c_char_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
 _lib.proj_emit_source_ex.restype = ctypes.c_int
 _lib.proj_swiglu.argtypes = [_p, _p, _i64, _i64, ctypes.c_int, _p]
 _lib.proj_swiglu.restype = ctypes.c_int
@@ -114,9 +122,12 @@ def _epi_code(epilogue) -> int:
     raise ValueError(f"unsupported epilogue {epilogue!r} (None or 'swiglu')")
 
 
-def emit_source(N: int, K: int, dtype: str = "f32", arch: str = "gfx950", epilogue=None) -> str:
-    """The HIP source a plan for (N, K, dtype[, epilogue]) compiles (no GPU needed)."""
-    return _text(_lib.proj_emit_source_ex, N, K, _dtype_code(dtype), _epi_code(epilogue), arch.encode())
+def emit_source(N: int, K: int, dtype: str = "f32", arch: str = "gfx950", epilogue=None, rmsnorm_eps=None) -> str:
+    """The HIP source a plan for (N, K, dtype[, epilogue, RMSNorm prologue])
+    compiles (no GPU needed)."""
+    fusion = _epi_code(epilogue) | (PRO_RMSNORM if rmsnorm_eps is not None else 0)
+    return _text(_lib.proj_emit_source_ex, N, K, _dtype_code(dtype), fusion,
+                 float(rmsnorm_eps or 0.0), arch.encode())
 
 
 def _dtype_code(dtype) -> int:
@@ -156,16 +167,19 @@ class Plan:
     """A compiled, tuned projection plan for fixed (N, K) and output dtype.
 
     epilogue="swiglu": W is a gate_up matrix (gate rows then up rows) and the
-    plan writes Y[M, N/2] = silu(gate) * up (see proj_plan_create_ex)."""
+    plan writes Y[M, N/2] = silu(gate) * up; rmsnorm_eps=<eps>: X is
+    RMS-normalised first with the gamma given to run (see proj_plan_create_ex)."""
 
-    def __init__(self, N: int, K: int, dtype="f32", epilogue=None):
+    def __init__(self, N: int, K: int, dtype="f32", epilogue=None, rmsnorm_eps=None):
         self.N, self.K = int(N), int(K)
         self.dtype_code = _dtype_code(dtype)
         self.epi_code = _epi_code(epilogue)
+        self.norm = rmsnorm_eps is not None
         self.NO = self.N // 2 if self.epi_code == EPI_SWIGLU else self.N
-        h = _lib.proj_plan_create_ex(self.N, self.K, self.dtype_code, self.epi_code)
+        fusion = self.epi_code | (PRO_RMSNORM if self.norm else 0)
+        h = _lib.proj_plan_create_ex(self.N, self.K, self.dtype_code, fusion, float(rmsnorm_eps or 0.0))
         if not h:
-            raise ProjError(-1, f"proj_plan_create_ex({N}, {K}, {dtype}, {epilogue})")
+            raise ProjError(-1, f"proj_plan_create_ex({N}, {K}, {dtype}, {epilogue}, {rmsnorm_eps})")
         self._h = ctypes.c_void_p(h)
 
     @property
@@ -204,21 +218,33 @@ class Plan:
             raise ValueError(f"Y must be a contiguous [>= {M}, {self.NO}] {self.out_dtype} matrix")
         return M, Y
 
-    def run(self, X, W, Y=None, stream=None):
-        """Y[:M] = X . W^T for all M rows of X, enqueued on `stream` (default: current)."""
+    def _gamma(self, gamma):
+        import torch
+        if gamma is None:
+            return None
+        if not gamma.is_cuda or gamma.dtype != torch.float32 or gamma.numel() != self.K or not gamma.is_contiguous():
+            raise ValueError(f"gamma must be a contiguous float32 device vector of {self.K} values")
+        return gamma.data_ptr()
+
+    def run(self, X, W, Y=None, stream=None, gamma=None):
+        """Y[:M] = X . W^T for all M rows of X (RMS-normalised with gamma for a
+        plan with the norm prologue), enqueued on `stream` (default: current)."""
         M, Y = self._prep(X, W, Y)
-        _check(_lib.proj_run(self._h, X.data_ptr(), W.data_ptr(), Y.data_ptr(), M, _stream_handle(stream)),
-               "proj_run")
+        _check(_lib.proj_run_ex(self._h, X.data_ptr(), W.data_ptr(), Y.data_ptr(), M, self._gamma(gamma),
+                                _stream_handle(stream)), "proj_run_ex")
         return Y
 
-    def run_ptr(self, X_ptr: int, W_ptr: int, Y_ptr: int, M: int, stream_handle) -> None:
-        """proj_run on raw device addresses (benchmark loops)."""
-        _check(_lib.proj_run(self._h, X_ptr, W_ptr, Y_ptr, M, stream_handle), "proj_run")
+    def run_ptr(self, X_ptr: int, W_ptr: int, Y_ptr: int, M: int, stream_handle, gamma_ptr=None) -> None:
+        """proj_run(_ex) on raw device addresses (benchmark loops)."""
+        if gamma_ptr is None:
+            _check(_lib.proj_run(self._h, X_ptr, W_ptr, Y_ptr, M, stream_handle), "proj_run")
+        else:
+            _check(_lib.proj_run_ex(self._h, X_ptr, W_ptr, Y_ptr, M, gamma_ptr, stream_handle), "proj_run_ex")
 
-    def run_candidate(self, idx: int, X, W, Y=None, stream=None):
+    def run_candidate(self, idx: int, X, W, Y=None, stream=None, gamma=None):
         M, Y = self._prep(X, W, Y)
-        _check(_lib.proj_run_candidate(self._h, idx, X.data_ptr(), W.data_ptr(), Y.data_ptr(), M,
-                                       _stream_handle(stream)), "proj_run_candidate")
+        _check(_lib.proj_run_candidate_ex(self._h, idx, X.data_ptr(), W.data_ptr(), Y.data_ptr(), M,
+                                          self._gamma(gamma), _stream_handle(stream)), "proj_run_candidate_ex")
         return Y
 
     def num_candidates(self) -> int:
@@ -263,6 +289,24 @@ def swiglu(G, H=None, stream=None):
     _check(_lib.proj_swiglu(G.data_ptr(), H.data_ptr(), M, N, _dtype_code(G.dtype), _stream_handle(stream)),
            "proj_swiglu")
     return H
+
+
+def rmsnorm(X, gamma, eps: float, Xn=None, stream=None):
+    """Xn = RMSNorm(X) * gamma row by row with the library's kernel (the
+    unfused path of the norm prologue): X bf16 [M, K], gamma float32 [K]."""
+    import torch
+    if X.dim() != 2 or not X.is_contiguous() or X.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("rmsnorm: X must be a contiguous bf16 [M, K] matrix")
+    M, K = X.shape
+    if not gamma.is_cuda or gamma.dtype != torch.float32 or gamma.numel() != K or not gamma.is_contiguous():
+        raise ValueError(f"rmsnorm: gamma must be a contiguous float32 device vector of {K} values")
+    if Xn is None:
+        Xn = torch.empty_like(X)
+    elif tuple(Xn.shape) != (M, K) or Xn.element_size() != 2 or not Xn.is_contiguous():
+        raise ValueError(f"rmsnorm: Xn must be a contiguous 16-bit [{M}, {K}] matrix")
+    _check(_lib.proj_rmsnorm(X.data_ptr(), gamma.data_ptr(), Xn.data_ptr(), M, K, float(eps), _stream_handle(stream)),
+           "proj_rmsnorm")
+    return Xn
 
 
 def round_bf16(inp, out, stream=None) -> None:

@@ -16,17 +16,18 @@ int set_error(int code, const char* f, ...);
 int compile_source(const std::string& src, const std::string& arch, const char* name,
                    std::shared_ptr<std::vector<char>>* code);
 int device_arch(int dev, std::string* arch, int* cus);
-int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out);
+int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, proj_plan** out);
 void destroy_plan(proj_plan* p);
-int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream);
+int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream,
+             const float* gamma);
 int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M);
 int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y,
-                     int64_t M, hipStream_t stream);
+                     int64_t M, hipStream_t stream, const float* gamma);
 
 // Shape-independent support module, one per device, loaded on first use.
 struct SupportModule {
     hipModule_t mod = nullptr;
-    hipFunction_t probe = nullptr, round = nullptr, swiglu_f32 = nullptr, swiglu_bf16 = nullptr;
+    hipFunction_t probe = nullptr, round = nullptr, swiglu_f32 = nullptr, swiglu_bf16 = nullptr, rmsnorm = nullptr;
     int cus = 256;
 };
 static std::mutex g_support_mu;
@@ -51,7 +52,8 @@ static int support_module(SupportModule** out)
         if ((e = hipModuleGetFunction(&sm.probe, sm.mod, "proj_probe_read")) != hipSuccess ||
             (e = hipModuleGetFunction(&sm.round, sm.mod, "proj_round_bf16")) != hipSuccess ||
             (e = hipModuleGetFunction(&sm.swiglu_f32, sm.mod, "proj_swiglu_f32")) != hipSuccess ||
-            (e = hipModuleGetFunction(&sm.swiglu_bf16, sm.mod, "proj_swiglu_bf16")) != hipSuccess)
+            (e = hipModuleGetFunction(&sm.swiglu_bf16, sm.mod, "proj_swiglu_bf16")) != hipSuccess ||
+            (e = hipModuleGetFunction(&sm.rmsnorm, sm.mod, "proj_rmsnorm_rows")) != hipSuccess)
             return set_error(PROJ_EDEVICE, "hipModuleGetFunction(support): %s", hipGetErrorString(e));
     }
     *out = &sm;
@@ -84,7 +86,8 @@ static std::string describe(const proj_plan* p)
 {
     std::ostringstream s;
     s << "{\"N\": " << p->N << ", \"K\": " << p->K << ", \"NO\": " << p->NO << ", \"epilogue\": \""
-      << (p->epi ? "swiglu" : "none") << "\", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
+      << (p->epi ? "swiglu" : "none") << "\", \"prologue\": \"" << (p->pro ? "rmsnorm" : "none")
+      << "\", \"norm_eps\": " << p->eps << ", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
       << "\", \"arch\": \"" << p->arch << "\", \"device\": " << p->device << ", \"compile_s\": " << p->compile_s
       << ", \"tune_s\": " << p->tune_s << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
       << ", \"cache\": \"" << p->cache << "\", \"cache_path\": \"" << json_escape(p->cache_path) << "\""
@@ -119,20 +122,26 @@ extern "C" {
 
 proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype)
 {
-    return proj_plan_create_ex(N, K, dtype, PROJ_EPI_NONE);
+    return proj_plan_create_ex(N, K, dtype, PROJ_EPI_NONE, 0.f);
 }
 
-proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int epilogue)
+proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int fusion, float norm_eps)
 {
     g_last_error.clear();
     proj_plan* p = nullptr;
-    if (create_plan(N, K, dtype, epilogue, &p) != PROJ_OK) return nullptr;
+    if (create_plan(N, K, dtype, fusion, norm_eps, &p) != PROJ_OK) return nullptr;
     return p;
 }
 
 int proj_run(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream)
 {
-    return run_plan(plan, X, W, Y, M, stream);
+    return run_plan(plan, X, W, Y, M, stream, nullptr);
+}
+
+int proj_run_ex(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, const float* gamma,
+                hipStream_t stream)
+{
+    return run_plan(plan, X, W, Y, M, stream, gamma);
 }
 
 void proj_plan_destroy(proj_plan* plan) { destroy_plan(plan); }
@@ -141,22 +150,22 @@ const char* proj_last_error(void) { return g_last_error.c_str(); }
 
 int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* buf, size_t cap, size_t* needed)
 {
-    return proj_emit_source_ex(N, K, dtype, PROJ_EPI_NONE, arch, buf, cap, needed);
+    return proj_emit_source_ex(N, K, dtype, PROJ_EPI_NONE, 0.f, arch, buf, cap, needed);
 }
 
-int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int epilogue, const char* arch, char* buf, size_t cap,
-                        size_t* needed)
+int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, const char* arch, char* buf,
+                        size_t cap, size_t* needed)
 {
+    const int epilogue = fusion & PROJ_EPI_SWIGLU;
+    if (fusion & ~(PROJ_EPI_SWIGLU | PROJ_PRO_RMSNORM)) return set_error(PROJ_EINVAL, "invalid fusion flags %d", fusion);
     if (N < 1 || K < 8 || K % 8 != 0)
         return set_error(PROJ_EINVAL, "invalid shape N=%lld K=%lld", (long long)N, (long long)K);
     if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16) return set_error(PROJ_EINVAL, "invalid dtype %d", dtype);
-    if (epilogue != PROJ_EPI_NONE && epilogue != PROJ_EPI_SWIGLU)
-        return set_error(PROJ_EINVAL, "invalid epilogue %d", epilogue);
     if (epilogue == PROJ_EPI_SWIGLU && N % 2)
         return set_error(PROJ_EINVAL, "the SwiGLU epilogue needs an even N, got N=%lld", (long long)N);
     const std::string a = (arch && *arch) ? arch : "gfx950";
-    return copy_text(emit_source(N, K, dtype, a, kDefaultCUs, enumerate_candidates(N, K, kDefaultCUs, epilogue),
-                                 epilogue),
+    return copy_text(emit_source(N, K, dtype, a, kDefaultCUs, enumerate_candidates(N, K, kDefaultCUs, fusion),
+                                 fusion, (fusion & PROJ_PRO_RMSNORM) ? norm_eps : 0.f),
                      buf, cap, needed);
 }
 
@@ -194,10 +203,18 @@ int64_t proj_plan_candidate_max_m(const proj_plan* plan, int idx)
 int proj_run_candidate(const proj_plan* plan, int idx, const void* X, const void* W, void* Y, int64_t M,
                        hipStream_t stream)
 {
+    return proj_run_candidate_ex(plan, idx, X, W, Y, M, nullptr, stream);
+}
+
+int proj_run_candidate_ex(const proj_plan* plan, int idx, const void* X, const void* W, void* Y, int64_t M,
+                          const float* gamma, hipStream_t stream)
+{
     int rc = check_run_args(plan, X, W, Y, M);
     if (rc || M == 0) return rc;
     if (idx < 0 || idx >= (int)plan->cands.size()) return set_error(PROJ_EINVAL, "candidate %d out of range", idx);
-    return launch_candidate(plan, plan->cands[idx], X, W, Y, M, stream);
+    if (plan->pro && (!gamma || ((uintptr_t)gamma & 15)))
+        return set_error(PROJ_EINVAL, "this plan has the RMSNorm prologue: a 16-byte aligned gamma is required");
+    return launch_candidate(plan, plan->cands[idx], X, W, Y, M, stream, gamma);
 }
 
 int proj_plan_choice(const proj_plan* plan, int64_t M)
@@ -226,6 +243,27 @@ int proj_probe_read(const void* buf, int64_t bytes, uint32_t never, void* sink, 
     const unsigned gx = (unsigned)((n16 + 2047) / 2048);  // one 32 KiB span per block
     hipError_t e = hipModuleLaunchKernel(sm->probe, gx, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
     if (e != hipSuccess) return set_error(PROJ_EDEVICE, "probe launch: %s", hipGetErrorString(e));
+    return PROJ_OK;
+}
+
+int proj_rmsnorm(const void* X, const float* gamma, void* Xn, int64_t M, int64_t K, float eps, hipStream_t stream)
+{
+    if (M < 0 || K < 0) return set_error(PROJ_EINVAL, "M and K must not be negative");
+    if (!(eps >= 0.f && eps < 1e30f)) return set_error(PROJ_EINVAL, "invalid epsilon %g", (double)eps);
+    if (M == 0 || K == 0) return PROJ_OK;
+    if (M > 0x7fffffff) return set_error(PROJ_EINVAL, "M=%lld: at most 2^31-1 rows", (long long)M);
+    if (!X || !gamma || !Xn) return set_error(PROJ_EINVAL, "null pointer");
+    SupportModule* sm = nullptr;
+    int rc = support_module(&sm);
+    if (rc) return rc;
+    const void* x = X;
+    const float* g = gamma;
+    void* xo = Xn;
+    long kk = (long)K;
+    float e2 = eps;
+    void* args[] = {&x, &g, &xo, &kk, &e2};
+    hipError_t e = hipModuleLaunchKernel(sm->rmsnorm, (unsigned)M, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
+    if (e != hipSuccess) return set_error(PROJ_EDEVICE, "rmsnorm launch: %s", hipGetErrorString(e));
     return PROJ_OK;
 }
 

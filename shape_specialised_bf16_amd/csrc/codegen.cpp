@@ -34,8 +34,9 @@ static std::string fmt(const char* f, ...)
     return buf;
 }
 
-std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int epi)
+std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int fusion)
 {
+    const int epi = fusion & 1, pro = (fusion & 2) ? 1 : 0;
     std::vector<Candidate> out;
     const int64_t CH = K / 8;  // 16-byte chunks per row
 
@@ -75,6 +76,20 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int e
                 out.push_back(c);
             }
         }
+    }
+
+    // ---- with the RMSNorm prologue: every candidate also runs unfused (the norm
+    //      kernel into the plan's workspace, then the candidate on it); the M = 1
+    //      vector GEMVs come a second time with the norm folded in ("_nf")
+    if (pro) {
+        const size_t n = out.size();
+        for (size_t i = 0; i < n; ++i)
+            if (out[i].fam == Family::GemvValu && out[i].MMAX == 1) {
+                Candidate c = out[i];
+                c.PRO = 1;
+                c.name += "_nf";
+                out.push_back(c);
+            }
     }
 
     // ---- MFMA skinny GEMV for M <= 16: (S waves splitting K, U MFMA steps per load batch)
@@ -163,13 +178,17 @@ std::string emit_support_source()
 }
 
 std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
-                        const std::vector<Candidate>& cands, int epi)
+                        const std::vector<Candidate>& cands, int fusion, float norm_eps)
 {
     const char* out = dtype == 1 ? "OUT_BF16" : "OUT_F32";
+    const int epi = fusion & 1;
+    char eps_lit[64];
+    snprintf(eps_lit, sizeof eps_lit, "%a", (double)norm_eps);
     std::ostringstream s;
     s << "// Generated by libproj for Y[M," << N << "] = X[M," << K << "] . W[" << N << "," << K
       << "]^T, output " << (dtype == 1 ? "bf16" : "f32") << ", target " << arch
-      << (epi ? ", SwiGLU epilogue: Y[M, N/2] = silu(gate) * up" : "") << ".\n";
+      << (epi ? ", SwiGLU epilogue: Y[M, N/2] = silu(gate) * up" : "")
+      << ((fusion & 2) ? ", RMSNorm prologue on X" : "") << ".\n";
     s << "// Every constant below is an immediate of the kernels; M is the only run-time size.\n";
     s << "constexpr long N = " << N << ";            // output rows = rows of W\n";
     s << "constexpr long K = " << K << ";            // row length (bf16 values)\n";
@@ -179,7 +198,9 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
     s << "constexpr int DEVICE_CUS = " << cus << ";     // compute units of the device the code is for\n";
     s << "constexpr int EPI = " << epi << ";            // epilogue: 0 none, 1 SwiGLU of gate rows [0, N/2) and up rows [N/2, N)\n";
     s << "constexpr long NOUT = " << (epi ? N / 2 : N) << ";         // columns of Y\n";
-    s << "constexpr int OUT_SEL = " << dtype << ";        // storage type of Y: 0 f32, 1 bf16\n\n";
+    s << "constexpr int OUT_SEL = " << dtype << ";        // storage type of Y: 0 f32, 1 bf16\n";
+    s << "constexpr float NORM_EPS = " << eps_lit << "f;   // RMSNorm epsilon of the fused prologue ("
+      << ((fusion & 2) ? "" : "unused: ") << norm_eps << ")\n\n";
     s << kDeviceCommonSrc << "\n";
     s << kKernelsHeadSrc << "\n";
     s << kGemvSrc << "\n";
@@ -190,7 +211,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
     bool reduce_emitted[5] = {false, false, false, false, false};
     for (const Candidate& c : cands) {
         const char* sig = "(const u16* __restrict__ X, const u16* __restrict__ W, void* __restrict__ Y, "
-                          "float* __restrict__ ws, int M)";
+                          "float* __restrict__ ws, const float* __restrict__ gamma, int M)";
         switch (c.fam) {
         case Family::GemvValu: {
             const int64_t chs = K / 8 / c.S;
@@ -200,7 +221,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
             s << "static_assert(K_BLOCKS16 / " << c.S << " / 64 == " << chs / 64 << ", \"trip count\");\n";
             s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_valu<"
               << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out << ", "
-              << c.P << ">(X, W, Y, M); }\n";
+              << c.P << ", " << c.PRO << ">(X, W, Y, gamma, M); }\n";
             break;
         }
         case Family::GemvMfma: {

@@ -70,6 +70,40 @@ __device__ __forceinline__ float swiglu(float g, float u)
     return s * u;
 }
 
+// RMSNorm of one bf16 row x[0..K) by a whole block of 256 threads ("#004 the
+// same compiler on Apple's chips", section "Decode": the norm folded into the
+// projection that follows it, with the same bits as the separate kernels).
+// The sum of squares has one fixed order: thread t adds x[k]^2 for k = t,
+// t + 256, ... ascending with f32 FMA, then the 256 partials are added by
+// pairwise halving in LDS; every kernel that normalises a row calls this, so
+// they all get the same scale r = 1 / sqrt(ss / K + eps) (IEEE division and
+// square root).  red: 256 floats of LDS; all threads receive r.
+__device__ __forceinline__ float rms_scale_block(const u16* __restrict__ x, long K, float eps, float* red)
+{
+    const int t = threadIdx.x;
+    float ss = 0.f;
+    for (long k = t; k < K; k += 256) {
+        const float v = __builtin_bit_cast(float, (u32)x[k] << 16);
+        ss = __builtin_fmaf(v, v, ss);
+    }
+    red[t] = ss;
+    __syncthreads();
+#pragma unroll
+    for (int h = 128; h > 0; h >>= 1) {
+        if (t < h) red[t] = red[t] + red[t + h];
+        __syncthreads();
+    }
+    const float r = 1.0f / __builtin_sqrtf(red[0] / (float)K + eps);
+    __syncthreads();   // red may be reused after every thread has read red[0]
+    return r;
+}
+
+// One normalised element: bf16((x * r) * gamma), the products in f32, one rounding.
+__device__ __forceinline__ u16 rms_apply(u16 x, float r, float gamma)
+{
+    return to_bf16((__builtin_bit_cast(float, (u32)x << 16) * r) * gamma);
+}
+
 template <int OUT>
 __device__ __forceinline__ void store1(void* Y, long idx, float v)
 {

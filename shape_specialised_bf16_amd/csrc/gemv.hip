@@ -21,13 +21,22 @@
 // and their up rows NOUT + j..; after the reduction the up sum of a gate value
 // sits 32 lanes above it, and the wave stores silu(gate) * up in column j.
 //
+// With the RMSNorm prologue (PRO == 1, M = 1 only) the block first
+// normalises the X row into LDS with the same dev::rms_scale_block and
+// dev::rms_apply as the separate norm kernel (gamma f32 [K], epsilon NORM_EPS),
+// then reads X from there: the norm folded into the projection that follows
+// it ("#004 the same compiler on Apple's chips", section "Decode").  Each
+// block re-reads the K-element row, the extra traffic the pages name as the
+// reason the fused norm loses on larger models.
+//
 // Block: 256 threads = 4 waves = (4/S) row groups x S K-slices.
 // Grid:  N / (R * 4/S) blocks.
 // ---------------------------------------------------------------------------
-template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0>
+template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0, int PRO = 0>
 __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* __restrict__ W,
-                                          void* __restrict__ Y, int M)
+                                          void* __restrict__ Y, const float* __restrict__ gamma, int M)
 {
+    static_assert(PRO == 0 || MMAX == 1, "the fused norm prologue serves M = 1");
     static_assert(4 % S == 0, "S divides the 4 waves of a block");
     constexpr long CH = K / 8;                  // 16-byte chunks per row
     static_assert(K % 8 == 0 && CH % S == 0, "K slice must be whole chunks");
@@ -50,7 +59,28 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
     const long n0 = ((long)blockIdx.x * RG + rg) * (EPI ? R / 2 : R);   // first weight row = first output column
 
     const u32x4* __restrict__ Wp = reinterpret_cast<const u32x4*>(W) + n0 * CH + s * CHS + lane;
-    const u32x4* __restrict__ Xp = reinterpret_cast<const u32x4*>(X) + s * CHS + lane;
+    const u32x4* __restrict__ Xg = reinterpret_cast<const u32x4*>(X) + s * CHS + lane;
+    __shared__ u32x4 xs[PRO ? CH : 1];         // the normalised X row
+    __shared__ float red[PRO ? 256 : 1];
+    if constexpr (PRO) {
+        const float r = dev::rms_scale_block(X, K, NORM_EPS, red);
+        for (long c = threadIdx.x; c < CH; c += 256) {
+            const u32x4 xv = reinterpret_cast<const u32x4*>(X)[c];
+            const f32x4 g0 = reinterpret_cast<const f32x4*>(gamma)[2 * c];
+            const f32x4 g1 = reinterpret_cast<const f32x4*>(gamma)[2 * c + 1];
+            auto pair = [&](u32 v, float ga, float gb) -> u32 {
+                return (u32)dev::rms_apply((u16)(v & 0xFFFFu), r, ga) | ((u32)dev::rms_apply((u16)(v >> 16), r, gb) << 16);
+            };
+            xs[c] = u32x4{pair(xv.x, g0.x, g0.y), pair(xv.y, g0.z, g0.w), pair(xv.z, g1.x, g1.y),
+                          pair(xv.w, g1.z, g1.w)};
+        }
+        __syncthreads();
+    }
+    // X chunk i of this lane's slice (the normalised row in LDS with PRO)
+    auto Xp = [&](long i) -> u32x4 {
+        if constexpr (PRO) return xs[s * CHS + lane + i];
+        else return Xg[i];
+    };
 
     float acc[V];
 #pragma unroll
@@ -65,7 +95,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
             for (int u = 0; u < U; ++u) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) w[slot][u][r] = dev::load16<NT>(Wp + rowoff(r) * CH + (t0 + u) * 64);
-                xv[slot][u] = Xp[(t0 + u) * 64];
+                xv[slot][u] = Xp((t0 + u) * 64);
             }
         };
         auto dot = [&](int slot) {
@@ -96,7 +126,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
 #pragma unroll
             for (int m = 0; m < MMAX; ++m) {
                 if (m < M) {
-                    const u32x4 x = Xp[m * CH + (t0 + u) * 64];
+                    const u32x4 x = Xp(m * CH + (t0 + u) * 64);
 #pragma unroll
                     for (int r = 0; r < R; ++r)
                         acc[r * MMAX + m] = dev::dot8(w[u][r], x, acc[r * MMAX + m]);
@@ -112,7 +142,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
 #pragma unroll
             for (int m = 0; m < MMAX; ++m) {
                 if (m < M) {
-                    const u32x4 x = Xp[m * CH + TRIPS * 64];
+                    const u32x4 x = Xp(m * CH + TRIPS * 64);
 #pragma unroll
                     for (int r = 0; r < R; ++r)
                         acc[r * MMAX + m] = dev::dot8(w[r], x, acc[r * MMAX + m]);

@@ -153,7 +153,7 @@ static LaunchGeom geom(const Candidate& c, int64_t N, int64_t NO, int64_t M)
 
 // Enqueue candidate c for one block of M <= c.max_m rows.
 int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y,
-                     int64_t M, hipStream_t stream)
+                     int64_t M, hipStream_t stream, const float* gamma)
 {
     if (M > c.max_m) return set_error(PROJ_EINVAL, "M=%lld exceeds %s's limit of %lld rows",
                                       (long long)M, c.name.c_str(), (long long)c.max_m);
@@ -165,8 +165,19 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
     const void* w = W;
     void* y = Y;
     float* ws = (float*)p->ws;
+    const float* gam = gamma;
     int m = (int)M;
-    void* args[] = {&x, &w, &y, &ws, &m};
+    if (p->pro && !c.PRO) {
+        // unfused: the norm kernel writes the normalised rows into the workspace
+        const void* xin = X;
+        void* xo = p->xn;
+        long kk = (long)p->K;
+        float eps = p->eps;
+        void* nargs[] = {&xin, &gam, &xo, &kk, &eps};
+        HIP_TRY(hipModuleLaunchKernel(p->f_norm, (unsigned)M, 1, 1, 256, 1, 1, 0, stream, nargs, nullptr));
+        x = p->xn;
+    }
+    void* args[] = {&x, &w, &y, &ws, &gam, &m};
     HIP_TRY(hipModuleLaunchKernel(c.fn, g.gx, g.gy, 1, g.threads, 1, 1, 0, stream, args, nullptr));
     if (c.needs_ws()) {
         int64_t total4 = M * p->N / 4;              // split-K: every output
@@ -206,6 +217,8 @@ struct Tuner {
     hipFunction_t f_fill_probe = nullptr, f_fill_u32 = nullptr, f_ref = nullptr, f_ref_epi = nullptr,
                   f_check = nullptr, f_probe = nullptr;
     void *Xr = nullptr, *Xi = nullptr, *Wr = nullptr, *Wi = nullptr, *Y = nullptr;
+    float* gamma = nullptr;            // RMSNorm prologue: the probe's norm weights (K floats)
+    void *Xnr = nullptr, *Xni = nullptr; // and the normalised probe rows the reference reads
     float *ref_r = nullptr, *ref_i = nullptr;
     int* rows_d = nullptr;
     CheckStats* stats_d = nullptr;
@@ -217,7 +230,8 @@ struct Tuner {
 
     ~Tuner()
     {
-        for (void* q : {Xr, Xi, Wr, Wi, Y, (void*)ref_r, (void*)ref_i, (void*)rows_d, (void*)stats_d, flush})
+        for (void* q : {Xr, Xi, Wr, Wi, Y, (void*)ref_r, (void*)ref_i, (void*)rows_d, (void*)stats_d, flush,
+                        (void*)gamma, Xnr, Xni})
             if (q) (void)hipFree(q);
         if (e0) (void)hipEventDestroy(e0);
         if (e1) (void)hipEventDestroy(e1);
@@ -283,6 +297,55 @@ struct Tuner {
         if ((rc = fill_probe(Wr, p->N * p->K, 2, 0, 0.0625f))) return rc;
         if ((rc = fill_probe(Xi, mmax * p->K, 3, 1, 1.0f))) return rc;
         if ((rc = fill_probe(Wi, p->N * p->K, 4, 1, 1.0f))) return rc;
+        if (p->pro) {
+            // norm weights uniform in [0.5, 1.5): fill K bf16 values in [-0.5, 0.5),
+            // widen on the host, add 1
+            std::vector<uint16_t> hb(p->K);
+            void* tmp = nullptr;
+            if (hipMalloc(&gamma, p->K * 4) != hipSuccess || hipMalloc(&tmp, p->K * 2) != hipSuccess ||
+                hipMalloc(&Xnr, xb) != hipSuccess || hipMalloc(&Xni, xb) != hipSuccess) {
+                if (tmp) (void)hipFree(tmp);
+                return set_error(PROJ_ENOMEM, "tuner norm buffers could not be allocated");
+            }
+            if ((rc = fill_probe(tmp, p->K, 5, 0, 0.5f))) { (void)hipFree(tmp); return rc; }
+            HIP_TRY(hipStreamSynchronize(st));
+            hipError_t e = hipMemcpy(hb.data(), tmp, p->K * 2, hipMemcpyDeviceToHost);
+            (void)hipFree(tmp);
+            HIP_TRY(e);
+            std::vector<float> hg(p->K);
+            for (int64_t k = 0; k < p->K; ++k) hg[k] = 1.0f + bf16_to_f(hb[k]);
+            HIP_TRY(hipMemcpy(gamma, hg.data(), p->K * 4, hipMemcpyHostToDevice));
+        }
+        HIP_TRY(hipStreamSynchronize(st));
+        return PROJ_OK;
+    }
+
+    // With the RMSNorm prologue: the reference reads the probe rows normalised
+    // by the separate norm kernel (recomputed per bucket, after the reference
+    // kernel's self-check on the raw integer rows).
+    int reference_norm(const std::vector<int>& rows)
+    {
+        if (!p->pro) return PROJ_OK;
+        for (int pass = 0; pass < 2; ++pass) {
+            const void* xin = pass ? Xi : Xr;
+            const float* g = gamma;
+            void* xo = pass ? Xni : Xnr;
+            long kk = (long)p->K;
+            float eps = p->eps;
+            void* nargs[] = {&xin, &g, &xo, &kk, &eps};
+            HIP_TRY(hipModuleLaunchKernel(p->f_norm, (unsigned)mmax, 1, 1, 256, 1, 1, 0, st, nargs, nullptr));
+        }
+        HIP_TRY(hipMemcpyAsync(rows_d, rows.data(), rows.size() * 4, hipMemcpyHostToDevice, st));
+        int nr = (int)rows.size();
+        unsigned gx = (unsigned)((p->N + 255) / 256);
+        for (int pass = 0; pass < 2; ++pass) {
+            const void* x = pass ? Xni : Xnr;
+            const void* w = pass ? Wi : Wr;
+            float* r = pass ? ref_i : ref_r;
+            int* rd = rows_d;
+            void* args[] = {&x, &w, &rd, &nr, &r};
+            HIP_TRY(hipModuleLaunchKernel(f_ref, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
+        }
         HIP_TRY(hipStreamSynchronize(st));
         return PROJ_OK;
     }
@@ -352,13 +415,15 @@ struct Tuner {
         int rc;
         if ((rc = fill_sentinel(M + kGuardRows))) return rc;
         HIP_TRY(hipMemsetAsync(stats_d, 0, sizeof(CheckStats), st));
-        if ((rc = launch_candidate(p, c, integer ? Xi : Xr, integer ? Wi : Wr, Y, M, st))) return rc;
+        if ((rc = launch_candidate(p, c, integer ? Xi : Xr, integer ? Wi : Wr, Y, M, st, gamma))) return rc;
         const void* yp = Y;
         long ra = (long)(M + kGuardRows);
         int m = (int)M;
         const float* r = integer ? ref_i : ref_r;
         const int* rd = rows_d;
-        int ex = integer ? 1 : 0;
+        // normalised rows are not integers: with the norm prologue the integer
+        // probe is held to the tolerance, not to bit equality
+        int ex = (integer && !p->pro) ? 1 : 0;
         CheckStats* sd = stats_d;
         void* args[] = {&yp, &ra, &m, &r, &rd, &nrows, &ex, &sd};
         HIP_TRY(hipModuleLaunchKernel(f_check, 1024, 1, 1, 256, 1, 1, 0, st, args, nullptr));
@@ -385,12 +450,12 @@ struct Tuner {
     {
         int rc;
         for (int i = 0; i < 2; ++i)
-            if ((rc = launch_candidate(p, c, Xr, Wr, Y, M, st))) return rc;
+            if ((rc = launch_candidate(p, c, Xr, Wr, Y, M, st, gamma))) return rc;
         std::vector<double> t;
         for (int i = 0; i < reps; ++i) {
             if ((rc = flush_cache())) return rc;
             HIP_TRY(hipEventRecord(e0, st));
-            if ((rc = launch_candidate(p, c, (i & 1) ? Xi : Xr, (i & 1) ? Wi : Wr, Y, M, st))) return rc;
+            if ((rc = launch_candidate(p, c, (i & 1) ? Xi : Xr, (i & 1) ? Wi : Wr, Y, M, st, gamma))) return rc;
             HIP_TRY(hipEventRecord(e1, st));
             HIP_TRY(hipEventSynchronize(e1));
             float ms = 0;
@@ -557,6 +622,7 @@ int tune_plan(proj_plan* p)
             ref_checked = true;
         }
         const int nrows = (int)rows.size();
+        if ((rc = T.reference_norm(rows))) return rc;
         if ((rc = T.reference_epilogue(nrows))) return rc;
 
         std::vector<int> ok;
@@ -663,16 +729,19 @@ int tune_plan(proj_plan* p)
     return PROJ_OK;
 }
 
-int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out)
+int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, proj_plan** out)
 {
+    const int epi = fusion & PROJ_EPI_SWIGLU;
     *out = nullptr;
     if (N < 1 || K < 8 || K % 8 != 0 || N > (int64_t)1 << 30 || K > (int64_t)1 << 24)
         return set_error(PROJ_EINVAL, "invalid shape N=%lld K=%lld (need N >= 1, K >= 8, K %% 8 == 0)",
                          (long long)N, (long long)K);
     if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16)
         return set_error(PROJ_EINVAL, "invalid dtype %d (PROJ_OUT_F32=0 or PROJ_OUT_BF16=1)", dtype);
-    if (epi != PROJ_EPI_NONE && epi != PROJ_EPI_SWIGLU)
-        return set_error(PROJ_EINVAL, "invalid epilogue %d (PROJ_EPI_NONE=0 or PROJ_EPI_SWIGLU=1)", epi);
+    if (fusion & ~(PROJ_EPI_SWIGLU | PROJ_PRO_RMSNORM))
+        return set_error(PROJ_EINVAL, "invalid fusion flags %d (PROJ_EPI_SWIGLU=1 | PROJ_PRO_RMSNORM=2)", fusion);
+    if ((fusion & PROJ_PRO_RMSNORM) && !(norm_eps >= 0.f && norm_eps < 1e30f))
+        return set_error(PROJ_EINVAL, "invalid RMSNorm epsilon %g", (double)norm_eps);
     if (epi == PROJ_EPI_SWIGLU && N % 2)
         return set_error(PROJ_EINVAL, "the SwiGLU epilogue needs an even N (gate and up halves), got N=%lld",
                          (long long)N);
@@ -681,6 +750,8 @@ int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out)
     p->K = K;
     p->dtype = dtype;
     p->epi = epi;
+    p->pro = (fusion & PROJ_PRO_RMSNORM) ? 1 : 0;
+    p->eps = p->pro ? norm_eps : 0.f;
     p->NO = epi == PROJ_EPI_SWIGLU ? N / 2 : N;
     HIP_TRY(hipGetDevice(&p->device));
     int rc;
@@ -688,14 +759,14 @@ int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out)
     if ((rc = device_arch(p->device, &p->arch, &cus))) return rc;
     for (int b = 0; b < kNumBuckets; ++b) p->choice[b] = -1, p->choice_us[b] = -1;
 
-    p->cands = enumerate_candidates(N, K, cus, epi);
-    const std::string src = emit_source(N, K, dtype, p->arch, cus, p->cands, epi);
+    p->cands = enumerate_candidates(N, K, cus, fusion);
+    const std::string src = emit_source(N, K, dtype, p->arch, cus, p->cands, fusion, p->eps);
     if ((rc = cache_key(p.get(), src))) return rc;
     const double t0 = now_s();
     std::shared_ptr<std::vector<char>> code;
     char name[96];
-    snprintf(name, sizeof name, "proj_%lldx%lld_%s%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32",
-             epi ? "_swiglu" : "");
+    snprintf(name, sizeof name, "proj_%lldx%lld_%s%s%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32",
+             epi ? "_swiglu" : "", p->pro ? "_rmsnorm" : "");
     if ((rc = compile_source(src, p->arch, name, &code))) return rc;
     p->compile_s = now_s() - t0;
     p->code_bytes = code->size();
@@ -707,6 +778,14 @@ int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out)
         }
     }
     HIP_TRY(hipModuleLoadData(&p->module, code->data()));
+    if (p->pro) {
+        HIP_TRY(hipModuleGetFunction(&p->f_norm, p->module, "proj_rmsnorm_rows"));
+        if (hipMalloc(&p->xn, (size_t)kMaxBlockRows * K * 2) != hipSuccess) {
+            p->xn = nullptr;
+            (void)hipModuleUnload(p->module);
+            return set_error(PROJ_ENOMEM, "RMSNorm workspace of %lld bytes", (long long)kMaxBlockRows * K * 2);
+        }
+    }
     for (Candidate& c : p->cands) {
         HIP_TRY(hipModuleGetFunction(&c.fn, p->module, c.name.c_str()));
         if (!c.reduce_name.empty()) HIP_TRY(hipModuleGetFunction(&c.reduce_fn, p->module, c.reduce_name.c_str()));
@@ -718,6 +797,7 @@ int create_plan(int64_t N, int64_t K, int dtype, int epi, proj_plan** out)
     plog(p.get(), line);
     if ((rc = tune_plan(p.get()))) {
         if (p->ws) (void)hipFree(p->ws);
+        if (p->xn) (void)hipFree(p->xn);
         if (p->module) (void)hipModuleUnload(p->module);
         return rc;
     }
@@ -735,6 +815,7 @@ void destroy_plan(proj_plan* p)
     (void)hipGetDevice(&cur);
     if (cur != p->device) (void)hipSetDevice(p->device);
     if (p->ws) (void)hipFree(p->ws);
+    if (p->xn) (void)hipFree(p->xn);
     if (p->module) (void)hipModuleUnload(p->module);
     if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
     delete p;
@@ -755,16 +836,19 @@ int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, in
     return PROJ_OK;
 }
 
-int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream)
+int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream,
+             const float* gamma)
 {
     int rc = check_run_args(p, X, W, Y, M);
     if (rc || M == 0) return rc;
+    if (p->pro && !gamma) return set_error(PROJ_EINVAL, "this plan has the RMSNorm prologue: gamma is required");
+    if (p->pro && ((uintptr_t)gamma & 15)) return set_error(PROJ_EINVAL, "gamma must be 16-byte aligned");
     const size_t ysz = p->dtype == PROJ_OUT_BF16 ? 2 : 4;
     for (int64_t off = 0; off < M; off += kMaxBlockRows) {
         const int64_t m = std::min<int64_t>(kMaxBlockRows, M - off);
         const Candidate& c = p->cands[p->choice[bucket_of(m)]];
         rc = launch_candidate(p, c, (const char*)X + (size_t)off * p->K * 2, W, (char*)Y + (size_t)off * p->NO * ysz,
-                              m, stream);
+                              m, stream, gamma);
         if (rc) return rc;
     }
     return PROJ_OK;

@@ -27,6 +27,7 @@ struct Candidate {
     // GEMV parameters
     int R = 1, S = 1, MMAX = 1, U = 1, NT = 1;
     int P = 0;       // 1: software-pipelined batches of U trips (vector GEMV, M = 1)
+    int PRO = 0;     // 1: RMSNorm folded into the kernel (vector GEMV, M = 1)
     // GEMM parameters: block tile, k-tile, LDS buffers, wave grid, split-K,
     // tile-row group, LDS swizzle period
     int BM = 0, BN = 0, BK = 64, ST = 2, WM = 0, WN = 0, SK = 1, GM = 8, SWZ = 0;
@@ -75,13 +76,14 @@ struct Candidate {
 // Enumerate the candidates that tile (N, K) exactly.  Always ends with the
 // plain kernel, which fits any shape.
 // `cus` is the device's compute-unit count (it sets the tail split's round size).
-// epi: 0 plain projection, 1 fused SwiGLU epilogue (only the families that have it)
-std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int epi = 0);
+// fusion: bit 0 the SwiGLU epilogue (only the families that have it), bit 1 the
+// RMSNorm prologue (every candidate unfused, plus the M = 1 GEMVs with it folded in)
+std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int fusion = 0);
 
 // The full translation unit for (N, K, dtype): prelude with the shape as
 // literals, device helpers, kernel templates, one wrapper per candidate.
 std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
-                        const std::vector<Candidate>& cands, int epi = 0);
+                        const std::vector<Candidate>& cands, int fusion = 0, float norm_eps = 0.f);
 
 // Compute units assumed when no device is queried (MI355X).
 constexpr int kDefaultCUs = 256;
@@ -106,6 +108,10 @@ struct proj_plan {
     int64_t N = 0, K = 0;
     int dtype = 0;
     int epi = 0;        // PROJ_EPI_NONE or PROJ_EPI_SWIGLU
+    int pro = 0;        // 1: RMSNorm prologue (proj_run_ex needs gamma)
+    float eps = 0.f;    // its epsilon
+    void* xn = nullptr; // workspace: normalised X rows for the unfused candidates (kMaxBlockRows x K bf16)
+    hipFunction_t f_norm = nullptr;  // the module's separate norm kernel (proj_rmsnorm_rows)
     uint64_t key = 0;   // tuning-cache key: device, runtime and driver versions, emitted source
     std::string cache;  // tuning cache: "off", "miss", "hit", "stale" (a cached choice failed the gate)
     std::string cache_path;

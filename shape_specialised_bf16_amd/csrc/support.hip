@@ -72,3 +72,18 @@ extern "C" __global__ __launch_bounds__(256) void proj_swiglu_bf16(const void* G
 {
     swiglu_rows<OUT_BF16>(G, H, M, N);
 }
+
+// The RMSNorm as a kernel of its own -- the unfused path that the fused
+// prologue must reproduce bit for bit: one block of 256 threads per row of
+// X [M, K] (bf16), Xn[m][k] = bf16((X[m][k] * r_m) * gamma[k]) with gamma f32
+// [K] and r_m from dev::rms_scale_block.  Grid: M blocks.
+extern "C" __global__ __launch_bounds__(256) void proj_rmsnorm_rows(const u16* __restrict__ X,
+                                                                    const float* __restrict__ gamma,
+                                                                    u16* __restrict__ Xn, long K, float eps)
+{
+    __shared__ float red[256];
+    const u16* x = X + (long)blockIdx.x * K;
+    const float r = dev::rms_scale_block(x, K, eps, red);
+    u16* xn = Xn + (long)blockIdx.x * K;
+    for (long k = threadIdx.x; k < K; k += 256) xn[k] = dev::rms_apply(x[k], r, gamma[k]);
+}

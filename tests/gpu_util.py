@@ -16,13 +16,14 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def plan(N: int, K: int, dtype: str = "f32", epilogue=None):
+def plan(N: int, K: int, dtype: str = "f32", epilogue=None, rmsnorm_eps=None):
     from shape_specialised_bf16_amd import Plan
 
-    key = (N, K, dtype, epilogue)
+    key = (N, K, dtype, epilogue, rmsnorm_eps)
     if key not in _plans:
-        log(f"[plan] creating {N}x{K} {dtype}" + (f" epilogue {epilogue}" if epilogue else ""))
-        _plans[key] = Plan(N, K, dtype, epilogue=epilogue)
+        log(f"[plan] creating {N}x{K} {dtype}" + (f" epilogue {epilogue}" if epilogue else "")
+            + (f" rmsnorm eps {rmsnorm_eps}" if rmsnorm_eps is not None else ""))
+        _plans[key] = Plan(N, K, dtype, epilogue=epilogue, rmsnorm_eps=rmsnorm_eps)
     return _plans[key]
 
 

@@ -57,7 +57,8 @@ def test_trip_counts_and_block_strides_are_literals(row):
 
 
 def test_no_runtime_shape_arguments():
-    """Every candidate wrapper takes only pointers and M: no run-time N or K."""
+    """Every candidate wrapper takes only pointers and M: no run-time N or K
+    (gamma, the norm weights of a plan with the RMSNorm prologue, is a pointer)."""
     src = ssb.emit_source(5120, 2560, "bf16")
     sigs = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void (gemv_\w+|gemm_\w+)(\([^)]*\))', src)
     assert len(sigs) >= 10
@@ -66,7 +67,7 @@ def test_no_runtime_shape_arguments():
             assert sig == "(const float* __restrict__ ws, void* __restrict__ Y, int M)", name
             continue
         assert sig == ("(const u16* __restrict__ X, const u16* __restrict__ W, void* __restrict__ Y, "
-                       "float* __restrict__ ws, int M)"), name
+                       "float* __restrict__ ws, const float* __restrict__ gamma, int M)"), name
 
 
 @pytest.mark.parametrize("N,K", [(2048, 1024), (151936, 1024), (5120, 2560), (2560, 9216),
@@ -141,6 +142,32 @@ def test_swiglu_odd_n_rejected():
 def test_swiglu_source_compiles_for_gfx950(tmp_path):
     src = ssb.emit_source(1000, 520, "bf16", epilogue="swiglu")
     f = tmp_path / "proj_1000x520_swiglu.hip"
+    f.write_text(src)
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-device-only", "-c", "-O3",
+                        "-std=c++17", "-include", "hip/hip_runtime.h", str(f), "-o", str(f) + ".o"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+
+
+def test_rmsnorm_module_has_folded_and_unfused_candidates():
+    """With the RMSNorm prologue the epsilon is a literal of the module, every
+    ordinary candidate is kept (it runs after the separate norm kernel) and
+    each M = 1 vector GEMV comes a second time with the norm folded in."""
+    src = ssb.emit_source(2048, 1024, "f32", rmsnorm_eps=1e-6)
+    assert "constexpr float NORM_EPS = 0x1.0c6f7ap-20f;" in src        # 1e-6 as an f32, exactly
+    names = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\(', src)
+    plain = set(re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\(',
+                           ssb.emit_source(2048, 1024, "f32")))
+    assert plain <= set(names)
+    folded = [n for n in names if n.endswith("_nf")]
+    assert folded and all(n.startswith("gemv_valu") and "_m1_" in n for n in folded)
+    assert {n[:-3] for n in folded} == {n for n in plain if n.startswith("gemv_valu") and "_m1_" in n}
+    assert "gemv_valu<" in src and ", 1>(X, W, Y, gamma, M)" in src
+
+
+def test_rmsnorm_and_swiglu_module_compiles(tmp_path):
+    src = ssb.emit_source(1000, 520, "bf16", epilogue="swiglu", rmsnorm_eps=1e-5)
+    f = tmp_path / "proj_1000x520_both.hip"
     f.write_text(src)
     r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-device-only", "-c", "-O3",
                         "-std=c++17", "-include", "hip/hip_runtime.h", str(f), "-o", str(f) + ".o"],

@@ -23,6 +23,8 @@ Reported (one JSON line on stdout):
              the 2.5 PFLOP/s dense bf16 MFMA peak, with its dominant kernel
   swiglu_epilogue  the gate/up projection with the fused SwiGLU epilogue
              against the plain plan + the separate activation kernel
+  rmsnorm_prologue  decode projections with the RMSNorm folded in (as the
+             tuner chose) against the separate norm kernel + plain plan
   long_prompt, layer_27b  the caller-side prompt-block driver (8192 rows in
              blocks of 1024, then the head) and the 27B-like layer
   cpu_baseline  the fp64 CPU oracle on the same decode step, all host cores
@@ -482,6 +484,86 @@ def time_swiglu(steps: int = 1000, reps: int = 20):
     return out
 
 
+def time_rmsnorm(steps: int = 1000):
+    """The RMSNorm prologue folded into a decode projection (M = 1) against the
+    separate path (proj_rmsnorm, then the plain plan), with rotating weight
+    copies; the tuner's own timings of its best folded and best unfused
+    candidates are reported beside the choice it made."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import tolerance
+    import shape_specialised_bf16_amd as ssb
+    import synth
+
+    eps = 1e-6
+    stream = torch.cuda.current_stream()
+    sh = __import__("ctypes").c_void_p(stream.cuda_stream)
+    out = {}
+    for key, cfg_no, pname, dt in (("decode_qkv_08b_m1", 1, "qkv", "f32"), ("decode_head_08b_m1", 1, "head", "f32"),
+                                   ("decode_qkv_27b_m1", 4, "qkv", "bf16")):
+        cfg = synth.CONFIGS[cfg_no]
+        pi = [p.name for p in cfg.projections].index(pname)
+        p = cfg.projections[pi]
+        normp = ssb.Plan(p.N, p.K, dt, rmsnorm_eps=eps)
+        plain = ssb.Plan(p.N, p.K, dt)
+        Wh, Xh = synth.weights(cfg, pi), synth.activations(cfg, pi, 1)
+        gh = (1.0 + 0.25 * np.random.default_rng(cfg_no * 10 + pi).standard_normal(p.K)).astype(np.float32)
+        W, X, g = upload(Wh), upload(Xh), torch.from_numpy(gh).cuda()
+        copies = max(1, -(-ROTATE_BYTES // (W.numel() * 2)))
+        Wrot = [W] + [W.clone() for _ in range(copies - 1)]
+        odt = torch.bfloat16 if dt == "bf16" else torch.float32
+        Y = torch.empty((1, p.N), dtype=odt, device="cuda")
+        Y2 = torch.empty((1, p.N), dtype=odt, device="cuda")
+        Xn = torch.empty_like(X)
+        xp, gp, xnp, yp, y2p = X.data_ptr(), g.data_ptr(), Xn.data_ptr(), Y.data_ptr(), Y2.data_ptr()
+        wps = [w.data_ptr() for w in Wrot]
+        norm_c = ssb._lib.proj_rmsnorm
+
+        def separate(s):
+            norm_c(xp, gp, xnp, 1, p.K, eps, sh)
+            plain.run_ptr(xnp, wps[s % copies], y2p, 1, sh)
+
+        def tuned(s):
+            normp.run_ptr(xp, wps[s % copies], yp, 1, sh, gp)
+
+        res = {}
+        n = steps if p.N * p.K < (1 << 26) else steps // 10
+        for name, fn in (("separate", separate), ("tuned", tuned)):
+            for s in range(20):
+                fn(s)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s in range(n):
+                fn(s)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / n * 1e3
+        ref = oracle.rmsnorm_matmul(Xh, gh, Wh, eps)
+        terms = oracle.rmsnorm_matmul(Xh, gh, Wh, eps, absolute=True)
+        got = Y.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16" else Y.cpu().numpy()
+        rep = tolerance.check_norm_projection(got, ref, terms, dt)
+        if not rep.ok:
+            raise SystemExit(f"bench: {key} with the norm prologue does not match the oracle: {rep}")
+        t = normp.describe()["buckets"][0]["timings_us"]
+        folded = {k: v for k, v in t.items() if k.endswith("_nf")}
+        unfused = {k: v for k, v in t.items() if not k.endswith("_nf")}
+        o = dict(shape=f"{p.N}x{p.K}", dtype=dt, tuned_us=round(res["tuned"], 3), separate_us=round(res["separate"], 3),
+                 choice=normp.choice(1), weight_copies_rotated=copies)
+        if folded and unfused:
+            bf, bu = min(folded, key=folded.get), min(unfused, key=unfused.get)
+            o["tuner_best_folded"] = {bf: round(folded[bf], 3)}
+            o["tuner_best_unfused"] = {bu: round(unfused[bu], 3)}
+        out[key] = o
+        log(f"  RMSNorm {key}: tuned {res['tuned']:.2f} us ({o['choice']}), separate {res['separate']:.2f} us")
+        normp.close()
+        plain.close()
+        del Wrot, W
+    return out
+
+
 def probe_bandwidth():
     import torch
     import shape_specialised_bf16_amd as ssb
@@ -615,6 +697,7 @@ def main():
                                          "2560->18432, down 9216->2560, Y bf16", **time_prefill()}
     if not args.no_extra:
         result["swiglu_epilogue"] = time_swiglu()
+        result["rmsnorm_prologue"] = time_rmsnorm()
         result["long_prompt"] = time_long_prompt()
         torch.cuda.empty_cache()
         result["layer_27b"] = time_27b()

@@ -120,11 +120,11 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int f
     //      split along K so the last round is not mostly idle).
     struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[2]; };
     const GT gts[] = {
-        {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 0}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2, 0}},
-        {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {0, 0}},
+        {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2}},
+        {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},
-        {128, 128, 64, 2, 2, 2, 1, 4, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {0, 0}},
-        {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {0, 0}}, {64, 128, 64, 2, 1, 2, 1, 4, 8, 1, {0, 0}}};
+        {128, 128, 64, 2, 2, 2, 1, 4, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
+        {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 4, 8, 1, {}}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
         const int cpr = g.BK / 8, rpi = 64 * g.WM * g.WN / cpr;

@@ -168,6 +168,33 @@ def rmsnorm_matmul(X: np.ndarray, gamma: np.ndarray, W: np.ndarray, eps: float, 
     return out
 
 
+PANEL_ROWS = 128
+PANEL_COLS = 64
+
+
+def pack_panels(W: np.ndarray) -> np.ndarray:
+    """W [N, K] (row-major) in the library's packed weight layout, as an array of
+    shape (N/128, K/64, 128, 64) whose C order is the packed memory order:
+    element [p, b, r, q] is W[128 p + r, 64 b + q] -- 128-row panels, each as
+    K/64 consecutive blocks of 128 rows x 64 values, each block row-major.
+    This layout is the library's own (declared with proj_pack_weights); the
+    pages behind it pack weights so that the kernel reads them in the order it
+    consumes them ("#001 un compilateur pour moteur de LLM", section "Lire le
+    meme emetteur rempli deux fois": 16-column blocks a fixed distance apart)
+    and leave the GPU benefit to be measured kernel by kernel ("#002 le meme
+    compilateur sur un GPU", section "Les autres cartes").  Written as one
+    block copy per (panel, block); values are moved, never changed."""
+    W = np.asarray(W)
+    N, K = W.shape
+    if N % PANEL_ROWS or K % PANEL_COLS:
+        raise ValueError(f"packed layout needs N % 128 == 0 and K % 64 == 0, got {N}x{K}")
+    out = np.empty((N // PANEL_ROWS, K // PANEL_COLS, PANEL_ROWS, PANEL_COLS), dtype=W.dtype)
+    for p in range(N // PANEL_ROWS):
+        for b in range(K // PANEL_COLS):
+            out[p, b] = W[p * PANEL_ROWS:(p + 1) * PANEL_ROWS, b * PANEL_COLS:(b + 1) * PANEL_COLS]
+    return out
+
+
 def round_f32(Y: np.ndarray) -> np.ndarray:
     """Round fp64 results once to f32 (IEEE RNE)."""
     Y = np.ascontiguousarray(Y, dtype=np.float64)

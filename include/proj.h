@@ -14,9 +14,11 @@
  * Conventions for every entry point below:
  *   - X, W, Y and every other buffer argument are DEVICE pointers on the
  *     plan's device unless stated otherwise; the caller owns them.
- *   - X [M,K], W [N,K], Y [M,N] are dense row-major.  X and W hold bf16 bit
- *     patterns; Y holds f32 (PROJ_OUT_F32) or bf16 (PROJ_OUT_BF16).  All three
- *     must be 16-byte aligned; Y must not overlap X or W.
+ *   - X [M,K], W [N,K], Y [M,N] are dense row-major, except W for a plan
+ *     created with PROJ_W_PACKED (the packed layout of proj_pack_weights).  X
+ *     and W hold bf16 bit patterns; Y holds f32 (PROJ_OUT_F32) or bf16
+ *     (PROJ_OUT_BF16).  All three must be 16-byte aligned; Y must not overlap
+ *     X or W.
  *   - Work is enqueued on `stream` (a HIP stream of the plan's device, or NULL
  *     for the null stream) and the call returns without synchronising and
  *     without allocating.
@@ -43,8 +45,9 @@ typedef struct proj_plan proj_plan; /* opaque; owned by the library */
 /* Storage type of Y.  X and W are always bf16. */
 enum { PROJ_OUT_F32 = 0, PROJ_OUT_BF16 = 1 };
 
-/* Work folded into a plan's kernels (flags of proj_plan_create_ex). */
-enum { PROJ_EPI_NONE = 0, PROJ_EPI_SWIGLU = 1, PROJ_PRO_RMSNORM = 2 };
+/* Flags of proj_plan_create_ex: work folded into a plan's kernels, and the
+ * layout its kernels read W in. */
+enum { PROJ_EPI_NONE = 0, PROJ_EPI_SWIGLU = 1, PROJ_PRO_RMSNORM = 2, PROJ_W_PACKED = 4 };
 
 enum {
     PROJ_OK = 0,
@@ -90,8 +93,9 @@ enum {
 proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
 
 /*
- * Like proj_plan_create, with work folded into the plan's kernels; `fusion` is
- * PROJ_EPI_NONE or an OR of the flags below.  The pages fold exactly these two
+ * Like proj_plan_create, with work folded into the plan's kernels or with
+ * weights in the packed layout; `flags` is PROJ_EPI_NONE or an OR of the flags
+ * below.  The pages fold exactly these two
  * ("#004 the same compiler on Apple's chips", section "Decode": the norms into
  * the projection that follows them, the SwiGLU into the gate_up projection),
  * each with the same bits as the kernels it replaces.
@@ -126,12 +130,21 @@ proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
  * small models and slower from the 4B on, where every workgroup re-reads the
  * whole row.  proj_run on such a plan fails with PROJ_EINVAL: use proj_run_ex.
  *
- * Unknown flags, an odd N with PROJ_EPI_SWIGLU, or a negative or non-finite
- * norm_eps with PROJ_PRO_RMSNORM return NULL with PROJ_EINVAL in
- * proj_last_error.  norm_eps is ignored without PROJ_PRO_RMSNORM;
- * proj_plan_create_ex(N, K, dtype, PROJ_EPI_NONE, 0) is proj_plan_create.
+ * PROJ_W_PACKED: every kernel of the plan reads W in the packed layout that
+ * proj_pack_weights writes (N % 128 == 0 and K % 64 == 0), and the plan runs
+ * through proj_run_packed (proj_run and proj_run_ex fail with PROJ_EINVAL).
+ * Each candidate reads the same values in the same order as on row-major
+ * weights, so a packed plan gives the same bits as a row-major plan running
+ * the same kernel variant; only the memory addresses change.  Combines with
+ * the two flags above.
+ *
+ * Unknown flags, an odd N with PROJ_EPI_SWIGLU, a negative or non-finite
+ * norm_eps with PROJ_PRO_RMSNORM, or a shape without whole 128 x 64 blocks with
+ * PROJ_W_PACKED return NULL with PROJ_EINVAL in proj_last_error.  norm_eps is
+ * ignored without PROJ_PRO_RMSNORM; proj_plan_create_ex(N, K, dtype,
+ * PROJ_EPI_NONE, 0) is proj_plan_create.
  */
-proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int fusion, float norm_eps);
+proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int flags, float norm_eps);
 
 /*
  * Enqueue Y[0:M, :] = X[0:M, :] . W^T on `stream`.  Rows of Y at or past M are
@@ -145,7 +158,8 @@ proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int fusion, floa
  * no allocation, no synchronisation, no memset, so the call may be recorded
  * into a HIP graph by stream capture.  Calls on one plan share its workspace:
  * they must not run concurrently (different streams without ordering, or
- * overlapping graph replays).
+ * overlapping graph replays).  A plan created with PROJ_W_PACKED gives
+ * PROJ_EINVAL here: it runs through proj_run_packed.
  */
 int proj_run(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M,
              hipStream_t stream);
@@ -155,6 +169,40 @@ int proj_run(const proj_plan* plan, const void* X, const void* W, void* Y, int64
  * plans without the prologue; missing or misaligned for one: PROJ_EINVAL). */
 int proj_run_ex(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, const float* gamma,
                 hipStream_t stream);
+
+/*
+ * Load-time weight repacking.  Enqueue the copy of the row-major weights W
+ * [N, K] (bf16 bit patterns) into Wp, the same N * K values in the packed
+ * layout: W is cut into panels of 128 consecutive rows, each panel is stored
+ * as K/64 consecutive blocks of 128 rows x 64 values, each block row-major, so
+ *     Wp[((n / 128) * (K / 64) + k / 64) * 8192 + (n % 128) * 64 + k % 64] = W[n][k].
+ * A 64-value slice of 128 rows -- what one k-step of an MFMA tile reads -- is
+ * then one contiguous 16 KiB block instead of 128 separate 128-byte pieces; a
+ * decode GEMV still reads each row in 128-byte runs.  The pages pack their
+ * weights in the order their kernels read them (16-column blocks at a fixed
+ * distance: "#001 un compilateur pour moteur de LLM", section "Lire le meme
+ * emetteur rempli deux fois"; aligned to cache lines: section "Les chiffres"),
+ * and expect the layout to pay on GPUs too, to be measured kernel by kernel
+ * ("#002 le meme compilateur sur un GPU", section "Les autres cartes").
+ *
+ * N % 128 == 0 and K % 64 == 0; W and Wp are caller-owned device buffers of
+ * N * K * 2 bytes, 16-byte aligned and not overlapping (no in-place packing).
+ * Independent of any plan: pack once at load, then run any PROJ_W_PACKED plan
+ * of that shape on Wp with proj_run_packed.  N == 0 or K == 0 is a no-op;
+ * other shapes, null, misaligned or overlapping buffers give PROJ_EINVAL.
+ */
+int proj_pack_weights(int64_t N, int64_t K, const void* W, void* Wp, hipStream_t stream);
+
+/*
+ * proj_run_ex for a plan created with PROJ_W_PACKED: Wp holds the weights in
+ * the packed layout (proj_pack_weights); gamma as in proj_run_ex (required for
+ * a PROJ_PRO_RMSNORM plan, NULL otherwise).  Same results, bit for bit, as a
+ * plan without PROJ_W_PACKED running the same kernel variant on the row-major
+ * W; same errors as proj_run_ex, and PROJ_EINVAL for a plan without
+ * PROJ_W_PACKED.
+ */
+int proj_run_packed(const proj_plan* plan, const void* X, const void* Wp, void* Y, int64_t M, const float* gamma,
+                    hipStream_t stream);
 
 /* Free the plan's module and workspace.  NULL-safe.  No launch of this plan may
  * still be pending on the device. */
@@ -177,8 +225,8 @@ const char* proj_last_error(void);
  */
 int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* buf, size_t cap,
                      size_t* needed);
-/* The same for a plan with fused work (proj_plan_create_ex's fusion flags and epsilon). */
-int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, const char* arch, char* buf,
+/* The same for a plan with fused work or packed weights (proj_plan_create_ex's flags and epsilon). */
+int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int flags, float norm_eps, const char* arch, char* buf,
                         size_t cap, size_t* needed);
 
 /* JSON text (host buffer) describing the plan: shape, candidates, per-bucket
@@ -197,7 +245,8 @@ int64_t proj_plan_candidate_max_m(const proj_plan* plan, int idx);
 
 /*
  * Like proj_run but with candidate `idx` instead of the tuned choice; M must
- * be within the candidate's limit (proj_plan_candidate_max_m).  The analogue of
+ * be within the candidate's limit (proj_plan_candidate_max_m); W is in the
+ * plan's layout (packed for a PROJ_W_PACKED plan).  The analogue of
  * the pages' command-line override of a tuned variant ("#004 the same compiler
  * on Apple's chips", section "Reproducing at home").
  */

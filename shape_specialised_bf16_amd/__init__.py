@@ -1,12 +1,16 @@
 """Python binding of libproj: shape-specialised bf16 projections Y = X . W^T on gfx950.
 
 Argument marshalling only.  Every step of the computation runs in the HIP
-kernels of ``libproj.so`` (built in-tree by ``shape_specialised_bf16_amd.build``);
+kernels of ``libproj.so`` (built in-tree by ``shape_specialised_bf16_amd/build.py``);
 torch supplies device memory and the current stream.  Importing this package
 without the built library raises ImportError: there is no fallback.
 
     plan = Plan(N, K, "f32")          # emit, compile (hipRTC), validate and tune
     Y = plan.run(X, W)                # X [M,K] bf16, W [N,K] bf16 -> Y [M,N] f32
+
+    Wp = pack_weights(W)              # once at load: the packed weight layout
+    pp = Plan(N, K, "f32", packed=True)
+    Y = pp.run_packed(X, Wp)          # same bits as plan.run(X, W) per kernel variant
 
 C entry points and their semantics: ``include/proj.h``.
 """
@@ -16,8 +20,8 @@ import ctypes
 import json
 import os
 
-__all__ = ["Plan", "ProjError", "emit_source", "probe_read", "round_bf16", "LIB_PATH",
-           "OUT_F32", "OUT_BF16", "EXPORTED_SYMBOLS"]
+__all__ = ["Plan", "ProjError", "emit_source", "probe_read", "round_bf16", "pack_weights", "swiglu", "rmsnorm",
+           "LIB_PATH", "OUT_F32", "OUT_BF16", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libproj.so")
@@ -27,6 +31,8 @@ OUT_BF16 = 1
 EPI_NONE = 0
 EPI_SWIGLU = 1
 PRO_RMSNORM = 2
+W_PACKED = 4
+PANEL_ROWS, PANEL_COLS = 128, 64   # blocks of the packed weight layout
 _ERRORS = {-1: "PROJ_EINVAL", -2: "PROJ_EDEVICE", -3: "PROJ_ECOMPILE", -4: "PROJ_ENOCAND", -5: "PROJ_ENOMEM"}
 
 # Every function declared in include/proj.h.
@@ -35,11 +41,11 @@ EXPORTED_SYMBOLS = (
     "proj_plan_describe", "proj_plan_num_candidates", "proj_plan_candidate_name",
     "proj_plan_candidate_max_m", "proj_run_candidate", "proj_plan_choice", "proj_probe_read",
     "proj_round_bf16", "proj_plan_create_ex", "proj_emit_source_ex", "proj_swiglu", "proj_run_ex",
-    "proj_run_candidate_ex", "proj_rmsnorm",
+    "proj_run_candidate_ex", "proj_rmsnorm", "proj_pack_weights", "proj_run_packed",
 )
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m shape_specialised_bf16_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python shape_specialised_bf16_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 # torch ships its own HIP runtime (SONAME libamdhip64.so.7, loaded by torch under
@@ -91,6 +97,10 @@ _lib.proj_probe_read.argtypes = [_p, _i64, ctypes.c_uint32, _p, _p]
 _lib.proj_probe_read.restype = ctypes.c_int
 _lib.proj_round_bf16.argtypes = [_p, _p, _i64, _p]
 _lib.proj_round_bf16.restype = ctypes.c_int
+_lib.proj_pack_weights.argtypes = [_i64, _i64, _p, _p, _p]
+_lib.proj_pack_weights.restype = ctypes.c_int
+_lib.proj_run_packed.argtypes = [_p, _p, _p, _p, _i64, _p, _p]
+_lib.proj_run_packed.restype = ctypes.c_int
 
 
 class ProjError(RuntimeError):
@@ -122,10 +132,11 @@ def _epi_code(epilogue) -> int:
     raise ValueError(f"unsupported epilogue {epilogue!r} (None or 'swiglu')")
 
 
-def emit_source(N: int, K: int, dtype: str = "f32", arch: str = "gfx950", epilogue=None, rmsnorm_eps=None) -> str:
-    """The HIP source a plan for (N, K, dtype[, epilogue, RMSNorm prologue])
-    compiles (no GPU needed)."""
-    fusion = _epi_code(epilogue) | (PRO_RMSNORM if rmsnorm_eps is not None else 0)
+def emit_source(N: int, K: int, dtype: str = "f32", arch: str = "gfx950", epilogue=None, rmsnorm_eps=None,
+                packed: bool = False) -> str:
+    """The HIP source a plan for (N, K, dtype[, epilogue, RMSNorm prologue,
+    packed weights]) compiles (no GPU needed)."""
+    fusion = _epi_code(epilogue) | (PRO_RMSNORM if rmsnorm_eps is not None else 0) | (W_PACKED if packed else 0)
     return _text(_lib.proj_emit_source_ex, N, K, _dtype_code(dtype), fusion,
                  float(rmsnorm_eps or 0.0), arch.encode())
 
@@ -168,18 +179,21 @@ class Plan:
 
     epilogue="swiglu": W is a gate_up matrix (gate rows then up rows) and the
     plan writes Y[M, N/2] = silu(gate) * up; rmsnorm_eps=<eps>: X is
-    RMS-normalised first with the gamma given to run (see proj_plan_create_ex)."""
+    RMS-normalised first with the gamma given to run; packed=True: the plan
+    reads weights in the packed layout of pack_weights and runs with
+    run_packed (see proj_plan_create_ex)."""
 
-    def __init__(self, N: int, K: int, dtype="f32", epilogue=None, rmsnorm_eps=None):
+    def __init__(self, N: int, K: int, dtype="f32", epilogue=None, rmsnorm_eps=None, packed: bool = False):
         self.N, self.K = int(N), int(K)
         self.dtype_code = _dtype_code(dtype)
         self.epi_code = _epi_code(epilogue)
         self.norm = rmsnorm_eps is not None
+        self.packed = bool(packed)
         self.NO = self.N // 2 if self.epi_code == EPI_SWIGLU else self.N
-        fusion = self.epi_code | (PRO_RMSNORM if self.norm else 0)
+        fusion = self.epi_code | (PRO_RMSNORM if self.norm else 0) | (W_PACKED if self.packed else 0)
         h = _lib.proj_plan_create_ex(self.N, self.K, self.dtype_code, fusion, float(rmsnorm_eps or 0.0))
         if not h:
-            raise ProjError(-1, f"proj_plan_create_ex({N}, {K}, {dtype}, {epilogue}, {rmsnorm_eps})")
+            raise ProjError(-1, f"proj_plan_create_ex({N}, {K}, {dtype}, {epilogue}, {rmsnorm_eps}, packed={packed})")
         self._h = ctypes.c_void_p(h)
 
     @property
@@ -207,9 +221,12 @@ class Plan:
     def _prep(self, X, W, Y):
         import torch
         _bf16_2d(X, "X", self.K)
-        _bf16_2d(W, "W", self.K)
-        if W.shape[0] != self.N:
-            raise ValueError(f"W must be [{self.N}, {self.K}], got {tuple(W.shape)}")
+        if self.packed:
+            _bf16_packed(W, "Wp", self.N, self.K)
+        else:
+            _bf16_2d(W, "W", self.K)
+            if W.shape[0] != self.N:
+                raise ValueError(f"W must be [{self.N}, {self.K}], got {tuple(W.shape)}")
         M = X.shape[0]
         if Y is None:
             Y = torch.empty((M, self.NO), dtype=self.out_dtype, device=X.device)
@@ -234,9 +251,20 @@ class Plan:
                                 _stream_handle(stream)), "proj_run_ex")
         return Y
 
+    def run_packed(self, X, Wp, Y=None, stream=None, gamma=None):
+        """run() for a packed plan: Wp is pack_weights(W)."""
+        M, Y = self._prep(X, Wp, Y)
+        _check(_lib.proj_run_packed(self._h, X.data_ptr(), Wp.data_ptr(), Y.data_ptr(), M, self._gamma(gamma),
+                                    _stream_handle(stream)), "proj_run_packed")
+        return Y
+
     def run_ptr(self, X_ptr: int, W_ptr: int, Y_ptr: int, M: int, stream_handle, gamma_ptr=None) -> None:
-        """proj_run(_ex) on raw device addresses (benchmark loops)."""
-        if gamma_ptr is None:
+        """proj_run(_ex), or proj_run_packed for a packed plan, on raw device
+        addresses (benchmark loops)."""
+        if self.packed:
+            _check(_lib.proj_run_packed(self._h, X_ptr, W_ptr, Y_ptr, M, gamma_ptr, stream_handle),
+                   "proj_run_packed")
+        elif gamma_ptr is None:
             _check(_lib.proj_run(self._h, X_ptr, W_ptr, Y_ptr, M, stream_handle), "proj_run")
         else:
             _check(_lib.proj_run_ex(self._h, X_ptr, W_ptr, Y_ptr, M, gamma_ptr, stream_handle), "proj_run_ex")
@@ -266,6 +294,36 @@ class Plan:
 
     def describe(self) -> dict:
         return json.loads(_text(_lib.proj_plan_describe, self._h))
+
+
+def _bf16_packed(t, name: str, N: int, K: int):
+    import torch
+    shape = (N // PANEL_ROWS, K // PANEL_COLS, PANEL_ROWS, PANEL_COLS)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 values (bfloat16 or 16-bit bit patterns), got {t.dtype}")
+    if tuple(t.shape) != shape or not t.is_contiguous():
+        raise ValueError(f"{name} must be packed weights, a contiguous {shape} tensor (pack_weights), "
+                         f"got {tuple(t.shape)}")
+
+
+def pack_weights(W, Wp=None, stream=None):
+    """W [N, K] (bf16, row-major, on the device) in the packed layout of
+    proj_pack_weights, as a (N/128, K/64, 128, 64) tensor whose memory order is
+    that layout: element [p, b, r, q] = W[128 p + r, 64 b + q]."""
+    import torch
+    if W.dim() != 2 or not W.is_contiguous() or W.element_size() != 2 or not W.is_cuda:
+        raise ValueError("pack_weights: W must be a contiguous 16-bit [N, K] device matrix")
+    N, K = W.shape
+    if N % PANEL_ROWS or K % PANEL_COLS:
+        raise ValueError(f"pack_weights: N % 128 == 0 and K % 64 == 0 needed, got {N}x{K}")
+    if Wp is None:
+        Wp = torch.empty((N // PANEL_ROWS, K // PANEL_COLS, PANEL_ROWS, PANEL_COLS), dtype=W.dtype, device=W.device)
+    else:
+        _bf16_packed(Wp, "Wp", N, K)
+    _check(_lib.proj_pack_weights(N, K, W.data_ptr(), Wp.data_ptr(), _stream_handle(stream)), "proj_pack_weights")
+    return Wp
 
 
 def probe_read(buf, sink, never: int = 0x9E3779B9, stream=None) -> None:

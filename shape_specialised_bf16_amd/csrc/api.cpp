@@ -19,7 +19,7 @@ int device_arch(int dev, std::string* arch, int* cus);
 int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, proj_plan** out);
 void destroy_plan(proj_plan* p);
 int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream,
-             const float* gamma);
+             const float* gamma, bool packed);
 int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M);
 int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y,
                      int64_t M, hipStream_t stream, const float* gamma);
@@ -27,7 +27,8 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
 // Shape-independent support module, one per device, loaded on first use.
 struct SupportModule {
     hipModule_t mod = nullptr;
-    hipFunction_t probe = nullptr, round = nullptr, swiglu_f32 = nullptr, swiglu_bf16 = nullptr, rmsnorm = nullptr;
+    hipFunction_t probe = nullptr, round = nullptr, swiglu_f32 = nullptr, swiglu_bf16 = nullptr, rmsnorm = nullptr,
+                  pack = nullptr;
     int cus = 256;
 };
 static std::mutex g_support_mu;
@@ -53,7 +54,8 @@ static int support_module(SupportModule** out)
             (e = hipModuleGetFunction(&sm.round, sm.mod, "proj_round_bf16")) != hipSuccess ||
             (e = hipModuleGetFunction(&sm.swiglu_f32, sm.mod, "proj_swiglu_f32")) != hipSuccess ||
             (e = hipModuleGetFunction(&sm.swiglu_bf16, sm.mod, "proj_swiglu_bf16")) != hipSuccess ||
-            (e = hipModuleGetFunction(&sm.rmsnorm, sm.mod, "proj_rmsnorm_rows")) != hipSuccess)
+            (e = hipModuleGetFunction(&sm.rmsnorm, sm.mod, "proj_rmsnorm_rows")) != hipSuccess ||
+            (e = hipModuleGetFunction(&sm.pack, sm.mod, "proj_pack_panels")) != hipSuccess)
             return set_error(PROJ_EDEVICE, "hipModuleGetFunction(support): %s", hipGetErrorString(e));
     }
     *out = &sm;
@@ -87,7 +89,8 @@ static std::string describe(const proj_plan* p)
     std::ostringstream s;
     s << "{\"N\": " << p->N << ", \"K\": " << p->K << ", \"NO\": " << p->NO << ", \"epilogue\": \""
       << (p->epi ? "swiglu" : "none") << "\", \"prologue\": \"" << (p->pro ? "rmsnorm" : "none")
-      << "\", \"norm_eps\": " << p->eps << ", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
+      << "\", \"norm_eps\": " << p->eps << ", \"layout\": \"" << (p->wpack ? "packed" : "rows")
+      << "\", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
       << "\", \"arch\": \"" << p->arch << "\", \"device\": " << p->device << ", \"compile_s\": " << p->compile_s
       << ", \"tune_s\": " << p->tune_s << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
       << ", \"cache\": \"" << p->cache << "\", \"cache_path\": \"" << json_escape(p->cache_path) << "\""
@@ -135,13 +138,43 @@ proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int fusion, floa
 
 int proj_run(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream)
 {
-    return run_plan(plan, X, W, Y, M, stream, nullptr);
+    return run_plan(plan, X, W, Y, M, stream, nullptr, false);
 }
 
 int proj_run_ex(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, const float* gamma,
                 hipStream_t stream)
 {
-    return run_plan(plan, X, W, Y, M, stream, gamma);
+    return run_plan(plan, X, W, Y, M, stream, gamma, false);
+}
+
+int proj_run_packed(const proj_plan* plan, const void* X, const void* Wp, void* Y, int64_t M, const float* gamma,
+                    hipStream_t stream)
+{
+    return run_plan(plan, X, Wp, Y, M, stream, gamma, true);
+}
+
+int proj_pack_weights(int64_t N, int64_t K, const void* W, void* Wp, hipStream_t stream)
+{
+    if (N < 0 || K < 0) return set_error(PROJ_EINVAL, "N and K must not be negative");
+    if (N % 128 || K % 64)
+        return set_error(PROJ_EINVAL, "the packed layout needs N %% 128 == 0 and K %% 64 == 0, got N=%lld K=%lld",
+                         (long long)N, (long long)K);
+    if (N == 0 || K == 0) return PROJ_OK;
+    if (!W || !Wp) return set_error(PROJ_EINVAL, "null pointer (W=%p Wp=%p)", W, Wp);
+    if (((uintptr_t)W | (uintptr_t)Wp) & 15) return set_error(PROJ_EINVAL, "W and Wp must be 16-byte aligned");
+    const uintptr_t bytes = (uintptr_t)N * (uintptr_t)K * 2, a = (uintptr_t)W, b = (uintptr_t)Wp;
+    if (a < b + bytes && b < a + bytes) return set_error(PROJ_EINVAL, "W and Wp overlap");
+    SupportModule* sm = nullptr;
+    int rc = support_module(&sm);
+    if (rc) return rc;
+    const void* w = W;
+    void* wp = Wp;
+    long nn = (long)N, kk = (long)K;
+    void* args[] = {&w, &wp, &nn, &kk};
+    const unsigned gx = (unsigned)std::min<int64_t>((N * K / 8 + 255) / 256, 65536);
+    hipError_t e = hipModuleLaunchKernel(sm->pack, gx, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
+    if (e != hipSuccess) return set_error(PROJ_EDEVICE, "pack launch: %s", hipGetErrorString(e));
+    return PROJ_OK;
 }
 
 void proj_plan_destroy(proj_plan* plan) { destroy_plan(plan); }
@@ -157,9 +190,12 @@ int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int fusion, float norm_
                         size_t cap, size_t* needed)
 {
     const int epilogue = fusion & PROJ_EPI_SWIGLU;
-    if (fusion & ~(PROJ_EPI_SWIGLU | PROJ_PRO_RMSNORM)) return set_error(PROJ_EINVAL, "invalid fusion flags %d", fusion);
+    if (fusion & ~(PROJ_EPI_SWIGLU | PROJ_PRO_RMSNORM | PROJ_W_PACKED))
+        return set_error(PROJ_EINVAL, "invalid flags %d", fusion);
     if (N < 1 || K < 8 || K % 8 != 0)
         return set_error(PROJ_EINVAL, "invalid shape N=%lld K=%lld", (long long)N, (long long)K);
+    if ((fusion & PROJ_W_PACKED) && (N % 128 || K % 64))
+        return set_error(PROJ_EINVAL, "the packed layout needs N %% 128 == 0 and K %% 64 == 0");
     if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16) return set_error(PROJ_EINVAL, "invalid dtype %d", dtype);
     if (epilogue == PROJ_EPI_SWIGLU && N % 2)
         return set_error(PROJ_EINVAL, "the SwiGLU epilogue needs an even N, got N=%lld", (long long)N);

@@ -36,7 +36,7 @@ static std::string fmt(const char* f, ...)
 
 std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int fusion)
 {
-    const int epi = fusion & 1, pro = (fusion & 2) ? 1 : 0;
+    const int epi = fusion & 1, pro = (fusion & 2) ? 1 : 0, wpack = (fusion & 4) ? 1 : 0;
     std::vector<Candidate> out;
     const int64_t CH = K / 8;  // 16-byte chunks per row
 
@@ -96,6 +96,7 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int f
     for (int S : {1, 2, 4}) {
         if (epi) break;                 // no fused epilogue in the MFMA GEMV
         for (int U : {2, 4}) {
+            if (wpack && U % 2) continue;   // panel layout: a batch is whole 8-chunk block rows
             const int RG = 4 / S;
             if (N % (16 * RG)) continue;
             if (K % (32 * U * S)) continue;
@@ -127,6 +128,7 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int f
         {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 4, 8, 1, {}}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
+        if (wpack && 64 % g.BK) continue;  // panel layout: a k-tile inside one 64-value block
         const int cpr = g.BK / 8, rpi = 64 * g.WM * g.WN / cpr;
         if ((rpi >> g.SWZ) % cpr) continue;  // the copy slots' swizzled column must not vary per copy
         const int lds = g.ST * (g.BM + g.BN) * g.BK * 2;
@@ -181,14 +183,18 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
                         const std::vector<Candidate>& cands, int fusion, float norm_eps)
 {
     const char* out = dtype == 1 ? "OUT_BF16" : "OUT_F32";
-    const int epi = fusion & 1;
+    const int epi = fusion & 1, wpack = (fusion & 4) ? 1 : 0;
     char eps_lit[64];
     snprintf(eps_lit, sizeof eps_lit, "%a", (double)norm_eps);
+    // how the candidate comments below describe the weight stream
+    const std::string wdesc = wpack ? std::string("weights in 16 KiB panel blocks")
+                                    : fmt("weight row stride %lld B", (long long)(2 * K));
     std::ostringstream s;
     s << "// Generated by libproj for Y[M," << N << "] = X[M," << K << "] . W[" << N << "," << K
       << "]^T, output " << (dtype == 1 ? "bf16" : "f32") << ", target " << arch
       << (epi ? ", SwiGLU epilogue: Y[M, N/2] = silu(gate) * up" : "")
-      << ((fusion & 2) ? ", RMSNorm prologue on X" : "") << ".\n";
+      << ((fusion & 2) ? ", RMSNorm prologue on X" : "")
+      << (wpack ? ", W in the panel layout (128-row panels of 128 x 64 blocks)" : "") << ".\n";
     s << "// Every constant below is an immediate of the kernels; M is the only run-time size.\n";
     s << "constexpr long N = " << N << ";            // output rows = rows of W\n";
     s << "constexpr long K = " << K << ";            // row length (bf16 values)\n";
@@ -199,6 +205,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
     s << "constexpr int EPI = " << epi << ";            // epilogue: 0 none, 1 SwiGLU of gate rows [0, N/2) and up rows [N/2, N)\n";
     s << "constexpr long NOUT = " << (epi ? N / 2 : N) << ";         // columns of Y\n";
     s << "constexpr int OUT_SEL = " << dtype << ";        // storage type of Y: 0 f32, 1 bf16\n";
+    s << "constexpr int WPACK = " << wpack << ";          // layout of W: 0 row-major, 1 panels of 128 rows x 64-value blocks\n";
     s << "constexpr float NORM_EPS = " << eps_lit << "f;   // RMSNorm epsilon of the fused prologue ("
       << ((fusion & 2) ? "" : "unused: ") << norm_eps << ")\n\n";
     s << kDeviceCommonSrc << "\n";
@@ -217,7 +224,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
             const int64_t chs = K / 8 / c.S;
             s << "// " << c.name << ": " << c.R << " row(s)/wave, K split " << c.S << " ways, "
               << chs << " blocks/slice = " << chs / 64 << " trip(s) of 64 lanes + " << chs % 64
-              << " tail lanes, weight row stride " << 2 * K << " B\n";
+              << " tail lanes, " << wdesc << "\n";
             s << "static_assert(K_BLOCKS16 / " << c.S << " / 64 == " << chs / 64 << ", \"trip count\");\n";
             s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_valu<"
               << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out << ", "
@@ -227,8 +234,8 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
         case Family::GemvMfma: {
             const int64_t batches = K / c.S / (32 * c.U);
             s << "// " << c.name << ": 16 rows/wave on mfma_16x16x32_bf16, K split " << c.S << " ways, "
-              << batches << " batch(es) of " << c.U << " MFMA steps, weight row stride " << 2 * K
-              << " B, next 16-row weight block at +" << 32 * K << " B\n";
+              << batches << " batch(es) of " << c.U << " MFMA steps, " << wdesc << ", next 16-row weight block at +"
+              << (wpack ? 16 * 64 * 2 : 32 * K) << " B\n";
             s << "static_assert(K / " << c.S << " / " << 32 * c.U << " == " << batches << ", \"trip count\");\n";
             s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_mfma<"
               << c.S << ", " << c.U << ", " << c.NT << ", " << out << ">(X, W, Y, M); }\n";
@@ -238,8 +245,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
             const int64_t kt = K / c.SK / c.BK;
             s << "// " << c.name << ": " << c.BM << "x" << c.BN << " tile, " << c.WM * c.WN << " waves, "
               << c.ST << " LDS buffers of " << (c.BM + c.BN) * c.BK * 2 << " B, K split " << c.SK << " ways, "
-              << kt << " k-tile(s) of " << c.BK << ", " << N / c.BN << " tile column(s), weight row stride "
-              << 2 * K << " B\n";
+              << kt << " k-tile(s) of " << c.BK << ", " << N / c.BN << " tile column(s), " << wdesc << "\n";
             s << "static_assert(K / " << c.SK << " / " << c.BK << " == " << kt << ", \"trip count\");\n";
             s << "extern \"C\" __global__ __launch_bounds__(" << c.threads << ") void " << c.name << sig
               << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.BK << ", " << c.ST << ", " << c.WM << ", "

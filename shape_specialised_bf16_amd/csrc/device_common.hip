@@ -153,6 +153,16 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&v)[V], int lane)
     return v[0];
 }
 
+// Panel layout of a weight matrix W [N, K] (N % 128 == 0, K % 64 == 0), the
+// alternative to row-major that proj_pack_panels writes: W is cut into panels
+// of 128 consecutive rows, each panel is stored as K/64 consecutive blocks of
+// 128 rows x 64 values (16 KiB), and each block is row-major.  Counted in
+// 16-byte chunks (8 values), chunk c of row n (values 8c .. 8c+7) sits at
+//     (n / 128) * 16K + (c / 8) * 1024 + (n % 128) * 8 + c % 8.
+// The 64-value k-slice of up to 128 rows that one MFMA tile step reads is then
+// one contiguous run of memory instead of one 128-byte piece per row.
+constexpr long kPanelRows = 128, kPanelCols = 64;
+
 template <int V> struct log2_of { static constexpr int value = 1 + log2_of<V / 2>::value; };
 template <> struct log2_of<1> { static constexpr int value = 0; };
 

@@ -189,7 +189,11 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     const int r0 = tid / CPR;
     const int ccol = (tid % CPR) ^ ((r0 >> SWZ) & (CPR - 1));
     const u16* __restrict__ abase = X + m0 * K + kbeg;
-    const u16* __restrict__ bbase = W + n0 * K + kbeg;
+    // B source: row-major, from the tile's first row at column kbeg; in the
+    // panel layout, from the start of the panel holding that row (pb), with the
+    // k position in the scalar offset (koffb)
+    const long pb = WPACK ? n0 - (n0 & (dev::kPanelRows - 1)) : n0;
+    const u16* __restrict__ bbase = WPACK ? W + pb * K : W + n0 * K + kbeg;
     const long mlast = (long)M - 1 - m0;              // last valid row relative to m0
     unsigned aoff[IA];
 #pragma unroll
@@ -218,18 +222,35 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     // compiler can only wait for all LDS reads at once.)
     constexpr long B_ROWS = EPI ? NOUT + BN / 2 : BN;   // weight rows spanned by the B descriptor
     static_assert((long)(BM > B_ROWS ? BM : B_ROWS) * K * 2 < (1L << 31), "tile rows fit a 32-bit buffer size");
+    static_assert(!WPACK || (B_ROWS / dev::kPanelRows + 2) * dev::kPanelRows * K * 2 < (1L << 31),
+                  "the panels a tile touches fit a 32-bit buffer size");
     const long rows_a = (long)M - m0 < BM ? (long)M - m0 : BM;
+    // bytes of W the descriptor covers: the tile's rows from column kbeg on, or
+    // the whole panels that hold the tile's rows
+    const long bspan = WPACK ? ((n0 + B_ROWS - 1) / dev::kPanelRows - pb / dev::kPanelRows + 1) *
+                                   dev::kPanelRows * K * 2
+                             : (B_ROWS * K - kbeg) * 2;
     const __amdgpu_buffer_rsrc_t rsa =
         __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, (int)((rows_a * K - kbeg) * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsb =
-        __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)((B_ROWS * K - kbeg) * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)bspan, 0x00020000);
     unsigned abyte[IA], bbyte[IB];
 #pragma unroll
     for (int i = 0; i < IA; ++i) abyte[i] = aoff[i] * 2;
+    // (in the panel layout a k-tile's chunks of one row are contiguous: BK is at
+    //  most one 64-value block and k-tiles start at multiples of BK)
+    static_assert(!WPACK || dev::kPanelCols % BK == 0, "k-tiles inside one panel block");
 #pragma unroll
-    for (int i = 0; i < IB; ++i) bbyte[i] = (unsigned)((wrow(i * RPI + r0) * K + ccol * 8) * 2);
+    for (int i = 0; i < IB; ++i)
+        bbyte[i] = WPACK ? (unsigned)((w_row(n0 + wrow(i * RPI + r0)) - w_row(pb) + ccol) * 16)
+                         : (unsigned)((wrow(i * RPI + r0) * K + ccol * 8) * 2);
+    // byte offset of k-tile kt of this tile's K range in the B source
+    auto koffb = [&](long kt) -> unsigned {
+        if constexpr (WPACK) return (unsigned)(w_col((kbeg + kt * BK) / 8) * 16);
+        else return (unsigned)(kt * BK * 2);
+    };
     auto issue = [&](u32x4* dst, long kt) {
         const unsigned koff = (unsigned)(kt * BK * 2);
+        const unsigned kob = koffb(kt);
 #pragma unroll
         for (int i = 0; i < IA; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(dst + i * NTHR + wave * 64), 16, abyte[i],
@@ -237,16 +258,16 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 #pragma unroll
         for (int i = 0; i < IB; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(dst + CA + i * NTHR + wave * 64), 16,
-                                                     bbyte[i], koff, 0, 0);
+                                                     bbyte[i], kob, 0, 0);
     };
     u32x4 ra[DMA ? 1 : IA], rb[DMA ? 1 : IB];
     auto gload = [&](long kt) {
         const u16* a = abase + kt * BK;
-        const u16* b = bbase + kt * BK;
+        const char* b = reinterpret_cast<const char*>(bbase) + koffb(kt);
 #pragma unroll
         for (int i = 0; i < IA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a + aoff[i]);
 #pragma unroll
-        for (int i = 0; i < IB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b + bbyte[i] / 2);
+        for (int i = 0; i < IB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b + bbyte[i]);
     };
     auto lstore = [&](u32x4* dst) {
 #pragma unroll
@@ -507,13 +528,13 @@ __device__ __forceinline__ void gemm_plain(const u16* __restrict__ X, const u16*
     if (idx >= (long)M * NOUT) return;
     const long m = idx / NOUT, n = idx % NOUT;
     const u32x4* xp = reinterpret_cast<const u32x4*>(X + m * K);
-    const u32x4* wp = reinterpret_cast<const u32x4*>(W + n * K);
+    const u32x4* wp = reinterpret_cast<const u32x4*>(W) + w_row(n);
     float acc = 0.f;
-    for (long c = 0; c < K / 8; ++c) acc = dev::dot8(wp[c], xp[c], acc);
+    for (long c = 0; c < K / 8; ++c) acc = dev::dot8(wp[w_col(c)], xp[c], acc);
     if constexpr (EPI) {           // the up row of output column n is W row NOUT + n
-        const u32x4* up = reinterpret_cast<const u32x4*>(W + (NOUT + n) * K);
+        const u32x4* up = reinterpret_cast<const u32x4*>(W) + w_row(NOUT + n);
         float au = 0.f;
-        for (long c = 0; c < K / 8; ++c) au = dev::dot8(up[c], xp[c], au);
+        for (long c = 0; c < K / 8; ++c) au = dev::dot8(up[w_col(c)], xp[c], au);
         acc = dev::swiglu<OUT>(acc, au);
     }
     dev::store1<OUT>(Y, idx, acc);

@@ -9,7 +9,9 @@
 // lanes striding over 16-byte (8 x bf16) blocks of the weight row, the row
 // length in blocks and the row count as constants ("#002 le meme compilateur
 // sur un GPU", section "Emettre pour un GPU").  The S waves of a row group
-// split K and combine through LDS in a fixed order.
+// split K and combine through LDS in a fixed order.  With W in the panel
+// layout the same chunks are read in the same order (so the sums are the
+// same); a load instruction then covers 8 runs of 128 bytes, 16 KiB apart.
 //
 // With P = 1 (M = 1 only) the batches of U trips are software-pipelined: the
 // loads of batch b+1 (weights and the matching X chunks) are issued before the
@@ -58,7 +60,8 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
     const int rg = wave / S;
     const long n0 = ((long)blockIdx.x * RG + rg) * (EPI ? R / 2 : R);   // first weight row = first output column
 
-    const u32x4* __restrict__ Wp = reinterpret_cast<const u32x4*>(W) + n0 * CH + s * CHS + lane;
+    // this lane's chunks of the slice; W row n, trip t: Wl + w_row(n) + t * W_TRIP
+    const u32x4* __restrict__ Wl = reinterpret_cast<const u32x4*>(W) + w_col(s * CHS + lane);
     const u32x4* __restrict__ Xg = reinterpret_cast<const u32x4*>(X) + s * CHS + lane;
     __shared__ u32x4 xs[PRO ? CH : 1];         // the normalised X row
     __shared__ float red[PRO ? 256 : 1];
@@ -94,7 +97,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) w[slot][u][r] = dev::load16<NT>(Wp + rowoff(r) * CH + (t0 + u) * 64);
+                for (int r = 0; r < R; ++r) w[slot][u][r] = dev::load16<NT>(Wl + w_row(n0 + rowoff(r)) + (t0 + u) * W_TRIP);
                 xv[slot][u] = Xp((t0 + u) * 64);
             }
         };
@@ -120,7 +123,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                w[u][r] = dev::load16<NT>(Wp + rowoff(r) * CH + (t0 + u) * 64);
+                w[u][r] = dev::load16<NT>(Wl + w_row(n0 + rowoff(r)) + (t0 + u) * W_TRIP);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -138,7 +141,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
         if (lane < TAIL) {
             u32x4 w[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) w[r] = dev::load16<NT>(Wp + rowoff(r) * CH + TRIPS * 64);
+            for (int r = 0; r < R; ++r) w[r] = dev::load16<NT>(Wl + w_row(n0 + rowoff(r)) + TRIPS * W_TRIP);
 #pragma unroll
             for (int m = 0; m < MMAX; ++m) {
                 if (m < M) {
@@ -218,7 +221,12 @@ __device__ __forceinline__ void gemv_mfma(const u16* __restrict__ X, const u16* 
     const int r = lane & 15, g = lane >> 4;
     const int mrow = r < M ? r : M - 1;
 
-    const u16* __restrict__ Wrow = W + (n0 + r) * K + s * KS + g * 8 * U;
+    // the lane's U consecutive chunks of batch b: Wl[b * W_BATCH + u] (in the
+    // panel layout the U chunks stay inside one 8-chunk block row: U is even
+    // and every batch starts at a multiple of 8 chunks)
+    static_assert(WPACK == 0 || U % 2 == 0, "panel layout: whole 8-chunk block rows per batch");
+    constexpr long W_BATCH = WPACK ? (4 * U / 8) * 1024 : 4 * U;
+    const u32x4* __restrict__ Wl = reinterpret_cast<const u32x4*>(W) + w_row(n0 + r) + w_col(s * KS / 8 + g * U);
     const u16* __restrict__ Xrow = X + (long)mrow * K + s * KS + g * 8 * U;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -226,7 +234,7 @@ __device__ __forceinline__ void gemv_mfma(const u16* __restrict__ X, const u16* 
         u32x4 w[U], x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            w[u] = dev::load16<NT>(reinterpret_cast<const u32x4*>(Wrow + b * 32 * U + u * 8));
+            w[u] = dev::load16<NT>(Wl + b * W_BATCH + u);
 #pragma unroll
         for (int u = 0; u < U; ++u)
             x[u] = *reinterpret_cast<const u32x4*>(Xrow + b * 32 * U + u * 8);

@@ -217,6 +217,10 @@ struct Tuner {
     hipFunction_t f_fill_probe = nullptr, f_fill_u32 = nullptr, f_ref = nullptr, f_ref_epi = nullptr,
                   f_check = nullptr, f_probe = nullptr;
     void *Xr = nullptr, *Xi = nullptr, *Wr = nullptr, *Wi = nullptr, *Y = nullptr;
+    // the weights as the candidates read them: Wr and Wi themselves, or their
+    // copies in the panel layout (the reference kernel always reads row-major)
+    void *Wrc = nullptr, *Wic = nullptr;
+    void *Wrp = nullptr, *Wip = nullptr;
     float* gamma = nullptr;            // RMSNorm prologue: the probe's norm weights (K floats)
     void *Xnr = nullptr, *Xni = nullptr; // and the normalised probe rows the reference reads
     float *ref_r = nullptr, *ref_i = nullptr;
@@ -231,7 +235,7 @@ struct Tuner {
     ~Tuner()
     {
         for (void* q : {Xr, Xi, Wr, Wi, Y, (void*)ref_r, (void*)ref_i, (void*)rows_d, (void*)stats_d, flush,
-                        (void*)gamma, Xnr, Xni})
+                        (void*)gamma, Xnr, Xni, Wrp, Wip})
             if (q) (void)hipFree(q);
         if (e0) (void)hipEventDestroy(e0);
         if (e1) (void)hipEventDestroy(e1);
@@ -246,6 +250,15 @@ struct Tuner {
         long nn = (long)n;
         void* args[] = {&buf, &nn, &seed, &kind, &scale};
         HIP_TRY(hipModuleLaunchKernel(f_fill_probe, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
+        return PROJ_OK;
+    }
+
+    int pack(const void* w, void* wp)
+    {
+        long n = (long)p->N, k = (long)p->K;
+        void* args[] = {&w, &wp, &n, &k};
+        const unsigned gx = (unsigned)std::min<int64_t>((p->N * p->K / 8 + 255) / 256, 65536);
+        HIP_TRY(hipModuleLaunchKernel(p->f_pack, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
         return PROJ_OK;
     }
 
@@ -297,6 +310,16 @@ struct Tuner {
         if ((rc = fill_probe(Wr, p->N * p->K, 2, 0, 0.0625f))) return rc;
         if ((rc = fill_probe(Xi, mmax * p->K, 3, 1, 1.0f))) return rc;
         if ((rc = fill_probe(Wi, p->N * p->K, 4, 1, 1.0f))) return rc;
+        Wrc = Wr;
+        Wic = Wi;
+        if (p->wpack) {
+            if (hipMalloc(&Wrp, wb) != hipSuccess || hipMalloc(&Wip, wb) != hipSuccess)
+                return set_error(PROJ_ENOMEM, "tuner panel-layout weights (%zu MiB) could not be allocated",
+                                 (2 * wb) >> 20);
+            if ((rc = pack(Wr, Wrp)) || (rc = pack(Wi, Wip))) return rc;
+            Wrc = Wrp;
+            Wic = Wip;
+        }
         if (p->pro) {
             // norm weights uniform in [0.5, 1.5): fill K bf16 values in [-0.5, 0.5),
             // widen on the host, add 1
@@ -415,7 +438,7 @@ struct Tuner {
         int rc;
         if ((rc = fill_sentinel(M + kGuardRows))) return rc;
         HIP_TRY(hipMemsetAsync(stats_d, 0, sizeof(CheckStats), st));
-        if ((rc = launch_candidate(p, c, integer ? Xi : Xr, integer ? Wi : Wr, Y, M, st, gamma))) return rc;
+        if ((rc = launch_candidate(p, c, integer ? Xi : Xr, integer ? Wic : Wrc, Y, M, st, gamma))) return rc;
         const void* yp = Y;
         long ra = (long)(M + kGuardRows);
         int m = (int)M;
@@ -450,12 +473,12 @@ struct Tuner {
     {
         int rc;
         for (int i = 0; i < 2; ++i)
-            if ((rc = launch_candidate(p, c, Xr, Wr, Y, M, st, gamma))) return rc;
+            if ((rc = launch_candidate(p, c, Xr, Wrc, Y, M, st, gamma))) return rc;
         std::vector<double> t;
         for (int i = 0; i < reps; ++i) {
             if ((rc = flush_cache())) return rc;
             HIP_TRY(hipEventRecord(e0, st));
-            if ((rc = launch_candidate(p, c, (i & 1) ? Xi : Xr, (i & 1) ? Wi : Wr, Y, M, st, gamma))) return rc;
+            if ((rc = launch_candidate(p, c, (i & 1) ? Xi : Xr, (i & 1) ? Wic : Wrc, Y, M, st, gamma))) return rc;
             HIP_TRY(hipEventRecord(e1, st));
             HIP_TRY(hipEventSynchronize(e1));
             float ms = 0;
@@ -554,7 +577,8 @@ static void cache_write(proj_plan* p)
         if (!f) return;
         f << "libproj tuning cache 1\n";
         f << "# N=" << p->N << " K=" << p->K << " dtype=" << (p->dtype ? "bf16" : "f32")
-          << " epilogue=" << (p->epi ? "swiglu" : "none") << " arch=" << p->arch << "\n";
+          << " epilogue=" << (p->epi ? "swiglu" : "none") << " layout=" << (p->wpack ? "panels" : "rows")
+          << " arch=" << p->arch << "\n";
         for (int b = 0; b < kNumBuckets; ++b)
             if (p->choice[b] >= 0)
                 f << "bucket " << b << " " << p->cands[p->choice[b]].name << " " << p->choice_us[b] << "\n";
@@ -738,8 +762,12 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
                          (long long)N, (long long)K);
     if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16)
         return set_error(PROJ_EINVAL, "invalid dtype %d (PROJ_OUT_F32=0 or PROJ_OUT_BF16=1)", dtype);
-    if (fusion & ~(PROJ_EPI_SWIGLU | PROJ_PRO_RMSNORM))
-        return set_error(PROJ_EINVAL, "invalid fusion flags %d (PROJ_EPI_SWIGLU=1 | PROJ_PRO_RMSNORM=2)", fusion);
+    if (fusion & ~(PROJ_EPI_SWIGLU | PROJ_PRO_RMSNORM | PROJ_W_PACKED))
+        return set_error(PROJ_EINVAL, "invalid flags %d (PROJ_EPI_SWIGLU=1 | PROJ_PRO_RMSNORM=2 | PROJ_W_PACKED=4)",
+                         fusion);
+    if ((fusion & PROJ_W_PACKED) && (N % 128 || K % 64))
+        return set_error(PROJ_EINVAL, "the packed weight layout needs N %% 128 == 0 and K %% 64 == 0, got N=%lld K=%lld",
+                         (long long)N, (long long)K);
     if ((fusion & PROJ_PRO_RMSNORM) && !(norm_eps >= 0.f && norm_eps < 1e30f))
         return set_error(PROJ_EINVAL, "invalid RMSNorm epsilon %g", (double)norm_eps);
     if (epi == PROJ_EPI_SWIGLU && N % 2)
@@ -752,6 +780,7 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
     p->epi = epi;
     p->pro = (fusion & PROJ_PRO_RMSNORM) ? 1 : 0;
     p->eps = p->pro ? norm_eps : 0.f;
+    p->wpack = (fusion & PROJ_W_PACKED) ? 1 : 0;
     p->NO = epi == PROJ_EPI_SWIGLU ? N / 2 : N;
     HIP_TRY(hipGetDevice(&p->device));
     int rc;
@@ -765,8 +794,8 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
     const double t0 = now_s();
     std::shared_ptr<std::vector<char>> code;
     char name[96];
-    snprintf(name, sizeof name, "proj_%lldx%lld_%s%s%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32",
-             epi ? "_swiglu" : "", p->pro ? "_rmsnorm" : "");
+    snprintf(name, sizeof name, "proj_%lldx%lld_%s%s%s%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32",
+             epi ? "_swiglu" : "", p->pro ? "_rmsnorm" : "", p->wpack ? "_panels" : "");
     if ((rc = compile_source(src, p->arch, name, &code))) return rc;
     p->compile_s = now_s() - t0;
     p->code_bytes = code->size();
@@ -778,6 +807,7 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
         }
     }
     HIP_TRY(hipModuleLoadData(&p->module, code->data()));
+    HIP_TRY(hipModuleGetFunction(&p->f_pack, p->module, "proj_pack_panels"));
     if (p->pro) {
         HIP_TRY(hipModuleGetFunction(&p->f_norm, p->module, "proj_rmsnorm_rows"));
         if (hipMalloc(&p->xn, (size_t)kMaxBlockRows * K * 2) != hipSuccess) {
@@ -837,8 +867,11 @@ int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, in
 }
 
 int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream,
-             const float* gamma)
+             const float* gamma, bool packed)
 {
+    if (p && p->wpack != (packed ? 1 : 0))
+        return set_error(PROJ_EINVAL, packed ? "this plan reads row-major weights: use proj_run or proj_run_ex"
+                                             : "this plan reads weights in the packed layout: use proj_run_packed");
     int rc = check_run_args(p, X, W, Y, M);
     if (rc || M == 0) return rc;
     if (p->pro && !gamma) return set_error(PROJ_EINVAL, "this plan has the RMSNorm prologue: gamma is required");

@@ -77,7 +77,8 @@ struct Candidate {
 // plain kernel, which fits any shape.
 // `cus` is the device's compute-unit count (it sets the tail split's round size).
 // fusion: bit 0 the SwiGLU epilogue (only the families that have it), bit 1 the
-// RMSNorm prologue (every candidate unfused, plus the M = 1 GEMVs with it folded in)
+// RMSNorm prologue (every candidate unfused, plus the M = 1 GEMVs with it folded in),
+// bit 2 weights in the panel layout (every family reads it; N % 128 == 0, K % 64 == 0)
 std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int fusion = 0);
 
 // The full translation unit for (N, K, dtype): prelude with the shape as
@@ -109,6 +110,8 @@ struct proj_plan {
     int dtype = 0;
     int epi = 0;        // PROJ_EPI_NONE or PROJ_EPI_SWIGLU
     int pro = 0;        // 1: RMSNorm prologue (proj_run_ex needs gamma)
+    int wpack = 0;      // 1: W in the panel layout (proj_pack_weights; run with proj_run_packed)
+    hipFunction_t f_pack = nullptr;  // the module's repacking kernel (proj_pack_panels)
     float eps = 0.f;    // its epsilon
     void* xn = nullptr; // workspace: normalised X rows for the unfused candidates (kMaxBlockRows x K bf16)
     hipFunction_t f_norm = nullptr;  // the module's separate norm kernel (proj_rmsnorm_rows)

@@ -1,5 +1,6 @@
-// support.hip -- shape-independent device code: the memory read probe and the
-// exposed epilogue rounding.  Compiled once per process and device by hipRTC.
+// support.hip -- shape-independent device code: the memory read probe, the
+// exposed epilogue rounding, the unfused SwiGLU and RMSNorm kernels and the
+// weight repacking.  Compiled once per process and device by hipRTC.
 
 // (types and the dev:: helpers come from device_common.hip, prepended by the host)
 
@@ -86,4 +87,24 @@ extern "C" __global__ __launch_bounds__(256) void proj_rmsnorm_rows(const u16* _
     const float r = dev::rms_scale_block(x, K, eps, red);
     u16* xn = Xn + (long)blockIdx.x * K;
     for (long k = threadIdx.x; k < K; k += 256) xn[k] = dev::rms_apply(x[k], r, gamma[k]);
+}
+
+// Weight repacking into the panel layout (dev::kPanelRows x dev::kPanelCols
+// blocks, see device_common): Wp receives the row-major W [N, K] (bf16 bit
+// patterns; N % 128 == 0, K % 64 == 0).  One thread per 16-byte chunk of Wp,
+// taken in Wp order: the writes are contiguous and each group of 8 lanes reads
+// one 128-byte run of a weight row.  Grid-stride over all N * K / 8 chunks.
+extern "C" __global__ __launch_bounds__(256) void proj_pack_panels(const u32x4* __restrict__ W,
+                                                                   u32x4* __restrict__ Wp, long N, long K)
+{
+    const long CH = K / 8;                              // chunks per weight row
+    const long blocks = K / dev::kPanelCols;            // 64-value blocks per row
+    const long total = N * CH;
+    for (long j = (long)blockIdx.x * blockDim.x + threadIdx.x; j < total; j += (long)gridDim.x * blockDim.x) {
+        const long q = j & 7;                           // chunk within the block row
+        const long r = (j >> 3) & (dev::kPanelRows - 1);  // row within the panel
+        const long b = (j >> 10) % blocks;              // 64-value block along K
+        const long p = (j >> 10) / blocks;              // panel
+        Wp[j] = W[(p * dev::kPanelRows + r) * CH + b * 8 + q];
+    }
 }

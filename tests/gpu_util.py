@@ -16,14 +16,14 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def plan(N: int, K: int, dtype: str = "f32", epilogue=None, rmsnorm_eps=None):
+def plan(N: int, K: int, dtype: str = "f32", epilogue=None, rmsnorm_eps=None, packed: bool = False):
     from shape_specialised_bf16_amd import Plan
 
-    key = (N, K, dtype, epilogue, rmsnorm_eps)
+    key = (N, K, dtype, epilogue, rmsnorm_eps, packed)
     if key not in _plans:
         log(f"[plan] creating {N}x{K} {dtype}" + (f" epilogue {epilogue}" if epilogue else "")
-            + (f" rmsnorm eps {rmsnorm_eps}" if rmsnorm_eps is not None else ""))
-        _plans[key] = Plan(N, K, dtype, epilogue=epilogue, rmsnorm_eps=rmsnorm_eps)
+            + (f" rmsnorm eps {rmsnorm_eps}" if rmsnorm_eps is not None else "") + (" packed" if packed else ""))
+        _plans[key] = Plan(N, K, dtype, epilogue=epilogue, rmsnorm_eps=rmsnorm_eps, packed=packed)
     return _plans[key]
 
 

@@ -27,6 +27,9 @@ Reported (one JSON line on stdout):
              tuner chose) against the separate norm kernel + plain plan
   long_prompt, layer_27b  the caller-side prompt-block driver (8192 rows in
              blocks of 1024, then the head) and the 27B-like layer
+  packed_weights  the decode step, the 4B-like layer at M = 2048 and the
+             27B-like gate/up at M = 8192 with weights in the packed layout
+             (proj_pack_weights + proj_run_packed) against row-major
   cpu_baseline  the fp64 CPU oracle on the same decode step, all host cores
   probe      HBM read-probe bandwidth on the same device (the pages' denominator)
 Progress goes to stderr.
@@ -45,6 +48,42 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
 ROTATE_BYTES = 1536 << 20       # weights rotate over at least this many bytes
+
+
+WARM_MS = 30.0                  # device time of warm-up before each timed kernel measurement
+
+
+def _events_us(fn, n):
+    """Mean device time (us) per call of the enqueue-only closure fn(s), s = 0..n-1:
+    one event pair on torch's current stream around all n calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for s in range(n):
+        fn(s)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+def warm(fn, warm_ms: float = WARM_MS):
+    """Run fn for about warm_ms of device time.  After an idle gap the device
+    takes ~15 ms to reach its steady clocks: a 4B-like gate/up GEMM at M = 2048
+    (18432 x 2560) measured 196-206 us per launch over its first ~80 launches
+    after a 3 s pause, then 172-175 us for as long as it kept running."""
+    est = _events_us(fn, 2)
+    k = int(warm_ms * 1e3 / max(est, 1.0))
+    if k > 0:
+        _events_us(fn, k)
+
+
+def steady_us(fn, n, rounds: int = 3, warm_ms: float = WARM_MS):
+    """Steady-state device time (us) per call of fn: warm-up, then `rounds`
+    rounds of n calls, each timed with one event pair; the median round."""
+    import statistics
+    warm(fn, warm_ms)
+    return statistics.median(_events_us(fn, n) for _ in range(rounds))
 
 
 def log(msg):
@@ -212,22 +251,15 @@ def time_prefill(reps: int = 20):
     out = {}
     plans = [Plan(p.N, p.K, "bf16") for p in cfg.projections]
     Ws = [upload(synth.weights(cfg, i)) for i in range(len(cfg.projections))]
-    stream = torch.cuda.current_stream()
+    sh = __import__("ctypes").c_void_p(torch.cuda.current_stream().cuda_stream)
     for M in (512, 2048):
         Xs = [upload(synth.activations(cfg, i, M)) for i in range(len(cfg.projections))]
         Ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in cfg.projections]
         per = []
         flops = 0
         for i, p in enumerate(cfg.projections):
-            for _ in range(3):
-                plans[i].run(Xs[i], Ws[i], Ys[i])
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                plans[i].run(Xs[i], Ws[i], Ys[i])
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / reps * 1e3
+            xp, wp, yp, pl = Xs[i].data_ptr(), Ws[i].data_ptr(), Ys[i].data_ptr(), plans[i]
+            us = steady_us(lambda s: pl.run_ptr(xp, wp, yp, M, sh), reps)
             f = 2.0 * M * p.N * p.K
             flops += f
             per.append(dict(proj=p.name, N=p.N, K=p.K, kernel=plans[i].choice(M), us=round(us, 2),
@@ -298,15 +330,7 @@ def time_long_prompt(reps: int = 5):
                                  Ys[i].data_ptr() + b * block * p.N * 2, block, sh)
         hplan.run_ptr(HX.data_ptr(), HW.data_ptr(), logits.data_ptr(), 1, sh)
 
-    prompt()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        prompt()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / reps * 1e3
+    us = steady_us(lambda s: prompt(), reps)
     for i, p in enumerate(layer):
         _check_rows(Ys[i], *host[i], [0, block - 1, block, rows_total - 1], "bf16", f"long prompt {p.name}")
     _check_rows(logits, hx, hw, [0], "f32", "long prompt head")
@@ -323,7 +347,7 @@ def time_long_prompt(reps: int = 5):
     return out
 
 
-def time_27b(steps: int = 500, warmup: int = 20, reps: int = 5):
+def time_27b(steps: int = 500, reps: int = 5):
     """27B-like layer (weights with 1 % outliers x10, bf16 Y): the four
     projections at M = 1 (rotating weight copies, as the decode leg) and at
     M = 8192."""
@@ -354,16 +378,7 @@ def time_27b(steps: int = 500, warmup: int = 20, reps: int = 5):
         for i in range(len(projs)):
             plans[i].run_ptr(X1[i].data_ptr(), Wrot[i][c].data_ptr(), Y1[i].data_ptr(), 1, sh)
 
-    for s in range(warmup):
-        step(s)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for s in range(steps):
-        step(s)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / steps * 1e3
+    us = steady_us(step, steps)
     step_bytes = sum(2 * p.N * p.K + 2 * p.K + 2 * p.N for p in projs)
     for i, p in enumerate(projs):
         _check_rows(Y1[i], X1h[i], Wh[i], [0], "bf16", f"27b {p.name} M=1")
@@ -380,14 +395,8 @@ def time_27b(steps: int = 500, warmup: int = 20, reps: int = 5):
         xh = synth.activations(cfg, i, M)
         X = upload(xh)
         Y = torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda")
-        plans[i].run(X, Ws[i], Y)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            plans[i].run(X, Ws[i], Y)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / reps * 1e3
+        xp, wp, yp, pl = X.data_ptr(), Ws[i].data_ptr(), Y.data_ptr(), plans[i]
+        t = steady_us(lambda s: pl.run_ptr(xp, wp, yp, M, sh), reps)
         f = 2.0 * M * p.N * p.K
         flops += f
         _check_rows(Y, xh, Wh[i], [0, 4095, M - 1], "bf16", f"27b {p.name} M={M}")
@@ -446,18 +455,7 @@ def time_swiglu(steps: int = 1000, reps: int = 20):
         def fused_(s):
             fused.run_ptr(xp, wps[s % copies], hfp, M, sh)
 
-        res = {}
-        for name, fn in (("unfused", unfused), ("fused", fused_)):
-            for s in range(20):
-                fn(s)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for s in range(n):
-                fn(s)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            res[name] = e0.elapsed_time(e1) / n * 1e3
+        res = {name: steady_us(fn, n) for name, fn in (("unfused", unfused), ("fused", fused_))}
         rows = [0] if M == 1 else [0, 1023, M - 1]
         import oracle
         from oracle import tolerance
@@ -531,16 +529,7 @@ def time_rmsnorm(steps: int = 1000):
         res = {}
         n = steps if p.N * p.K < (1 << 26) else steps // 10
         for name, fn in (("separate", separate), ("tuned", tuned)):
-            for s in range(20):
-                fn(s)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for s in range(n):
-                fn(s)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            res[name] = e0.elapsed_time(e1) / n * 1e3
+            res[name] = steady_us(fn, n)
         ref = oracle.rmsnorm_matmul(Xh, gh, Wh, eps)
         terms = oracle.rmsnorm_matmul(Xh, gh, Wh, eps, absolute=True)
         got = Y.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16" else Y.cpu().numpy()
@@ -561,6 +550,118 @@ def time_rmsnorm(steps: int = 1000):
         normp.close()
         plain.close()
         del Wrot, W
+    return out
+
+
+def time_packed(steps: int = 1000, reps: int = 20, rounds: int = 3):
+    """Weights in the packed layout (proj_pack_weights once, then proj_run_packed)
+    against row-major weights, each on its own tuned plan of the same shape:
+    the 0.8B-like decode step at M = 1 (f32 Y, rotating weight copies, as the
+    decode leg), the 4B-like layer at M = 2048 and the 27B-like gate/up at
+    M = 8192 (bf16 Y).  The two layouts are timed in alternation, `rounds`
+    times, and the median of each is reported."""
+    import statistics
+
+    import torch
+
+    import synth
+    from shape_specialised_bf16_amd import Plan, pack_weights
+
+    stream = torch.cuda.current_stream()
+    sh = __import__("ctypes").c_void_p(stream.cuda_stream)
+
+    def alternate(fr, fp, n):
+        warm(fr)
+        tr, tp = [], []
+        for _ in range(rounds):
+            tr.append(_events_us(fr, n))
+            tp.append(_events_us(fp, n))
+        return statistics.median(tr), statistics.median(tp)
+
+    out = {"workload": "packed weights (128-row panels of 128 x 64 blocks) vs row-major, same shapes, "
+                       "each layout on its own tuned plan"}
+    # ---- decode step, M = 1
+    cfg = synth.CONFIGS[1]
+    projs = cfg.projections
+    pr = [Plan(p.N, p.K, "f32") for p in projs]
+    pk = [Plan(p.N, p.K, "f32", packed=True) for p in projs]
+    Wh = [synth.weights(cfg, i) for i in range(len(projs))]
+    Xh = [synth.activations(cfg, i, 1) for i in range(len(projs))]
+    Ws = [upload(w) for w in Wh]
+    Wps = [pack_weights(w) for w in Ws]
+    Xs = [upload(x) for x in Xh]
+    Yr = [torch.empty((1, p.N), dtype=torch.float32, device="cuda") for p in projs]
+    Yp = [torch.empty((1, p.N), dtype=torch.float32, device="cuda") for p in projs]
+    step_bytes = sum(2 * p.N * p.K + 2 * p.K + 4 * p.N for p in projs)
+    copies = max(2, -(-ROTATE_BYTES // sum(w.numel() * 2 for w in Ws)))
+    Wr_rot = [[w] + [w.clone() for _ in range(copies - 1)] for w in Ws]
+    Wp_rot = [[w] + [w.clone() for _ in range(copies - 1)] for w in Wps]
+
+    def dec(plans, rot, Ys):
+        def step(s):
+            c = s % copies
+            for i in range(len(projs)):
+                plans[i].run_ptr(Xs[i].data_ptr(), rot[i][c].data_ptr(), Ys[i].data_ptr(), 1, sh)
+        return step
+
+    for f in (dec(pr, Wr_rot, Yr), dec(pk, Wp_rot, Yp)):
+        for s in range(20):
+            f(s)
+    torch.cuda.synchronize()
+    ur, up = alternate(dec(pr, Wr_rot, Yr), dec(pk, Wp_rot, Yp), steps)
+    for i, p in enumerate(projs):
+        _check_rows(Yp[i], Xh[i], Wh[i], [0], "f32", f"packed {p.name} M=1")
+        if not torch.equal(Yp[i], Yr[i]) and pk[i].choice(1) == pr[i].choice(1):
+            raise SystemExit(f"bench: packed {p.name} differs from row-major with the same kernel")
+    out["decode_08b_m1"] = dict(unit="GB/s", rows=round(step_bytes / ur / 1e3, 1), packed=round(step_bytes / up / 1e3, 1),
+                                rows_step_us=round(ur, 2), packed_step_us=round(up, 2),
+                                packed_over_rows=round(ur / up, 3), weight_copies_rotated=copies,
+                                kernels_rows={p.name: pr[i].choice(1) for i, p in enumerate(projs)},
+                                kernels_packed={p.name: pk[i].choice(1) for i, p in enumerate(projs)})
+    log(f"  packed decode M=1: {out['decode_08b_m1']['packed']} GB/s vs row-major {out['decode_08b_m1']['rows']}")
+    for pl in pr + pk:
+        pl.close()
+    del Wr_rot, Wp_rot, Ws, Wps
+
+    # ---- prefill: the 4B-like layer at M = 2048, and the 27B-like gate/up at M = 8192
+    def prefill(cfg, idxs, M, n, key, label):
+        per, fl, tr_all, tp_all = [], 0.0, 0.0, 0.0
+        for i in idxs:
+            p = cfg.projections[i]
+            wh, xh = synth.weights(cfg, i), synth.activations(cfg, i, M)
+            W, X = upload(wh), upload(xh)
+            Wp = pack_weights(W)
+            a, b = Plan(p.N, p.K, "bf16"), Plan(p.N, p.K, "bf16", packed=True)
+            Ya = torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda")
+            Yb = torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda")
+            fa = lambda s: a.run_ptr(X.data_ptr(), W.data_ptr(), Ya.data_ptr(), M, sh)   # noqa: E731
+            fb = lambda s: b.run_ptr(X.data_ptr(), Wp.data_ptr(), Yb.data_ptr(), M, sh)  # noqa: E731
+            fa(0)
+            fb(0)
+            torch.cuda.synchronize()
+            tr, tp = alternate(fa, fb, n)
+            _check_rows(Yb, xh, wh, [0, M // 2, M - 1], "bf16", f"packed {p.name} M={M}")
+            if a.choice(M) == b.choice(M) and not torch.equal(Ya.view(torch.int16), Yb.view(torch.int16)):
+                raise SystemExit(f"bench: packed {p.name} M={M} differs from row-major with the same kernel")
+            f = 2.0 * M * p.N * p.K
+            fl += f
+            tr_all += tr
+            tp_all += tp
+            per.append(dict(proj=p.name, N=p.N, K=p.K, kernel_rows=a.choice(M), kernel_packed=b.choice(M),
+                            rows_us=round(tr, 1), packed_us=round(tp, 1), rows_tflops=round(f / tr / 1e6, 1),
+                            packed_tflops=round(f / tp / 1e6, 1)))
+            a.close()
+            b.close()
+            del W, X, Wp, Ya, Yb
+        out[key] = dict(unit="TFLOP/s", rows=round(fl / tr_all / 1e6, 1), packed=round(fl / tp_all / 1e6, 1),
+                        packed_over_rows=round(tr_all / tp_all, 3), projections=per)
+        log(f"  packed {label}: {out[key]['packed']} TFLOP/s vs row-major {out[key]['rows']}")
+
+    cfg4 = synth.CONFIGS[2]
+    prefill(cfg4, range(len(cfg4.projections)), 2048, reps, "prefill_4b_m2048", "4B layer M=2048")
+    cfg27 = synth.CONFIGS[4]
+    gu = [i for i, p in enumerate(cfg27.projections) if p.N == max(q.N for q in cfg27.projections)]
+    prefill(cfg27, gu, 8192, 5, "gate_up_27b_m8192", "27B gate/up M=8192")
     return out
 
 
@@ -604,7 +705,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    # 500 untimed decode steps are ~30 ms of device time: the device reaches its
+    # steady clocks within ~15 ms of work after an idle gap (see warm())
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-prompt and 27B-layer legs")
@@ -701,6 +804,7 @@ def main():
         result["long_prompt"] = time_long_prompt()
         torch.cuda.empty_cache()
         result["layer_27b"] = time_27b()
+        result["packed_weights"] = time_packed()
         torch.cuda.empty_cache()
     result["cpu_baseline"] = None if args.no_cpu else cpu_baseline(d["host"], d["step_bytes"])
     print(json.dumps(result), flush=True)

@@ -114,9 +114,14 @@ proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
  * projection of "#004 the same compiler on Apple's chips", section "Decode"
  * (each fusion gives the same bits as the kernels it replaces), and of "#002
  * le meme compilateur sur un GPU", section "Emettre pour un GPU" (the
- * activation fused with the projection that produces its input).  Only the
- * kernel families that have the fused epilogue are candidates (vector GEMVs
- * with an even row count per wave, whole-tile MFMA GEMMs, the plain kernel).
+ * activation fused with the projection that produces its input).  The fused
+ * candidates come from the kernel families that have the epilogue (vector
+ * GEMVs with an even row count per wave, whole-tile MFMA GEMMs, the plain
+ * kernel); every other candidate of a plain plan is compiled as well and run
+ * unfused -- its N-column projection into an intermediate of the plan (as
+ * many rows of N values as fit 256 MiB, at most 8192), then the activation
+ * kernel -- and the load-time tuner picks between fused and unfused per row
+ * bucket, the fusion being an option measured at load (same page and section).
  *
  * PROJ_PRO_RMSNORM: X is normalised first, row by row, as by proj_rmsnorm with
  * epsilon `norm_eps` (a constant of the generated code) and the norm weights

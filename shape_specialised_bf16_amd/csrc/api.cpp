@@ -93,6 +93,7 @@ static std::string describe(const proj_plan* p)
       << "\", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
       << "\", \"arch\": \"" << p->arch << "\", \"device\": " << p->device << ", \"compile_s\": " << p->compile_s
       << ", \"tune_s\": " << p->tune_s << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
+      << ", \"swiglu_intermediate_rows\": " << p->gu_rows
       << ", \"cache\": \"" << p->cache << "\", \"cache_path\": \"" << json_escape(p->cache_path) << "\""
       << ",\n \"candidates\": [";
     for (size_t i = 0; i < p->cands.size(); ++i) s << (i ? ", " : "") << "\"" << p->cands[i].name << "\"";

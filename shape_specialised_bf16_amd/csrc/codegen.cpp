@@ -34,7 +34,33 @@ static std::string fmt(const char* f, ...)
     return buf;
 }
 
+static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, int fusion);
+
 std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int fusion)
+{
+    if (!(fusion & 1)) return enumerate_family(N, K, cus, fusion);
+    // SwiGLU plans: the candidates with the activation fused into their epilogue,
+    // then every plain candidate (not the plain kernel) run unfused -- the
+    // projection into the plan's intermediate, then the activation kernel --
+    // so that the tuner measures the fusion against the kernels it replaces;
+    // the fused plain kernel stays last (the tuner's last resort)
+    std::vector<Candidate> out = enumerate_family(N, K, cus, fusion);
+    Candidate plain = out.back();
+    out.pop_back();
+    for (Candidate& c : out) c.E = 1;
+    for (Candidate c : enumerate_family(N, K, cus, fusion & ~1)) {
+        if (c.fam == Family::Plain) continue;
+        c.UF = 1;
+        c.name += "_uf";
+        if (c.TAILS > 1) c.reduce_name = c.name + "_reduce";
+        out.push_back(c);
+    }
+    plain.E = 1;
+    out.push_back(plain);
+    return out;
+}
+
+static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, int fusion)
 {
     const int epi = fusion & 1, pro = (fusion & 2) ? 1 : 0, wpack = (fusion & 4) ? 1 : 0;
     std::vector<Candidate> out;
@@ -228,7 +254,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
             s << "static_assert(K_BLOCKS16 / " << c.S << " / 64 == " << chs / 64 << ", \"trip count\");\n";
             s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_valu<"
               << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out << ", "
-              << c.P << ", " << c.PRO << ">(X, W, Y, gamma, M); }\n";
+              << c.P << ", " << c.PRO << ", " << c.E << ">(X, W, Y, gamma, M); }\n";
             break;
         }
         case Family::GemvMfma: {
@@ -250,7 +276,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
             s << "extern \"C\" __global__ __launch_bounds__(" << c.threads << ") void " << c.name << sig
               << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.BK << ", " << c.ST << ", " << c.WM << ", "
               << c.WN << ", " << c.SK << ", " << c.GM << ", " << c.SWZ << ", " << out << ", " << c.DMA << ", "
-              << c.TAILS << ", " << c.ROUND << ">(X, W, Y, ws, M); }\n";
+              << c.TAILS << ", " << c.ROUND << ", " << c.E << ">(X, W, Y, ws, M); }\n";
             if (c.TAILS > 1) {
                 s << "// " << c.reduce_name << ": tail tiles of " << c.name << ", " << c.TAILS
                   << " pieces each, rounds of " << c.ROUND << " workgroups\n";
@@ -269,7 +295,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
         case Family::Plain:
             s << "// gemm_plain: one thread per output, " << K / 8 << " blocks of 16 bytes per dot product\n";
             s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig
-              << "\n{ gemm_plain<" << out << ">(X, W, Y, M); }\n";
+              << "\n{ gemm_plain<" << out << ", " << c.E << ">(X, W, Y, M); }\n";
             break;
         }
     }

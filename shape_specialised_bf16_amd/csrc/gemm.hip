@@ -108,10 +108,11 @@ __device__ __forceinline__ long xcd_remap(long pid0, long nblk)
 }  // namespace gemm_detail
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SK, int GROUP_M, int SWZ, int OUT, int DMA = 1,
-          int TAILS = 1, int ROUND = 0>
+          int TAILS = 1, int ROUND = 0, int E = 0>
 __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* __restrict__ W,
                                           void* __restrict__ Y, float* __restrict__ ws, int M)
 {
+    constexpr long NO = E ? N / 2 : N;                // columns of Y
     using namespace gemm_detail;
     constexpr int NTHR = WM * WN * 64;
     constexpr int CPR = BK / 8;                       // 16-byte chunks per LDS row
@@ -126,7 +127,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(N % BN == 0, "tiles cover N exactly");
-    static_assert(EPI == 0 || (SK == 1 && TAILS == 1 && (BN / WN) % 64 == 0),
+    static_assert(E == 0 || (SK == 1 && TAILS == 1 && (BN / WN) % 64 == 0),
                   "fused SwiGLU: whole tiles, gate and up halves of every wave's columns");
     constexpr int CA = BM * CPR, CB = BN * CPR;       // chunks per buffer
     static_assert(CA % NTHR == 0 && CB % NTHR == 0, "copies split evenly over threads");
@@ -176,8 +177,8 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     const long m0 = tm * BM;
     // first weight row of the tile (with the SwiGLU epilogue: its first gate row,
     // which is also its first output column; the tile reads BN/2 gate rows and
-    // the BN/2 up rows NOUT below them)
-    const long n0 = tn * (EPI ? BN / 2 : BN);
+    // the BN/2 up rows NO below them)
+    const long n0 = tn * (E ? BN / 2 : BN);
 
     // ---- global sources of the copy slots.  Copy instruction i of thread t fills
     //      slot i*NTHR + t, i.e. row i*RPI + t/CPR of the buffer; the chunk's column
@@ -206,9 +207,9 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     // SwiGLU epilogue each wave's WTN columns are WTN/2 gate rows followed by
     // the matching up rows, so both halves of a pair land in the same lane
     auto wrow = [&](int rr) -> long {
-        if constexpr (EPI) {
+        if constexpr (E) {
             const int wv = rr / WTN, c = rr % WTN;
-            return c < WTN / 2 ? (long)wv * (WTN / 2) + c : NOUT + (long)wv * (WTN / 2) + c - WTN / 2;
+            return c < WTN / 2 ? (long)wv * (WTN / 2) + c : NO + (long)wv * (WTN / 2) + c - WTN / 2;
         } else {
             return rr;
         }
@@ -220,7 +221,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     // fixed; the k-tile advances in the scalar offset.  (The global_ form of
     // the same copy is a FLAT instruction, and while one is outstanding the
     // compiler can only wait for all LDS reads at once.)
-    constexpr long B_ROWS = EPI ? NOUT + BN / 2 : BN;   // weight rows spanned by the B descriptor
+    constexpr long B_ROWS = E ? NO + BN / 2 : BN;   // weight rows spanned by the B descriptor
     static_assert((long)(BM > B_ROWS ? BM : B_ROWS) * K * 2 < (1L << 31), "tile rows fit a 32-bit buffer size");
     static_assert(!WPACK || (B_ROWS / dev::kPanelRows + 2) * dev::kPanelRows * K * 2 < (1L << 31),
                   "the panels a tile touches fit a 32-bit buffer size");
@@ -443,7 +444,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
         }
     }
     kloop(ic<KT>{});
-    if constexpr (EPI) {
+    if constexpr (E) {
         // block j < TN/2 holds gate rows, block j + TN/2 the matching up rows
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -454,7 +455,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
                 for (int e = 0; e < 16; ++e) {
                     const long row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lhalf + (e & 3);
                     if (row < M)
-                        dev::store1<OUT>(Y, row * NOUT + col, dev::swiglu<OUT>(acc[i][j][e], acc[i][j + TN / 2][e]));
+                        dev::store1<OUT>(Y, row * NO + col, dev::swiglu<OUT>(acc[i][j][e], acc[i][j + TN / 2][e]));
                 }
             }
         return;
@@ -520,19 +521,20 @@ __device__ __forceinline__ void tail_reduce(const float* __restrict__ ws, void* 
 // Plain kernel for any shape: one thread per output, k ascending, f32 FMA.
 // Serves shapes no tiled candidate divides.
 // ---------------------------------------------------------------------------
-template <int OUT>
+template <int OUT, int E = 0>
 __device__ __forceinline__ void gemm_plain(const u16* __restrict__ X, const u16* __restrict__ W,
                                            void* __restrict__ Y, int M)
 {
+    constexpr long NO = E ? N / 2 : N;                // columns of Y
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long)M * NOUT) return;
-    const long m = idx / NOUT, n = idx % NOUT;
+    if (idx >= (long)M * NO) return;
+    const long m = idx / NO, n = idx % NO;
     const u32x4* xp = reinterpret_cast<const u32x4*>(X + m * K);
     const u32x4* wp = reinterpret_cast<const u32x4*>(W) + w_row(n);
     float acc = 0.f;
     for (long c = 0; c < K / 8; ++c) acc = dev::dot8(wp[w_col(c)], xp[c], acc);
-    if constexpr (EPI) {           // the up row of output column n is W row NOUT + n
-        const u32x4* up = reinterpret_cast<const u32x4*>(W) + w_row(NOUT + n);
+    if constexpr (E) {           // the up row of output column n is W row NO + n
+        const u32x4* up = reinterpret_cast<const u32x4*>(W) + w_row(NO + n);
         float au = 0.f;
         for (long c = 0; c < K / 8; ++c) au = dev::dot8(up[w_col(c)], xp[c], au);
         acc = dev::swiglu<OUT>(acc, au);

@@ -19,9 +19,11 @@
 // load to its last instead of waiting out one memory round trip per batch --
 // what long rows (K of several thousand) need.
 //
-// With the SwiGLU epilogue (EPI == 1) a wave's R rows are R/2 gate rows j..
-// and their up rows NOUT + j..; after the reduction the up sum of a gate value
-// sits 32 lanes above it, and the wave stores silu(gate) * up in column j.
+// With the SwiGLU epilogue (E == 1, in a module whose W is a gate_up matrix)
+// a wave's R rows are R/2 gate rows j.. and their up rows N/2 + j..; after the
+// reduction the up sum of a gate value sits 32 lanes above it, and the wave
+// stores silu(gate) * up in column j of Y [M, N/2].  With E == 0 the kernel
+// writes all N sums (Y [M, N]).
 //
 // With the RMSNorm prologue (PRO == 1, M = 1 only) the block first
 // normalises the X row into LDS with the same dev::rms_scale_block and
@@ -34,10 +36,11 @@
 // Block: 256 threads = 4 waves = (4/S) row groups x S K-slices.
 // Grid:  N / (R * 4/S) blocks.
 // ---------------------------------------------------------------------------
-template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0, int PRO = 0>
+template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0, int PRO = 0, int E = 0>
 __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* __restrict__ W,
                                           void* __restrict__ Y, const float* __restrict__ gamma, int M)
 {
+    constexpr long NO = E ? N / 2 : N;          // columns of Y
     static_assert(PRO == 0 || MMAX == 1, "the fused norm prologue serves M = 1");
     static_assert(4 % S == 0, "S divides the 4 waves of a block");
     constexpr long CH = K / 8;                  // 16-byte chunks per row
@@ -50,15 +53,15 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
     static_assert(N % (R * RG) == 0, "blocks tile N exactly");
     constexpr int V = R * MMAX;
     constexpr int LV = dev::log2_of<V>::value;
-    static_assert(EPI == 0 || R % 2 == 0, "gate/up pairs: an even row count per wave");
+    static_assert(E == 0 || R % 2 == 0, "gate/up pairs: an even row count per wave");
     // weight row of the wave's row r, relative to the wave's first row
-    auto rowoff = [](int r) -> long { return (EPI && r >= R / 2) ? NOUT - R / 2 + r : r; };
+    auto rowoff = [](int r) -> long { return (E && r >= R / 2) ? NO - R / 2 + r : r; };
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int s = wave % S;
     const int rg = wave / S;
-    const long n0 = ((long)blockIdx.x * RG + rg) * (EPI ? R / 2 : R);   // first weight row = first output column
+    const long n0 = ((long)blockIdx.x * RG + rg) * (E ? R / 2 : R);   // first weight row = first output column
 
     // this lane's chunks of the slice; W row n, trip t: Wl + w_row(n) + t * W_TRIP
     const u32x4* __restrict__ Wl = reinterpret_cast<const u32x4*>(W) + w_col(s * CHS + lane);
@@ -160,27 +163,27 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
     const int r = idx / MMAX, m = idx % MMAX;
 
     if constexpr (S == 1) {
-        if constexpr (EPI) {
+        if constexpr (E) {
             const float up = __shfl_down(sum, 32);      // value idx + (R/2)*MMAX
-            if (writer && r < R / 2 && m < M) dev::store1<OUT>(Y, (long)m * NOUT + n0 + r, dev::swiglu<OUT>(sum, up));
+            if (writer && r < R / 2 && m < M) dev::store1<OUT>(Y, (long)m * NO + n0 + r, dev::swiglu<OUT>(sum, up));
         } else {
-            if (writer && m < M) dev::store1<OUT>(Y, (long)m * NOUT + n0 + r, sum);
+            if (writer && m < M) dev::store1<OUT>(Y, (long)m * NO + n0 + r, sum);
         }
     } else {
         __shared__ float red[4][V];
         if (writer) red[wave][idx] = sum;
         __syncthreads();
-        if (s == 0 && writer && m < M && (!EPI || r < R / 2)) {
+        if (s == 0 && writer && m < M && (!E || r < R / 2)) {
             float t = red[wave][idx];
 #pragma unroll
             for (int j = 1; j < S; ++j) t += red[wave + j][idx];
-            if constexpr (EPI) {
+            if constexpr (E) {
                 float tu = red[wave][idx + (R / 2) * MMAX];
 #pragma unroll
                 for (int j = 1; j < S; ++j) tu += red[wave + j][idx + (R / 2) * MMAX];
                 t = dev::swiglu<OUT>(t, tu);
             }
-            dev::store1<OUT>(Y, (long)m * NOUT + n0 + r, t);
+            dev::store1<OUT>(Y, (long)m * NO + n0 + r, t);
         }
     }
 }
@@ -209,7 +212,6 @@ __device__ __forceinline__ void gemv_mfma(const u16* __restrict__ X, const u16* 
     constexpr int RG = 4 / S;
     static_assert(N % (16 * RG) == 0, "blocks tile N exactly");
     static_assert(K % (32 * U * S) == 0, "K slices are whole batches");
-    static_assert(EPI == 0, "no fused epilogue in the MFMA GEMV");
     constexpr long KS = K / S;
     constexpr long BATCHES = KS / (32 * U);
 

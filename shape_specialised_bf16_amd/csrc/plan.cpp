@@ -147,7 +147,7 @@ static LaunchGeom geom(const Candidate& c, int64_t N, int64_t NO, int64_t M)
         return {(unsigned)(tm * (N / c.BN)), (unsigned)c.SK, (unsigned)c.threads};
     }
     case Family::Plain:
-    default: return {(unsigned)((M * NO + 255) / 256), 1u, 256u};
+    default: return {(unsigned)((M * (c.UF ? N : NO) + 255) / 256), 1u, 256u};
     }
 }
 
@@ -160,10 +160,13 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
     if (c.ws_bytes(M, p->N) > p->ws_bytes)
         return set_error(PROJ_EINVAL, "%s needs %zu bytes of split-K workspace at M=%lld, plan has %zu",
                          c.name.c_str(), c.ws_bytes(M, p->N), (long long)M, p->ws_bytes);
+    if (c.UF && M > p->gu_rows)
+        return set_error(PROJ_EINVAL, "%s needs %lld rows of the SwiGLU intermediate, plan has %lld", c.name.c_str(),
+                         (long long)M, (long long)p->gu_rows);
     const LaunchGeom g = geom(c, p->N, p->NO, M);
     const void* x = X;
     const void* w = W;
-    void* y = Y;
+    void* y = c.UF ? p->gu : Y;    // unfused SwiGLU: the N-column projection goes to the intermediate
     float* ws = (float*)p->ws;
     const float* gam = gamma;
     int m = (int)M;
@@ -192,6 +195,15 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
             void* rargs[] = {&wsc, &y, &m};
             HIP_TRY(hipModuleLaunchKernel(c.reduce_fn, gx, 1, 1, 256, 1, 1, 0, stream, rargs, nullptr));
         }
+    }
+    if (c.UF) {
+        // the separate activation kernel: Y[M, N/2] = silu(gate) * up of the intermediate
+        const void* gsrc = p->gu;
+        void* h = Y;
+        long mm = (long)M, nn = (long)p->N;
+        void* sargs[] = {&gsrc, &h, &mm, &nn};
+        const unsigned gx = (unsigned)std::min<int64_t>(65536, (M * (p->N / 2) + 255) / 256);
+        HIP_TRY(hipModuleLaunchKernel(p->f_swiglu, gx, 1, 1, 256, 1, 1, 0, stream, sargs, nullptr));
     }
     return PROJ_OK;
 }
@@ -605,6 +617,18 @@ int tune_plan(proj_plan* p)
             return set_error(PROJ_ENOMEM, "split-K workspace of %zu bytes", need);
         p->ws_bytes = need;
     }
+    // SwiGLU plans: the intermediate of the unfused candidates, as many rows as
+    // fit the same cap; an unfused candidate serves up to that many rows
+    if (p->epi) {
+        const size_t row_bytes = (size_t)p->N * (p->dtype == PROJ_OUT_BF16 ? 2 : 4);
+        p->gu_rows = std::min<int64_t>(kMaxBlockRows, (int64_t)(ws_cap / row_bytes));
+        if (p->gu_rows > 0 && hipMalloc(&p->gu, (size_t)p->gu_rows * row_bytes) != hipSuccess)
+            return set_error(PROJ_ENOMEM, "SwiGLU intermediate of %zu bytes", (size_t)p->gu_rows * row_bytes);
+        for (Candidate& c : p->cands)
+            if (c.UF) c.max_m = std::min<int64_t>(c.max_m, p->gu_rows);
+        HIP_TRY(hipModuleGetFunction(&p->f_swiglu, p->module,
+                                     p->dtype == PROJ_OUT_BF16 ? "proj_swiglu_bf16" : "proj_swiglu_f32"));
+    }
 
     Tuner T;
     T.p = p;
@@ -827,6 +851,7 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
     plog(p.get(), line);
     if ((rc = tune_plan(p.get()))) {
         if (p->ws) (void)hipFree(p->ws);
+        if (p->gu) (void)hipFree(p->gu);
         if (p->xn) (void)hipFree(p->xn);
         if (p->module) (void)hipModuleUnload(p->module);
         return rc;
@@ -845,6 +870,7 @@ void destroy_plan(proj_plan* p)
     (void)hipGetDevice(&cur);
     if (cur != p->device) (void)hipSetDevice(p->device);
     if (p->ws) (void)hipFree(p->ws);
+    if (p->gu) (void)hipFree(p->gu);
     if (p->xn) (void)hipFree(p->xn);
     if (p->module) (void)hipModuleUnload(p->module);
     if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);

@@ -28,6 +28,10 @@ struct Candidate {
     int R = 1, S = 1, MMAX = 1, U = 1, NT = 1;
     int P = 0;       // 1: software-pipelined batches of U trips (vector GEMV, M = 1)
     int PRO = 0;     // 1: RMSNorm folded into the kernel (vector GEMV, M = 1)
+    // SwiGLU plans: E = 1, the activation fused into the kernel's epilogue (Y has
+    // N/2 columns); UF = 1, the kernel writes all N sums into the plan's
+    // intermediate and the separate activation kernel produces Y
+    int E = 0, UF = 0;
     // GEMM parameters: block tile, k-tile, LDS buffers, wave grid, split-K,
     // tile-row group, LDS swizzle period
     int BM = 0, BN = 0, BK = 64, ST = 2, WM = 0, WN = 0, SK = 1, GM = 8, SWZ = 0;
@@ -76,7 +80,8 @@ struct Candidate {
 // Enumerate the candidates that tile (N, K) exactly.  Always ends with the
 // plain kernel, which fits any shape.
 // `cus` is the device's compute-unit count (it sets the tail split's round size).
-// fusion: bit 0 the SwiGLU epilogue (only the families that have it), bit 1 the
+// fusion: bit 0 the SwiGLU epilogue (the families that have it fused, then every
+// plain candidate again run unfused, "_uf"), bit 1 the
 // RMSNorm prologue (every candidate unfused, plus the M = 1 GEMVs with it folded in),
 // bit 2 weights in the panel layout (every family reads it; N % 128 == 0, K % 64 == 0)
 std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int fusion = 0);
@@ -114,6 +119,9 @@ struct proj_plan {
     hipFunction_t f_pack = nullptr;  // the module's repacking kernel (proj_pack_panels)
     float eps = 0.f;    // its epsilon
     void* xn = nullptr; // workspace: normalised X rows for the unfused candidates (kMaxBlockRows x K bf16)
+    void* gu = nullptr; // workspace: the N-column projection of the unfused SwiGLU candidates
+    int64_t gu_rows = 0;             // rows it holds
+    hipFunction_t f_swiglu = nullptr;  // the module's separate activation kernel (proj_swiglu_*)
     hipFunction_t f_norm = nullptr;  // the module's separate norm kernel (proj_rmsnorm_rows)
     uint64_t key = 0;   // tuning-cache key: device, runtime and driver versions, emitted source
     std::string cache;  // tuning cache: "off", "miss", "hit", "stale" (a cached choice failed the gate)

@@ -112,16 +112,25 @@ def test_emitted_source_compiles_for_gfx950(tmp_path):
 
 def test_swiglu_module_constants_and_families():
     """A SwiGLU plan's module carries the epilogue and the halved output width
-    as literals, and compiles only the kernel families that have the fused
-    epilogue: vector GEMVs with an even row count per wave, whole-tile GEMMs
-    whose waves hold gate and up halves (no split-K, no split tail), and the
-    plain kernel -- no MFMA GEMV."""
+    as literals.  Its fused candidates (the activation in their epilogue, E = 1)
+    come only from the families that have it: vector GEMVs with an even row
+    count per wave, whole-tile GEMMs whose waves hold gate and up halves (no
+    split-K, no split tail), and the plain kernel -- no MFMA GEMV.  Then every
+    candidate of the plain plan except the plain kernel appears again run
+    unfused ("_uf", E = 0: the N-column projection, then the activation kernel),
+    so the tuner can measure the fusion against what it replaces."""
     src = ssb.emit_source(6144, 1024, "f32", epilogue="swiglu")
     assert "constexpr int EPI = 1;" in src
     assert "constexpr long NOUT = 3072;" in src
-    names = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\(', src)
-    assert "gemm_plain" in names and any(n.startswith("gemv_valu") for n in names)
-    for n in names:
+    wrappers = dict(re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\([^)]*\)\n\{ ([^;]*);',
+                               src))
+    names = [n for n in wrappers if not n.endswith("_reduce")]
+    assert names[-1] == "gemm_plain" and any(n.startswith("gemv_valu") for n in names)
+    fused = [n for n in names if not n.endswith("_uf")]
+    unfused = [n[:-3] for n in names if n.endswith("_uf")]
+    for n in fused:
+        assert wrappers[n].endswith(", 1>(X, W, Y, gamma, M)") or wrappers[n].endswith(", 1>(X, W, Y, ws, M)") \
+            or wrappers[n].endswith(", 1>(X, W, Y, M)"), (n, wrappers[n])
         assert not n.startswith("gemv_mfma"), n
         m = re.match(r"gemv_valu_r(\d+)_", n)
         if m:
@@ -132,6 +141,12 @@ def test_swiglu_module_constants_and_families():
             assert SK == 1 and "_tail" not in n and (BN // WN) % 64 == 0, n
     plain = ssb.emit_source(6144, 1024, "f32")
     assert "constexpr int EPI = 0;" in plain and "constexpr long NOUT = 6144;" in plain
+    plain_names = [n for n in re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\(',
+                                         plain) if not n.endswith("_reduce") and n != "gemm_plain"]
+    assert unfused == plain_names
+    for n in unfused:
+        if not n.startswith("gemv_mfma"):
+            assert ", 0>(" in wrappers[n + "_uf"], (n, wrappers[n + "_uf"])
 
 
 def test_swiglu_odd_n_rejected():
@@ -162,7 +177,8 @@ def test_rmsnorm_module_has_folded_and_unfused_candidates():
     folded = [n for n in names if n.endswith("_nf")]
     assert folded and all(n.startswith("gemv_valu") and "_m1_" in n for n in folded)
     assert {n[:-3] for n in folded} == {n for n in plain if n.startswith("gemv_valu") and "_m1_" in n}
-    assert "gemv_valu<" in src and ", 1>(X, W, Y, gamma, M)" in src
+    # the folded copies pass PRO = 1 (the template argument before the epilogue's)
+    assert "gemv_valu<" in src and ", 1, 0>(X, W, Y, gamma, M)" in src
 
 
 def test_rmsnorm_and_swiglu_module_compiles(tmp_path):

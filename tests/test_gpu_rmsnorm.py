@@ -66,7 +66,9 @@ def test_folded_norm_equals_unfused(N, K, dtype):
         M = min(pn.candidate_max_m(idx), 130)
         Y = G.empty_out(M, N, dtype, extra_rows=1)
         pn.run_candidate(idx, Xd[:M], Wd, Y[:M], gamma=gd)
-        base = name[:-3] if name.endswith("_nf") else name
+        base = name
+        while base.endswith(("_nf", "_uf")):       # folded norm / unfused SwiGLU copies
+            base = base[:-3]
         # the plain plan's same variant on the separately normalised rows
         Yp = pp.run_candidate(plain_names.index(base), Xn[:M], Wd)
         torch.cuda.synchronize()
@@ -127,7 +129,9 @@ def test_norm_and_swiglu_together_equal_unfused_chain():
     for idx, name in enumerate(pb.candidates()):
         M = min(pb.candidate_max_m(idx), 17)
         H = pb.run_candidate(idx, Xd[:M], Wd, gamma=gd)
-        base = name[:-3] if name.endswith("_nf") else name
+        base = name
+        while base.endswith(("_nf", "_uf")):       # folded norm / unfused SwiGLU copies
+            base = base[:-3]
         Hu = ssb.swiglu(pp.run_candidate(pp.candidates().index(base), Xn[:M], Wd))
         torch.cuda.synchronize()
         assert np.array_equal(G.host(H).view(np.uint32), G.host(Hu).view(np.uint32)), name

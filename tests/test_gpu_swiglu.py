@@ -1,5 +1,7 @@
 """The SwiGLU epilogue folded into the gate_up projection (plans created with
-epilogue="swiglu", through proj_plan_create_ex), on the GPU.
+epilogue="swiglu", through proj_plan_create_ex), on the GPU.  Such a plan holds
+fused candidates and the plain candidates run unfused ("_uf"), the tuner
+choosing between them.
 
 "#004 the same compiler on Apple's chips", section "Decode": each fusion gives
 the same bits as the kernels it replaces, and is an option measured at load
@@ -47,8 +49,11 @@ def test_every_fused_candidate_equals_unfused_path(N, K, dtype):
     Wd = G.dev(W)
     unfused_names = pu.candidates()
     for idx, name in enumerate(pf.candidates()):
-        assert name in unfused_names, name
-        uidx = unfused_names.index(name)
+        # a fused candidate, or one of the plain plan's run unfused ("_uf"): both
+        # must equal the plain plan's variant followed by proj_swiglu
+        base = name[:-3] if name.endswith("_uf") else name
+        assert base in unfused_names, name
+        uidx = unfused_names.index(base)
         mmax = min(pf.candidate_max_m(idx), pu.candidate_max_m(uidx))
         Ms = [1, 5, 16] if mmax <= 16 else [1, 17, 130, 600]
         for M in [m for m in Ms if m <= mmax]:
@@ -140,3 +145,20 @@ def test_prefill_gate_up_4b_tuned(M):
     rows = G.sample_rows(M, seed=M)
     _check_vs_oracle(H, X, W, "bf16", rows=rows, label=f"4B gate_up fused M={M} {plan.choice(M)}")
     assert np.all(G.host(H)[M].view(np.uint16) == 0x7FC1)
+
+
+def test_tuner_measures_fused_against_unfused():
+    """The fusion is an option measured at load ("#004 the same compiler on
+    Apple's chips", section "Decode"): in every row bucket the tuner times fused
+    candidates and unfused ones ("_uf") side by side and picks from both."""
+    plan = G.plan(6144, 1024, "f32", epilogue="swiglu")
+    d = plan.describe()
+    assert d["swiglu_intermediate_rows"] == 8192
+    for b in d["buckets"]:
+        t = b["timings_us"]
+        fused = [n for n in t if not n.endswith("_uf")]
+        unfused = [n for n in t if n.endswith("_uf")]
+        assert fused and unfused, (b["lo"], b["hi"], sorted(t))
+        assert b["choice"] in t
+        G.log(f"  bucket {b['lo']}..{b['hi']}: best fused {min(fused, key=t.get)} {min(t[n] for n in fused):.2f} us, "
+              f"best unfused {min(unfused, key=t.get)} {min(t[n] for n in unfused):.2f} us -> {b['choice']}")

@@ -424,7 +424,26 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     };
 
     // ---- epilogue.  acc[i][j][e] of lane l is C[row][col] of its 32x32 block with
-    //      row = 8*(e>>2) + 4*(l>>5) + (e&3), col = l & 31.
+    //      row = 8*(e>>2) + 4*(l>>5) + (e&3), col = l & 31.  A tile whose rows all
+    //      lie below M (every tile but those of the last tile-row of a ragged M)
+    //      stores without per-element row checks, element e at the compile-time
+    //      distance 8*(e>>2) + (e&3) rows from the lane's first row of the block
+    //      (one 64-bit add of a constant per element, no branch); other tiles
+    //      check each element's row against M.
+    const bool full = m0 + BM <= (long)M;             // uniform across the workgroup
+    // body(e, r0, dr): element e of block row i, whose row is r0 + dr (r0 counted
+    // from row 0 of the destination, dr a constant once unrolled)
+    auto rows = [&](int i, auto&& body) {
+        const long r0 = m0 + wm * WTM + i * 32 + 4 * lhalf;
+        if (full) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) body(e, r0, 8 * (e >> 2) + (e & 3));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (r0 + 8 * (e >> 2) + (e & 3) < M) body(e, r0, 8 * (e >> 2) + (e & 3));
+        }
+    };
     if constexpr (TAILS > 1) {
         if (tail) {
             kloop(ic<KT_TAIL>{});
@@ -434,11 +453,10 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int col = wn * WTN + j * 32 + (lane & 31);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int row = wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lhalf + (e & 3);
-                        if (m0 + row < M) part[row * BN + col] = acc[i][j][e];
-                    }
+                    rows(i, [&](int e, long r0, int dr) {
+                        float* p = part + (r0 - m0) * BN + col;
+                        p[(long)dr * BN] = acc[i][j][e];
+                    });
                 }
             return;
         }
@@ -451,12 +469,10 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 #pragma unroll
             for (int j = 0; j < TN / 2; ++j) {
                 const long col = n0 + wn * (WTN / 2) + j * 32 + (lane & 31);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const long row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lhalf + (e & 3);
-                    if (row < M)
-                        dev::store1<OUT>(Y, row * NO + col, dev::swiglu<OUT>(acc[i][j][e], acc[i][j + TN / 2][e]));
-                }
+                rows(i, [&](int e, long r0, int dr) {
+                    const long b = r0 * NO + col;
+                    dev::store1<OUT>(Y, b + (long)dr * NO, dev::swiglu<OUT>(acc[i][j][e], acc[i][j + TN / 2][e]));
+                });
             }
         return;
     }
@@ -465,14 +481,15 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const long col = n0 + wn * WTN + j * 32 + (lane & 31);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const long row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lhalf + (e & 3);
-                if (row < M) {
-                    if constexpr (SK == 1) dev::store1<OUT>(Y, row * N + col, acc[i][j][e]);
-                    else ws[((long)z * M + row) * N + col] = acc[i][j][e];
+            rows(i, [&](int e, long r0, int dr) {
+                if constexpr (SK == 1) {
+                    const long b = r0 * N + col;
+                    dev::store1<OUT>(Y, b + (long)dr * N, acc[i][j][e]);
+                } else {
+                    const long b = ((long)z * M + r0) * N + col;
+                    ws[b + (long)dr * N] = acc[i][j][e];
                 }
-            }
+            });
         }
     }
 }

@@ -19,8 +19,9 @@ Reported (one JSON line on stdout):
   roofline   the head GEMV (the step's dominant kernel): its algorithmic bytes
              per launch / its mean launch time (HIP events on the launch
              stream), against 8 TB/s
-  prefill    the 4B-like layer at M = 512 and 2048 (bf16 out): TFLOP/s against
-             the 2.5 PFLOP/s dense bf16 MFMA peak, with its dominant kernel
+  prefill    the 4B-like layer at M = 128, 512 and 2048 (bf16 out): TFLOP/s
+             against the 2.5 PFLOP/s dense bf16 MFMA peak, with its dominant
+             kernel's roofline (against HBM where it is memory-bound: M = 128)
   swiglu_epilogue  the gate/up projection on a SwiGLU plan (its tuned choice,
              fused or unfused) against the plain plan + the separate
              activation kernel
@@ -243,6 +244,11 @@ def time_decode(steps: int, warmup: int):
 
 
 def time_prefill(reps: int = 20):
+    """The 4B-like layer at M = 128, 512 and 2048 (bf16 Y), each projection timed in
+    steady state and its output checked against the oracle on sampled rows.  The
+    roofline of the layer's dominant kernel is priced against the MFMA peak, or
+    against HBM where its arithmetic intensity is below the ridge point (2.5
+    PFLOP/s over 8 TB/s = 312.5 flop per byte: M = 128)."""
     import torch
 
     import synth
@@ -251,31 +257,41 @@ def time_prefill(reps: int = 20):
     cfg = synth.CONFIGS[2]
     out = {}
     plans = [Plan(p.N, p.K, "bf16") for p in cfg.projections]
-    Ws = [upload(synth.weights(cfg, i)) for i in range(len(cfg.projections))]
+    Wh = [synth.weights(cfg, i) for i in range(len(cfg.projections))]
+    Ws = [upload(w) for w in Wh]
     sh = __import__("ctypes").c_void_p(torch.cuda.current_stream().cuda_stream)
-    for M in (512, 2048):
-        Xs = [upload(synth.activations(cfg, i, M)) for i in range(len(cfg.projections))]
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    for M in (128, 512, 2048):
+        Xh = [synth.activations(cfg, i, M) for i in range(len(cfg.projections))]
+        Xs = [upload(x) for x in Xh]
         Ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in cfg.projections]
         per = []
         flops = 0
         for i, p in enumerate(cfg.projections):
             xp, wp, yp, pl = Xs[i].data_ptr(), Ws[i].data_ptr(), Ys[i].data_ptr(), plans[i]
             us = steady_us(lambda s: pl.run_ptr(xp, wp, yp, M, sh), reps)
+            _check_rows(Ys[i], Xh[i], Wh[i], [0, M // 2, M - 1], "bf16", f"prefill {p.name} M={M}")
             f = 2.0 * M * p.N * p.K
             flops += f
             per.append(dict(proj=p.name, N=p.N, K=p.K, kernel=plans[i].choice(M), us=round(us, 2),
                             tflops=round(f / us / 1e6, 1)))
         tot_us = sum(x["us"] for x in per)
         dom = max(per, key=lambda x: x["us"])
+        dbytes = 2 * (M * dom["K"] + dom["N"] * dom["K"] + M * dom["N"])
+        dflops = 2.0 * M * dom["N"] * dom["K"]
+        if dflops / dbytes < ridge:
+            gbs = dbytes / dom["us"] / 1e3
+            roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(gbs / HBM_PEAK_GBS, 4), tflops=dom["tflops"])
+        else:
+            roof = dict(bound="mfma", achieved=dom["tflops"], peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                        frac=round(dom["tflops"] / MFMA_BF16_PEAK_TFS, 4))
+        roof.update(kernel=dom["kernel"], shape=f"{dom['N']}x{dom['K']}", mean_launch_us=dom["us"],
+                    traffic=traffic_for(f"{dom['kernel']}@{dom['N']}x{dom['K']}m{M}"), algorithmic_bytes=dbytes,
+                    flop_per_byte=round(dflops / dbytes, 1))
         out[f"M{M}"] = dict(value=round(flops / tot_us / 1e6, 1), unit="TFLOP/s",
                             pct_peak=round(100 * flops / tot_us / 1e6 / MFMA_BF16_PEAK_TFS, 1),
-                            layer_us=round(tot_us, 2), projections=per,
-                            roofline=dict(bound="mfma", kernel=dom["kernel"], shape=f"{dom['N']}x{dom['K']}",
-                                          achieved=dom["tflops"], peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
-                                          frac=round(dom["tflops"] / MFMA_BF16_PEAK_TFS, 4),
-                                          mean_launch_us=dom["us"],
-                                          traffic=traffic_for(f"{dom['kernel']}@{dom['N']}x{dom['K']}m{M}"),
-                                          algorithmic_bytes=2 * (M * dom["K"] + dom["N"] * dom["K"] + M * dom["N"])))
+                            layer_us=round(tot_us, 2), projections=per, roofline=roof)
         log(f"  prefill M={M}: {out[f'M{M}']['value']} TFLOP/s over the layer ({tot_us:.1f} us)")
     for p in plans:
         p.close()

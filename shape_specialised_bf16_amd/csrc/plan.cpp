@@ -276,8 +276,10 @@ struct Tuner {
 
     int fill_sentinel(int64_t rows)
     {
+        // whole 32-bit words: with bf16 output and an odd element count the last
+        // word also covers the 2 bytes after the rows (the buffer is padded for it)
         const int64_t bytes = rows * p->NO * (int64_t)ysize();
-        long n32 = (long)(bytes / 4);
+        long n32 = (long)((bytes + 3) / 4);
         uint32_t v = p->dtype == PROJ_OUT_BF16 ? 0x7FBA7FBAu : 0x7FBADBADu;
         unsigned gx = (unsigned)std::min<int64_t>((n32 + 255) / 256, 65536);
         void* yp = Y;
@@ -300,7 +302,7 @@ struct Tuner {
         HIP_TRY(hipModuleGetFunction(&f_check, p->module,
                                      p->dtype == PROJ_OUT_BF16 ? "proj_check_bf16" : "proj_check_f32"));
         const size_t xb = (size_t)mmax * p->K * 2, wb = (size_t)p->N * p->K * 2;
-        const size_t yb = (size_t)(mmax + kGuardRows) * p->NO * ysize();
+        const size_t yb = ((size_t)(mmax + kGuardRows) * p->NO * ysize() + 3) / 4 * 4;   // whole words
         if (hipMalloc(&Xr, xb) != hipSuccess || hipMalloc(&Xi, xb) != hipSuccess ||
             hipMalloc(&Wr, wb) != hipSuccess || hipMalloc(&Wi, wb) != hipSuccess ||
             hipMalloc(&Y, yb) != hipSuccess || hipMalloc(&ref_r, 8 * p->N * 4) != hipSuccess ||

@@ -185,3 +185,30 @@ def test_wrong_arguments_are_rejected():
         p.run_ptr(0, W.data_ptr(), Y.data_ptr(), 4, None)
     with pytest.raises(ValueError):
         p.run(X, W[:512])
+
+
+# ------------------------------------------------------------------ degenerate shapes
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 16), (17, 24), (64, 8)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_degenerate_shapes(N, K, dtype):
+    """The smallest shapes a plan accepts (one output row, one 16-byte chunk per
+    weight row, counts no tile divides): only the families whose constraints
+    they meet are compiled, and the tuned result matches the oracle at M = 1, 2
+    and a ragged 17, every candidate bit-exact on the integer probe."""
+    W = synth.normal_bf16(65, N * 100 + K, (N, K), 0.5)
+    p = G.plan(N, K, dtype)
+    assert "gemm_plain" in p.candidates()
+    for M in (1, 2, 17):
+        X = synth.normal_bf16(65, M, (M, K), 1.0)
+        Y = G.empty_out(M, N, dtype, extra_rows=1)
+        p.run(G.dev(X), G.dev(W), Y)
+        G.check_against_oracle(Y, X, W, dtype, label=f"{N}x{K} {p.choice(M)}")
+        pat = 0x7FC1 if dtype == "bf16" else 0x7FC00001
+        assert np.all(G.host(Y)[M:].view(np.uint16 if dtype == "bf16" else np.uint32) == pat)
+    Wi, Xi = synth.int_bf16(66, (N, K)), synth.int_bf16(67, (17, K))
+    exact = oracle.matmul(Xi, Wi)
+    want = oracle.round_bf16(exact) if dtype == "bf16" else oracle.round_f32(exact)
+    for idx, name in enumerate(p.candidates()):
+        M = min(p.candidate_max_m(idx), 17)
+        got = G.host(p.run_candidate(idx, G.dev(Xi[:M]), G.dev(Wi)))
+        assert np.array_equal(got.view(np.uint8), want[:M].view(np.uint8)), f"{N}x{K} {name}"

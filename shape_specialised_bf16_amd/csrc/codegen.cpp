@@ -150,8 +150,8 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2}},
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},
-        {128, 128, 64, 2, 2, 2, 1, 4, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
-        {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 4, 8, 1, {}}};
+        {128, 128, 64, 2, 2, 2, 1, 8, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
+        {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 8, 8, 1, {}}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
         if (wpack && 64 % g.BK) continue;  // panel layout: a k-tile inside one 64-value block
@@ -179,7 +179,7 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
             if ((g.BN / g.WN) % 64 == 0 && K % g.BK == 0) add(1, 1);
             continue;
         }
-        for (int SK : {1, 2, 4})
+        for (int SK : {1, 2, 4, 8})
             if (SK <= g.maxSK && K % (g.BK * SK) == 0) add(SK, 1);
         for (int TL : g.tails)
             if (TL > 1 && (K / g.BK) % TL == 0) add(1, TL);
@@ -241,7 +241,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
     s << kGateSrc << "\n";
     s << kSupportSrc << "\n";
     s << "// ===================== candidates for this shape =====================\n";
-    bool reduce_emitted[5] = {false, false, false, false, false};
+    bool reduce_emitted[9] = {};    // split-K reduce kernels already emitted, by SK (at most 8)
     for (const Candidate& c : cands) {
         const char* sig = "(const u16* __restrict__ X, const u16* __restrict__ W, void* __restrict__ Y, "
                           "float* __restrict__ ws, const float* __restrict__ gamma, int M)";

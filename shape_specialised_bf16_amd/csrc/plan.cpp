@@ -314,6 +314,9 @@ struct Tuner {
         // so the launch reads its weights from HBM, as every decode step does.
         flush_bytes = (size_t)512 << 20;
         if (hipMalloc(&flush, flush_bytes) != hipSuccess) {
+            // tuned without the flush; clear the runtime's last error so that a
+            // caller checking it later does not see this tolerated failure
+            (void)hipGetLastError();
             flush = nullptr;
             flush_bytes = 0;
         } else {
@@ -615,8 +618,10 @@ int tune_plan(proj_plan* p)
     for (const Candidate& c : p->cands) need = std::max(need, c.ws_bound(kMaxBlockRows, p->N));
     need = std::min(need, ws_cap);
     if (need) {
-        if (hipMalloc(&p->ws, need) != hipSuccess)
+        if (hipMalloc(&p->ws, need) != hipSuccess) {
+            p->ws = nullptr;
             return set_error(PROJ_ENOMEM, "split-K workspace of %zu bytes", need);
+        }
         p->ws_bytes = need;
     }
     // SwiGLU plans: the intermediate of the unfused candidates, as many rows as
@@ -624,8 +629,10 @@ int tune_plan(proj_plan* p)
     if (p->epi) {
         const size_t row_bytes = (size_t)p->N * (p->dtype == PROJ_OUT_BF16 ? 2 : 4);
         p->gu_rows = std::min<int64_t>(kMaxBlockRows, (int64_t)(ws_cap / row_bytes));
-        if (p->gu_rows > 0 && hipMalloc(&p->gu, (size_t)p->gu_rows * row_bytes) != hipSuccess)
+        if (p->gu_rows > 0 && hipMalloc(&p->gu, (size_t)p->gu_rows * row_bytes) != hipSuccess) {
+            p->gu = nullptr;
             return set_error(PROJ_ENOMEM, "SwiGLU intermediate of %zu bytes", (size_t)p->gu_rows * row_bytes);
+        }
         for (Candidate& c : p->cands)
             if (c.UF) c.max_m = std::min<int64_t>(c.max_m, p->gu_rows);
         HIP_TRY(hipModuleGetFunction(&p->f_swiglu, p->module,
@@ -800,6 +807,18 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
         return set_error(PROJ_EINVAL, "the SwiGLU epilogue needs an even N (gate and up halves), got N=%lld",
                          (long long)N);
     std::unique_ptr<proj_plan> p(new proj_plan());
+    // until the plan is handed out, any early return releases what it holds
+    struct Release {
+        proj_plan* p;
+        ~Release()
+        {
+            if (!p) return;
+            if (p->ws) (void)hipFree(p->ws);
+            if (p->gu) (void)hipFree(p->gu);
+            if (p->xn) (void)hipFree(p->xn);
+            if (p->module) (void)hipModuleUnload(p->module);
+        }
+    } release{p.get()};
     p->N = N;
     p->K = K;
     p->dtype = dtype;
@@ -838,7 +857,6 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
         HIP_TRY(hipModuleGetFunction(&p->f_norm, p->module, "proj_rmsnorm_rows"));
         if (hipMalloc(&p->xn, (size_t)kMaxBlockRows * K * 2) != hipSuccess) {
             p->xn = nullptr;
-            (void)hipModuleUnload(p->module);
             return set_error(PROJ_ENOMEM, "RMSNorm workspace of %lld bytes", (long long)kMaxBlockRows * K * 2);
         }
     }
@@ -851,16 +869,11 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
              (long long)N, (long long)K, dtype ? "bf16" : "f32", p->cands.size(), p->arch.c_str(), p->compile_s,
              p->code_bytes);
     plog(p.get(), line);
-    if ((rc = tune_plan(p.get()))) {
-        if (p->ws) (void)hipFree(p->ws);
-        if (p->gu) (void)hipFree(p->gu);
-        if (p->xn) (void)hipFree(p->xn);
-        if (p->module) (void)hipModuleUnload(p->module);
-        return rc;
-    }
+    if ((rc = tune_plan(p.get()))) return rc;
     snprintf(line, sizeof line, "[proj] %lldx%lld: tuned %d row buckets in %.2f s", (long long)N, (long long)K,
              kNumBuckets, p->tune_s);
     plog(p.get(), line);
+    release.p = nullptr;
     *out = p.release();
     return PROJ_OK;
 }

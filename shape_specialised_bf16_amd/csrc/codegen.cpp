@@ -145,9 +145,11 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     //      Each entry also lists the K-split factors of its split-tail variants
     //      (whole tiles for all full rounds of workgroups, the remaining tiles
     //      split along K so the last round is not mostly idle).
-    struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[2]; };
+    // BST = 3: a third buffer for W only (two-buffer tiles, W copies two k-tiles ahead)
+    struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[2]; int BST = 0; };
     const GT gts[] = {
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2}},
+        {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3},
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},
         {128, 128, 64, 2, 2, 2, 1, 8, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
@@ -157,19 +159,20 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         if (wpack && 64 % g.BK) continue;  // panel layout: a k-tile inside one 64-value block
         const int cpr = g.BK / 8, rpi = 64 * g.WM * g.WN / cpr;
         if ((rpi >> g.SWZ) % cpr) continue;  // the copy slots' swizzled column must not vary per copy
-        const int lds = g.ST * (g.BM + g.BN) * g.BK * 2;
+        const int lds = (g.BST == 3 ? 2 * g.BM + 3 * g.BN : g.ST * (g.BM + g.BN)) * g.BK * 2;
+        if (lds > 160 * 1024) continue;   // the LDS of one workgroup
         const int per_cu = std::max(1, std::min(2, 160 * 1024 / lds));
         auto add = [&](int SK, int TL) {
             Candidate c;
             c.fam = Family::Gemm;
             c.BM = g.BM; c.BN = g.BN; c.BK = g.BK; c.ST = g.ST; c.WM = g.WM; c.WN = g.WN;
-            c.SK = SK; c.GM = g.GM; c.SWZ = g.SWZ; c.DMA = g.DMA;
+            c.SK = SK; c.GM = g.GM; c.SWZ = g.SWZ; c.DMA = g.DMA; c.BST = g.BST;
             c.TAILS = TL;
             c.ROUND = TL > 1 ? cus * per_cu : 0;
             c.threads = 64 * g.WM * g.WN;
             c.max_m = kMaxBlockRows;
-            c.name = fmt("gemm_%dx%dx%d_st%d_w%dx%d_sw%d_g%d_sk%d%s", c.BM, c.BN, c.BK, c.ST, c.WM, c.WN, c.SWZ,
-                         c.GM, c.SK, c.DMA ? "" : "_reg");
+            c.name = fmt("gemm_%dx%dx%d_st%d_w%dx%d_sw%d_g%d_sk%d%s%s", c.BM, c.BN, c.BK, c.ST, c.WM, c.WN, c.SWZ,
+                         c.GM, c.SK, c.DMA ? "" : "_reg", c.BST == 3 ? "_b3" : "");
             if (TL > 1) c.name += fmt("_tail%d_r%d", TL, c.ROUND);
             if (SK > 1) c.reduce_name = fmt("splitk_reduce_sk%d", SK);
             if (TL > 1) c.reduce_name = c.name + "_reduce";
@@ -276,7 +279,7 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
             s << "extern \"C\" __global__ __launch_bounds__(" << c.threads << ") void " << c.name << sig
               << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.BK << ", " << c.ST << ", " << c.WM << ", "
               << c.WN << ", " << c.SK << ", " << c.GM << ", " << c.SWZ << ", " << out << ", " << c.DMA << ", "
-              << c.TAILS << ", " << c.ROUND << ", " << c.E << ">(X, W, Y, ws, M); }\n";
+              << c.TAILS << ", " << c.ROUND << ", " << c.E << ", " << c.BST << ">(X, W, Y, ws, M); }\n";
             if (c.TAILS > 1) {
                 s << "// " << c.reduce_name << ": tail tiles of " << c.name << ", " << c.TAILS
                   << " pieces each, rounds of " << c.ROUND << " workgroups\n";

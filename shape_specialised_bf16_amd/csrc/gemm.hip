@@ -108,7 +108,7 @@ __device__ __forceinline__ long xcd_remap(long pid0, long nblk)
 }  // namespace gemm_detail
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SK, int GROUP_M, int SWZ, int OUT, int DMA = 1,
-          int TAILS = 1, int ROUND = 0, int E = 0>
+          int TAILS = 1, int ROUND = 0, int E = 0, int BST = 0>
 __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* __restrict__ W,
                                           void* __restrict__ Y, float* __restrict__ ws, int M)
 {
@@ -137,16 +137,39 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     // step kt; otherwise that of tile kt+STAGES-1 at the start of step kt.
     constexpr bool EARLY = DMA && STAGES == 2;
     constexpr int LEAD = EARLY ? STAGES : STAGES - 1;   // tiles in flight after the prologue
-    static_assert((LEAD - 1) * PER_TILE <= 63, "younger copies fit the vmcnt counter");
+    // BST == 3: with two buffers, X (A) stays in two and W (B) gets a third
+    // buffer of its own, so each W copy is issued two k-tiles ahead of its use
+    // instead of one (the copies of W are the ones that miss the L2).
+    constexpr bool B3 = BST == 3;
+    static_assert(BST == 0 || (B3 && EARLY), "a third W buffer extends the two-buffer ring");
+    constexpr int LEAD_B = B3 ? 3 : LEAD;             // k-tiles of W in flight after the prologue
+    constexpr int PERIOD = B3 ? 6 : STAGES;           // ring positions before the buffer pattern repeats
+    // copies younger than the ones waited for: at the prologue (after tile 0),
+    // and in each step (after tile kt+1; with B3, W of tile kt+2 is issued
+    // after X of tile kt+1)
+    constexpr int WAIT0 = B3 ? IA + 2 * IB : (LEAD - 1) * PER_TILE;
+    constexpr int WAITK = B3 ? IB : (DMA ? (STAGES - 2) * PER_TILE : 0);
+    static_assert(WAIT0 <= 63, "younger copies fit the vmcnt counter");
     constexpr int STAGE = CA + CB;                    // 16-byte slots per buffer
     constexpr long TILES_N = N / BN;
     constexpr int KK = BK / 16;                       // MFMA k-steps per tile
 
-    __shared__ u32x4 lds0[STAGE];
-    __shared__ u32x4 lds1[STAGE];
-    __shared__ u32x4 lds2[STAGES > 2 ? STAGE : 1];
-    __shared__ u32x4 lds3[STAGES > 3 ? STAGE : 1];
+    // X and W of ring position s: one array per buffer holding both (X first),
+    // or with B3 two X arrays and three W arrays (5 x 32 KiB for 256 x 256 x 64)
+    __shared__ u32x4 lds0[B3 ? CA : STAGE];
+    __shared__ u32x4 lds1[B3 ? CA : STAGE];
+    __shared__ u32x4 lds2[B3 ? CB : (STAGES > 2 ? STAGE : 1)];
+    __shared__ u32x4 lds3[B3 ? CB : (STAGES > 3 ? STAGE : 1)];
+    __shared__ u32x4 lds4[B3 ? CB : 1];
     auto buf = [&](int s) -> u32x4* { return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : lds3; };
+    auto bufA = [&](int s) -> u32x4* {
+        if constexpr (B3) return s % 2 == 0 ? lds0 : lds1;
+        else return buf(s % STAGES);
+    };
+    auto bufB = [&](int s) -> u32x4* {
+        if constexpr (B3) return s % 3 == 0 ? lds2 : s % 3 == 1 ? lds3 : lds4;
+        else return buf(s % STAGES) + CA;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -249,17 +272,19 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
         if constexpr (WPACK) return (unsigned)(w_col((kbeg + kt * BK) / 8) * 16);
         else return (unsigned)(kt * BK * 2);
     };
-    auto issue = [&](u32x4* dst, long kt) {
+    auto issueA = [&](u32x4* dst, long kt) {
         const unsigned koff = (unsigned)(kt * BK * 2);
-        const unsigned kob = koffb(kt);
 #pragma unroll
         for (int i = 0; i < IA; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(dst + i * NTHR + wave * 64), 16, abyte[i],
                                                      koff, 0, 0);
+    };
+    auto issueB = [&](u32x4* dst, long kt) {
+        const unsigned kob = koffb(kt);
 #pragma unroll
         for (int i = 0; i < IB; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(dst + CA + i * NTHR + wave * 64), 16,
-                                                     bbyte[i], kob, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(dst + i * NTHR + wave * 64), 16, bbyte[i],
+                                                     kob, 0, 0);
     };
     u32x4 ra[DMA ? 1 : IA], rb[DMA ? 1 : IB];
     auto gload = [&](long kt) {
@@ -270,11 +295,11 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 #pragma unroll
         for (int i = 0; i < IB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b + bbyte[i]);
     };
-    auto lstore = [&](u32x4* dst) {
+    auto lstore = [&](u32x4* dA, u32x4* dB) {
 #pragma unroll
-        for (int i = 0; i < IA; ++i) dst[i * NTHR + tid] = ra[i];
+        for (int i = 0; i < IA; ++i) dA[i * NTHR + tid] = ra[i];
 #pragma unroll
-        for (int i = 0; i < IB; ++i) dst[CA + i * NTHR + tid] = rb[i];
+        for (int i = 0; i < IB; ++i) dB[i * NTHR + tid] = rb[i];
     };
     static_assert(DMA || STAGES == 2, "register-staged copies use two buffers");
 
@@ -293,7 +318,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
         return __builtin_bit_cast(bf16x8, p[i * 32 * CPR]);
     };
     auto frag_b = [&](const u32x4* b, int j, int kk) -> bf16x8 {
-        const u32x4* p = b + CA + rowb0 * CPR + ((kk * 2) ^ qb);
+        const u32x4* p = b + rowb0 * CPR + ((kk * 2) ^ qb);
         return __builtin_bit_cast(bf16x8, p[j * 32 * CPR]);
     };
 
@@ -317,11 +342,11 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     bf16x8 fa[2][TM], fb[2][TN];
     // W fragments first: the first MFMAs of a step then wait only for the reads
     // of their own operands, not for the whole set.
-    auto read_frags = [&](const u32x4* b, int kk, int slot) {
+    auto read_frags = [&](const u32x4* bA, const u32x4* bB, int kk, int slot) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[slot][j] = frag_b(b, j, kk);
+        for (int j = 0; j < TN; ++j) fb[slot][j] = frag_b(bB, j, kk);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[slot][i] = frag_a(b, i, kk);
+        for (int i = 0; i < TM; ++i) fa[slot][i] = frag_a(bA, i, kk);
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
@@ -342,53 +367,69 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
 
     auto kloop = [&](auto nkt) {
         constexpr long NKT = decltype(nkt)::value;
-        // prologue: tiles 0 .. LEAD-1 in flight, one per buffer (DMA), or tile 0
-        // in buffer 0; then tile 0 published and its first fragments read.
+        auto clamp = [&](long t) -> long { return t < NKT ? t : NKT - 1; };
+        // prologue: X of tiles 0 .. LEAD-1 and W of tiles 0 .. LEAD_B-1 in flight,
+        // in tile order (DMA), or tile 0 through registers; then tile 0
+        // published and its first fragments read.
         if constexpr (DMA) {
 #pragma unroll
-            for (int s = 0; s < LEAD; ++s) issue(buf(s), s < NKT ? s : NKT - 1);
+            for (int s = 0; s < LEAD_B; ++s) {
+                if (s < LEAD) issueA(bufA(s), clamp(s));
+                issueB(bufB(s), clamp(s));
+            }
         } else {
             gload(0);
-            lstore(lds0);
+            lstore(bufA(0), bufB(0));
         }
-        wait_vm_lds<DMA ? (LEAD - 1) * PER_TILE : 0>();
+        wait_vm_lds<DMA ? WAIT0 : 0>();
         barrier_lds();
-        read_frags(lds0, 0, 0);
-        // One k-tile kt in buffer b: the MFMAs of all but the last k step, then
-        // wait for this wave's copies of tile kt+1, barrier -- every wave has
-        // now read all of tile kt and written its part of tile kt+1 -- then the
-        // last k step's MFMAs beside the reads of tile kt+1's first fragments
-        // from buffer bn.  The copy of the next tile to fetch goes out right
-        // after that barrier into buffer b (EARLY: two buffers, so a copy gets
-        // a whole step between issue and wait) or at the start of the step into
-        // buffer bd, tile kt-1's (three or more buffers: already STAGES-1.75
-        // steps ahead).  Past the last tile the copy re-reads tile NKT-1 into
-        // the free buffer, so every step issues the same number of copies and
-        // the vmcnt bound stays exact without branches (branches here hide from
-        // the compiler which buffer a copy writes, and it then drains every copy
-        // before each LDS read).  With DMA == 0, tile kt+1 is loaded into
-        // registers before the MFMAs and written to buffer bn after them.
-        auto step = [&](u32x4* b, u32x4* bn, u32x4* bd, long kt) {
+        read_frags(bufA(0), bufB(0), 0, 0);
+        // One k-tile kt at ring position R: the MFMAs of all but the last k step,
+        // then wait for this wave's copies of tile kt+1, barrier -- every wave
+        // has now read all of tile kt and written its part of tile kt+1 -- then
+        // the last k step's MFMAs beside the reads of tile kt+1's first
+        // fragments.  The copies of the next tiles to fetch go out right after
+        // that barrier into tile kt's buffers (EARLY: X of tile kt+2, W of tile
+        // kt+LEAD_B, so a copy gets at least a whole step between issue and wait)
+        // or at the start of the step into tile kt-1's buffer (three or more
+        // buffers: already STAGES-1.75 steps ahead).  Past the last tile a copy
+        // re-reads tile NKT-1 into the free buffer, so every step issues the same
+        // number of copies and the vmcnt bound stays exact without branches
+        // (branches here hide from the compiler which buffer a copy writes, and
+        // it then drains every copy before each LDS read).  With DMA == 0, tile
+        // kt+1 is loaded into registers before the MFMAs and written to its
+        // buffers after them.
+        auto step = [&](auto r, long kt) {
+            constexpr int R = decltype(r)::value;
+            u32x4* bA = bufA(R);
+            u32x4* bB = bufB(R);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (!DMA) gload(kt + 1 < NKT ? kt + 1 : NKT - 1);
-            else if constexpr (!EARLY) issue(bd, kt + LEAD < NKT ? kt + LEAD : NKT - 1);
+            if constexpr (!DMA) {
+                gload(clamp(kt + 1));
+            } else if constexpr (!EARLY) {
+                issueA(bufA(R + STAGES - 1), clamp(kt + LEAD));
+                issueB(bufB(R + STAGES - 1), clamp(kt + LEAD));
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk + 1 < KK; ++kk) {
-                read_frags(b, kk + 1, (kk + 1) & 1);
+                read_frags(bA, bB, kk + 1, (kk + 1) & 1);
                 mfmas(kk & 1);
             }
 #pragma unroll
             for (int kk = 0; kk + 1 < KK; ++kk) interleave();
             if constexpr (!DMA) {
                 __builtin_amdgcn_sched_barrier(0);
-                lstore(bn);
+                lstore(bufA(R + 1), bufB(R + 1));
             }
             __builtin_amdgcn_sched_barrier(0);
-            wait_vm_lds<DMA ? (STAGES - 2) * PER_TILE : 0>();
+            wait_vm_lds<WAITK>();
             barrier_lds();
-            read_frags(bn, 0, 0);
-            if constexpr (EARLY) issue(b, kt + LEAD < NKT ? kt + LEAD : NKT - 1);
+            read_frags(bufA(R + 1), bufB(R + 1), 0, 0);
+            if constexpr (EARLY) {
+                issueA(bA, clamp(kt + LEAD));
+                issueB(bB, clamp(kt + LEAD_B));
+            }
             mfmas((KK - 1) & 1);
             // the reads first, then the MFMAs with any copies slotted between them
             __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
@@ -396,7 +437,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
                 constexpr int NMF = TM * TN;
                 constexpr int PAIRS = NMF < PER_TILE ? NMF : PER_TILE;
 #pragma unroll
-                for (int r = 0; r < PAIRS; ++r) {
+                for (int q = 0; q < PAIRS; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 }
@@ -406,20 +447,21 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
                 __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
             }
         };
-        auto ring = [&](auto r, long kt) {
-            constexpr int R = decltype(r)::value;
-            step(buf(R), buf((R + 1) % STAGES), buf((R + STAGES - 1) % STAGES), kt);
-        };
-        constexpr long KMAIN = NKT - NKT % STAGES;
-        for (long kt = 0; kt < KMAIN; kt += STAGES) {
-            ring(ic<0>{}, kt);
-            ring(ic<1>{}, kt + 1);
-            if constexpr (STAGES > 2) ring(ic<2>{}, kt + 2);
-            if constexpr (STAGES > 3) ring(ic<3>{}, kt + 3);
+        // PERIOD positions per pass (tile t at position t % PERIOD), then the rest
+        constexpr long KMAIN = NKT - NKT % PERIOD;
+        for (long kt = 0; kt < KMAIN; kt += PERIOD) {
+            step(ic<0>{}, kt);
+            step(ic<1>{}, kt + 1);
+            if constexpr (PERIOD > 2) step(ic<2>{}, kt + 2);
+            if constexpr (PERIOD > 3) step(ic<3>{}, kt + 3);
+            if constexpr (PERIOD > 4) step(ic<4>{}, kt + 4);
+            if constexpr (PERIOD > 5) step(ic<5>{}, kt + 5);
         }
-        if constexpr (NKT % STAGES > 0) ring(ic<0>{}, KMAIN);
-        if constexpr (NKT % STAGES > 1) ring(ic<1>{}, KMAIN + 1);
-        if constexpr (NKT % STAGES > 2) ring(ic<2>{}, KMAIN + 2);
+        if constexpr (NKT % PERIOD > 0) step(ic<0>{}, KMAIN);
+        if constexpr (NKT % PERIOD > 1) step(ic<1>{}, KMAIN + 1);
+        if constexpr (NKT % PERIOD > 2) step(ic<2>{}, KMAIN + 2);
+        if constexpr (NKT % PERIOD > 3) step(ic<3>{}, KMAIN + 3);
+        if constexpr (NKT % PERIOD > 4) step(ic<4>{}, KMAIN + 4);
         wait_vm_lds<0>();   // no copy may still write LDS when the block ends
     };
 

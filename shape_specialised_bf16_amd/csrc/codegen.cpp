@@ -145,12 +145,13 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     //      Each entry also lists the K-split factors of its split-tail variants
     //      (whole tiles for all full rounds of workgroups, the remaining tiles
     //      split along K so the last round is not mostly idle).
-    // BST = 3: a third buffer for W only (two-buffer tiles, W copies two k-tiles ahead)
+    // BST = ST + 1: one more LDS buffer for W than for X (W copies a k-tile further ahead)
     struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[2]; int BST = 0; };
     const GT gts[] = {
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2}},
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3},
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
+        {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}, 4},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},
         {128, 128, 64, 2, 2, 2, 1, 8, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
         {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 8, 8, 1, {}}};
@@ -159,7 +160,7 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         if (wpack && 64 % g.BK) continue;  // panel layout: a k-tile inside one 64-value block
         const int cpr = g.BK / 8, rpi = 64 * g.WM * g.WN / cpr;
         if ((rpi >> g.SWZ) % cpr) continue;  // the copy slots' swizzled column must not vary per copy
-        const int lds = (g.BST == 3 ? 2 * g.BM + 3 * g.BN : g.ST * (g.BM + g.BN)) * g.BK * 2;
+        const int lds = (g.BST ? g.ST * g.BM + g.BST * g.BN : g.ST * (g.BM + g.BN)) * g.BK * 2;
         if (lds > 160 * 1024) continue;   // the LDS of one workgroup
         const int per_cu = std::max(1, std::min(2, 160 * 1024 / lds));
         auto add = [&](int SK, int TL) {
@@ -172,7 +173,7 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
             c.threads = 64 * g.WM * g.WN;
             c.max_m = kMaxBlockRows;
             c.name = fmt("gemm_%dx%dx%d_st%d_w%dx%d_sw%d_g%d_sk%d%s%s", c.BM, c.BN, c.BK, c.ST, c.WM, c.WN, c.SWZ,
-                         c.GM, c.SK, c.DMA ? "" : "_reg", c.BST == 3 ? "_b3" : "");
+                         c.GM, c.SK, c.DMA ? "" : "_reg", c.BST ? fmt("_b%d", c.BST).c_str() : "");
             if (TL > 1) c.name += fmt("_tail%d_r%d", TL, c.ROUND);
             if (SK > 1) c.reduce_name = fmt("splitk_reduce_sk%d", SK);
             if (TL > 1) c.reduce_name = c.name + "_reduce";

@@ -75,6 +75,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <long V> struct ic { static constexpr long value = V; };
 
+// f(ic<I>{}, kt0 + I) for I = FROM .. TO-1, unrolled at compile time.
+template <long FROM, long TO, typename F>
+__device__ __forceinline__ void unroll_steps(F&& f, long kt0)
+{
+    if constexpr (FROM < TO) {
+        f(ic<FROM>{}, kt0 + FROM);
+        unroll_steps<FROM + 1, TO>(f, kt0);
+    }
+}
+
 // Whole tiles and split tail tiles of a launch: T tiles, ROUND workgroups at
 // once.  With T >= ROUND the tail is T % ROUND tiles; below one round every
 // tile is a tail tile.  (The host computes the same split for the launch.)
@@ -137,38 +147,48 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     // step kt; otherwise that of tile kt+STAGES-1 at the start of step kt.
     constexpr bool EARLY = DMA && STAGES == 2;
     constexpr int LEAD = EARLY ? STAGES : STAGES - 1;   // tiles in flight after the prologue
-    // BST == 3: with two buffers, X (A) stays in two and W (B) gets a third
-    // buffer of its own, so each W copy is issued two k-tiles ahead of its use
-    // instead of one (the copies of W are the ones that miss the L2).
-    constexpr bool B3 = BST == 3;
-    static_assert(BST == 0 || (B3 && EARLY), "a third W buffer extends the two-buffer ring");
-    constexpr int LEAD_B = B3 ? 3 : LEAD;             // k-tiles of W in flight after the prologue
-    constexpr int PERIOD = B3 ? 6 : STAGES;           // ring positions before the buffer pattern repeats
+    // BST == STAGES + 1: X (A) keeps STAGES buffers and W (B) gets one more of
+    // its own, so each W copy is issued one k-tile further ahead of its use
+    // (the copies of W are the ones that miss the L2).  BST == 0: X and W of a
+    // k-tile share one buffer.
+    constexpr bool SPLIT = BST != 0;
+    static_assert(BST == 0 || (DMA && BST == STAGES + 1), "one extra W buffer on the global->LDS ring");
+    constexpr int NB = SPLIT ? BST : STAGES;          // W buffers
+    constexpr int LEAD_B = SPLIT ? LEAD + 1 : LEAD;   // k-tiles of W in flight after the prologue
+    constexpr int PERIOD = STAGES * (SPLIT ? BST : 1);  // ring positions before the buffer pattern repeats
     // copies younger than the ones waited for: at the prologue (after tile 0),
-    // and in each step (after tile kt+1; with B3, W of tile kt+2 is issued
-    // after X of tile kt+1)
-    constexpr int WAIT0 = B3 ? IA + 2 * IB : (LEAD - 1) * PER_TILE;
-    constexpr int WAITK = B3 ? IB : (DMA ? (STAGES - 2) * PER_TILE : 0);
-    static_assert(WAIT0 <= 63, "younger copies fit the vmcnt counter");
+    // and in each step (after tile kt+1: with SPLIT, W of tile kt+2 goes out
+    // right after X of tile kt+1)
+    constexpr int WAIT0 = (LEAD - 1) * IA + (LEAD_B - 1) * IB;
+    constexpr int WAITK = (SPLIT ? IB : 0) + (DMA && !EARLY ? (STAGES - 2) * PER_TILE : 0);
+    static_assert(WAIT0 <= 63 && WAITK <= 63, "younger copies fit the vmcnt counter");
     constexpr int STAGE = CA + CB;                    // 16-byte slots per buffer
     constexpr long TILES_N = N / BN;
     constexpr int KK = BK / 16;                       // MFMA k-steps per tile
 
     // X and W of ring position s: one array per buffer holding both (X first),
-    // or with B3 two X arrays and three W arrays (5 x 32 KiB for 256 x 256 x 64)
-    __shared__ u32x4 lds0[B3 ? CA : STAGE];
-    __shared__ u32x4 lds1[B3 ? CA : STAGE];
-    __shared__ u32x4 lds2[B3 ? CB : (STAGES > 2 ? STAGE : 1)];
-    __shared__ u32x4 lds3[B3 ? CB : (STAGES > 3 ? STAGE : 1)];
-    __shared__ u32x4 lds4[B3 ? CB : 1];
+    // or with SPLIT STAGES arrays of X and STAGES+1 of W (each buffer its own
+    // array in either case; 5 x 32 KiB for 256x256x64 over two buffers, 3 x 32
+    // + 4 x 16 KiB for 256x128x64 over three)
+    constexpr int SZ = SPLIT ? CA : STAGE;
+    __shared__ u32x4 lds0[SZ];
+    __shared__ u32x4 lds1[SZ];
+    __shared__ u32x4 lds2[STAGES > 2 ? SZ : 1];
+    __shared__ u32x4 lds3[STAGES > 3 ? SZ : 1];
+    __shared__ u32x4 ldsb0[SPLIT ? CB : 1];
+    __shared__ u32x4 ldsb1[SPLIT ? CB : 1];
+    __shared__ u32x4 ldsb2[SPLIT ? CB : 1];
+    __shared__ u32x4 ldsb3[SPLIT && BST > 3 ? CB : 1];
+    __shared__ u32x4 ldsb4[SPLIT && BST > 4 ? CB : 1];
     auto buf = [&](int s) -> u32x4* { return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : lds3; };
-    auto bufA = [&](int s) -> u32x4* {
-        if constexpr (B3) return s % 2 == 0 ? lds0 : lds1;
-        else return buf(s % STAGES);
-    };
+    auto bufA = [&](int s) -> u32x4* { return buf(s % STAGES); };
     auto bufB = [&](int s) -> u32x4* {
-        if constexpr (B3) return s % 3 == 0 ? lds2 : s % 3 == 1 ? lds3 : lds4;
-        else return buf(s % STAGES) + CA;
+        if constexpr (SPLIT) {
+            const int t = s % NB;
+            return t == 0 ? ldsb0 : t == 1 ? ldsb1 : t == 2 ? ldsb2 : t == 3 ? ldsb3 : ldsb4;
+        } else {
+            return buf(s % STAGES) + CA;
+        }
     };
 
     const int tid = threadIdx.x;
@@ -408,7 +428,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
                 gload(clamp(kt + 1));
             } else if constexpr (!EARLY) {
                 issueA(bufA(R + STAGES - 1), clamp(kt + LEAD));
-                issueB(bufB(R + STAGES - 1), clamp(kt + LEAD));
+                issueB(bufB(R + NB - 1), clamp(kt + LEAD_B));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -449,19 +469,8 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
         };
         // PERIOD positions per pass (tile t at position t % PERIOD), then the rest
         constexpr long KMAIN = NKT - NKT % PERIOD;
-        for (long kt = 0; kt < KMAIN; kt += PERIOD) {
-            step(ic<0>{}, kt);
-            step(ic<1>{}, kt + 1);
-            if constexpr (PERIOD > 2) step(ic<2>{}, kt + 2);
-            if constexpr (PERIOD > 3) step(ic<3>{}, kt + 3);
-            if constexpr (PERIOD > 4) step(ic<4>{}, kt + 4);
-            if constexpr (PERIOD > 5) step(ic<5>{}, kt + 5);
-        }
-        if constexpr (NKT % PERIOD > 0) step(ic<0>{}, KMAIN);
-        if constexpr (NKT % PERIOD > 1) step(ic<1>{}, KMAIN + 1);
-        if constexpr (NKT % PERIOD > 2) step(ic<2>{}, KMAIN + 2);
-        if constexpr (NKT % PERIOD > 3) step(ic<3>{}, KMAIN + 3);
-        if constexpr (NKT % PERIOD > 4) step(ic<4>{}, KMAIN + 4);
+        for (long kt = 0; kt < KMAIN; kt += PERIOD) unroll_steps<0, PERIOD>(step, kt);
+        unroll_steps<0, NKT % PERIOD>(step, KMAIN);
         wait_vm_lds<0>();   // no copy may still write LDS when the block ends
     };
 

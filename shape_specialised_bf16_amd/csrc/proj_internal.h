@@ -36,7 +36,7 @@ struct Candidate {
     // tile-row group, LDS swizzle period
     int BM = 0, BN = 0, BK = 64, ST = 2, WM = 0, WN = 0, SK = 1, GM = 8, SWZ = 0;
     int DMA = 1;  // 1: global->LDS copies; 0: copies staged through registers
-    int BST = 0;  // 3: W in three LDS buffers, X in two (two-buffer tiles only)
+    int BST = 0;  // ST + 1: W in one LDS buffer more than X (0: X and W share each buffer)
     int TAILS = 1;   // >1: whole tiles plus a tail split TAILS ways along K
     int ROUND = 0;   // workgroups the device runs at once (CU count x blocks per CU)
 

@@ -1,10 +1,12 @@
 """Summaries of rocprofv3 output for the projection kernels.
 
-    python -m shape_specialised_bf16_amd.profile_summary stats <dir-or-db> [--match S] [--stream last]
+    python -m shape_specialised_bf16_amd.profile_summary stats <dir-or-db> [--match S] [--stream last] [--last N]
         per-kernel dispatch count and mean/min/max duration (us) from a
         ``--kernel-trace`` run (rocpd ``*_results.db`` or ``*_kernel_trace.csv``);
         ``--stream last`` keeps only the stream of the last dispatch (the timed
-        loop), dropping the load-time tuner's launches.
+        loop), dropping the load-time tuner's launches; ``--last N`` adds the mean
+        of each kernel's last N dispatches (a benchmark's timed rounds come after
+        its warm-up launches of the same kernel).
 
     python -m shape_specialised_bf16_amd.profile_summary traffic --fetch <dir> --write <dir>
             --kernel NAME --calib NAME --calib-bytes B [--out profiles/traffic.json --key KEY]
@@ -59,7 +61,7 @@ def _dispatches(path: str):
     return sorted(out, key=lambda t: t[2])
 
 
-def stats(path: str, match: str = "", stream: str = "all"):
+def stats(path: str, match: str = "", stream: str = "all", last: int = 0):
     rows = _dispatches(path)
     if stream == "last" and rows:
         s = rows[-1][1]
@@ -72,7 +74,7 @@ def stats(path: str, match: str = "", stream: str = "all"):
     out = []
     for (name, grid), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         out.append(dict(kernel=name, grid=grid, calls=len(d), mean_us=statistics.mean(d), min_us=min(d),
-                        max_us=max(d), total_us=sum(d)))
+                        max_us=max(d), total_us=sum(d), last_mean_us=statistics.mean(d[-last:]) if last else None))
     return out
 
 
@@ -129,6 +131,7 @@ def main(argv=None):
     s.add_argument("path")
     s.add_argument("--match", default="")
     s.add_argument("--stream", default="all", choices=["all", "last"])
+    s.add_argument("--last", type=int, default=0, help="also the mean of each kernel's last N dispatches")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -140,9 +143,10 @@ def main(argv=None):
     t.add_argument("--last", type=int, default=5, help="dispatches of the kernel to use, counted from the end")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        for r in stats(a.path, a.match, a.stream):
+        for r in stats(a.path, a.match, a.stream, a.last):
+            tail = f"  last{a.last} {r['last_mean_us']:9.3f}" if a.last else ""
             print(f"{r['kernel'][:48]:48s} grid {r['grid']:10d} calls {r['calls']:5d}  mean {r['mean_us']:9.3f} us  "
-                  f"min {r['min_us']:10.3f}  max {r['max_us']:10.3f}  total {r['total_us']:12.1f}")
+                  f"min {r['min_us']:10.3f}  max {r['max_us']:10.3f}  total {r['total_us']:12.1f}{tail}")
     else:
         r = traffic(a.fetch, a.write, a.kernel, a.calib, a.calib_bytes, a.last)
         r["source_sha"] = kernel_source_sha(a.kernel)

@@ -133,7 +133,7 @@ def test_swiglu_module_constants_and_families():
         gemm_mfma<BM, BN, BK, ST, WM, WN, SK, GM, SWZ, OUT, DMA, TAILS, ROUND, E, BST>, gemm_plain<OUT, E>)."""
         kernel, args = re.match(r"(\w+)<([^>]*)>", call).groups()
         args = [a.strip() for a in args.split(",")]
-        return {"gemv_valu": args[8], "gemm_mfma": args[13], "gemm_plain": args[1]}.get(kernel)
+        return args[{"gemv_valu": 8, "gemm_mfma": 13, "gemm_plain": 1}[kernel]]
 
     for n in fused:
         assert epilogue_arg(wrappers[n]) == "1", (n, wrappers[n])

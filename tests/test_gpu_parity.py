@@ -212,3 +212,31 @@ def test_degenerate_shapes(N, K, dtype):
         M = min(p.candidate_max_m(idx), 17)
         got = G.host(p.run_candidate(idx, G.dev(Xi[:M]), G.dev(Wi)))
         assert np.array_equal(got.view(np.uint8), want[:M].view(np.uint8)), f"{N}x{K} {name}"
+
+
+# ------------------------------------------------------------------ seeded random shapes
+def _random_shapes(n=12, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 3001))
+        K = 8 * int(rng.integers(1, 376))
+        out.append((N, K, "bf16" if i % 2 else "f32", int(rng.integers(1, 301))))
+    return out
+
+
+@pytest.mark.parametrize("N,K,dtype,M", _random_shapes())
+def test_random_shapes_against_oracle(N, K, dtype, M):
+    """Shapes drawn from a seeded generator (N in [1, 3000], K any multiple of 8
+    up to 3000, both output types, ragged M): plan creation succeeds, the tuned
+    path matches the oracle at M = 1, 16 and the drawn M, and nothing is written
+    past M."""
+    W = synth.normal_bf16(68, N * 7 + K, (N, K), 0.05)
+    p = G.plan(N, K, dtype)
+    pat = 0x7FC1 if dtype == "bf16" else 0x7FC00001
+    for m in sorted({1, 16, M}):
+        X = synth.normal_bf16(69, m + N, (m, K), 1.0)
+        Y = G.empty_out(m, N, dtype, extra_rows=1)
+        p.run(G.dev(X), G.dev(W), Y)
+        G.check_against_oracle(Y, X, W, dtype, label=f"random {N}x{K} {p.choice(m)}")
+        assert np.all(G.host(Y)[m:].view(np.uint16 if dtype == "bf16" else np.uint32) == pat), "row M was written"

@@ -88,7 +88,10 @@ enum {
  * candidates, and tunes afresh any bucket whose cached choice is unknown or
  * fails the gate (the cache the pages propose, and doubt because machine state
  * drifts: "#004 the same compiler on Apple's chips", section "Reproducing at
- * home").  proj_plan_describe reports "cache": off, miss, hit or stale.
+ * home").  The compiled module is kept under the same key (<dir>/proj-<key>.co,
+ * the key also covering the compile options), so such a plan skips hipRTC as
+ * well; a file that does not load is compiled afresh and replaced.
+ * proj_plan_describe reports "cache" and "code_cache": off, miss, hit or stale.
  */
 proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
 

@@ -94,7 +94,8 @@ static std::string describe(const proj_plan* p)
       << "\", \"arch\": \"" << p->arch << "\", \"device\": " << p->device << ", \"compile_s\": " << p->compile_s
       << ", \"tune_s\": " << p->tune_s << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
       << ", \"swiglu_intermediate_rows\": " << p->gu_rows
-      << ", \"cache\": \"" << p->cache << "\", \"cache_path\": \"" << json_escape(p->cache_path) << "\""
+      << ", \"cache\": \"" << p->cache << "\", \"code_cache\": \"" << p->code_cache << "\", \"cache_path\": \""
+      << json_escape(p->cache_path) << "\""
       << ",\n \"candidates\": [";
     for (size_t i = 0; i < p->cands.size(); ++i) s << (i ? ", " : "") << "\"" << p->cands[i].name << "\"";
     s << "],\n \"buckets\": [";

@@ -23,6 +23,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
+#include <iterator>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -92,6 +93,7 @@ int compile_source(const std::string& src, const std::string& arch, const char* 
     // -packed-fp32-ops: no packed f32 ALU instructions in any kernel.
     const char* opts[] = {arch_opt.c_str(), "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
                           "-packed-fp32-ops"};
+    static_assert(sizeof opts / sizeof opts[0] == 7, "keep kCompileOptions in step with the options");
     hiprtcResult r = hiprtcCompileProgram(prog, (int)(sizeof opts / sizeof opts[0]), opts);
     if (r != HIPRTC_SUCCESS) {
         size_t ls = 0;
@@ -556,6 +558,22 @@ static uint64_t fnv1a(uint64_t h, const std::string& s)
     return h;
 }
 
+// Whether buf holds a whole ELF64 image: the magic, and the program and section
+// header tables inside the buffer.  (hipModuleLoadData takes no size, so a
+// truncated or foreign cache file must not reach it.)
+static bool whole_elf64(const std::vector<char>& buf)
+{
+    if (buf.size() < 64 || memcmp(buf.data(), "\x7f" "ELF", 4) != 0 || buf[4] != 2) return false;
+    auto u64 = [&](size_t o) { uint64_t v; memcpy(&v, buf.data() + o, 8); return v; };
+    auto u16 = [&](size_t o) { uint16_t v; memcpy(&v, buf.data() + o, 2); return (uint64_t)v; };
+    const uint64_t n = buf.size();
+    const uint64_t ph = u64(32), sh = u64(40), phe = u16(54), phn = u16(56), she = u16(58), shn = u16(60);
+    return ph <= n && phe * phn <= n - ph && sh <= n && she * shn <= n - sh;
+}
+
+// The hipRTC options of compile_source, as text: part of the cache key.
+static const char* const kCompileOptions = "-O3 -std=c++17 -Xclang -target-feature -Xclang -packed-fp32-ops";
+
 static int cache_key(proj_plan* p, const std::string& src)
 {
     hipDeviceProp_t prop;
@@ -564,8 +582,8 @@ static int cache_key(proj_plan* p, const std::string& src)
     HIP_TRY(hipRuntimeGetVersion(&rt));
     HIP_TRY(hipDriverGetVersion(&drv));
     char head[512];
-    snprintf(head, sizeof head, "%s|cus=%d|runtime=%d|driver=%d|", prop.gcnArchName, prop.multiProcessorCount, rt,
-             drv);
+    snprintf(head, sizeof head, "%s|cus=%d|runtime=%d|driver=%d|options=%s|", prop.gcnArchName,
+             prop.multiProcessorCount, rt, drv, kCompileOptions);
     p->key = fnv1a(fnv1a(0xcbf29ce484222325ull, head), src);
     return PROJ_OK;
 }
@@ -841,7 +859,50 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
     char name[96];
     snprintf(name, sizeof name, "proj_%lldx%lld_%s%s%s%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32",
              epi ? "_swiglu" : "", p->pro ? "_rmsnorm" : "", p->wpack ? "_panels" : "");
-    if ((rc = compile_source(src, p->arch, name, &code))) return rc;
+    // With PROJ_CACHE_DIR, the compiled module is kept beside the tuned choices
+    // under the same key (device, runtime and driver versions, compile options,
+    // emitted source): a later plan of the same key loads it instead of
+    // compiling.  A file that does not load is compiled afresh and replaced.
+    std::string co_path;
+    if (const char* dir = getenv("PROJ_CACHE_DIR")) {
+        if (*dir) {
+            char file[64];
+            snprintf(file, sizeof file, "/proj-%016llx.co", (unsigned long long)p->key);
+            co_path = std::string(dir) + file;
+        }
+    }
+    p->code_cache = co_path.empty() ? "off" : "miss";
+    if (!co_path.empty()) {
+        std::ifstream f(co_path, std::ios::binary);
+        if (f) {
+            auto buf = std::make_shared<std::vector<char>>((std::istreambuf_iterator<char>(f)),
+                                                            std::istreambuf_iterator<char>());
+            if (whole_elf64(*buf) && hipModuleLoadData(&p->module, buf->data()) == hipSuccess) {
+                code = buf;
+                p->code_cache = "hit";
+            } else {
+                (void)hipGetLastError();
+                p->module = nullptr;
+                p->code_cache = "stale";
+            }
+        }
+    }
+    // write the compiled module to the cache file (a temporary file renamed
+    // into place, so readers never see a partial one)
+    auto store_code = [&]() {
+        if (co_path.empty()) return;
+        const std::string tmp = co_path + ".tmp";
+        bool ok = false;
+        {
+            std::ofstream f(tmp, std::ios::binary);
+            ok = f && f.write(code->data(), code->size());
+        }
+        if (!ok || std::rename(tmp.c_str(), co_path.c_str()) != 0) std::remove(tmp.c_str());
+    };
+    if (!code) {
+        if ((rc = compile_source(src, p->arch, name, &code))) return rc;
+        store_code();
+    }
     p->compile_s = now_s() - t0;
     p->code_bytes = code->size();
     if (const char* dir = getenv("PROJ_DUMP_DIR")) {
@@ -851,22 +912,41 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
             std::ofstream(base + "." + p->arch + ".co", std::ios::binary).write(code->data(), code->size());
         }
     }
-    HIP_TRY(hipModuleLoadData(&p->module, code->data()));
-    HIP_TRY(hipModuleGetFunction(&p->f_pack, p->module, "proj_pack_panels"));
+    if (!p->module) HIP_TRY(hipModuleLoadData(&p->module, code->data()));
+    // every kernel the plan launches, from the loaded module
+    auto bind = [&]() -> int {
+        HIP_TRY(hipModuleGetFunction(&p->f_pack, p->module, "proj_pack_panels"));
+        if (p->pro) HIP_TRY(hipModuleGetFunction(&p->f_norm, p->module, "proj_rmsnorm_rows"));
+        for (Candidate& c : p->cands) {
+            HIP_TRY(hipModuleGetFunction(&c.fn, p->module, c.name.c_str()));
+            if (!c.reduce_name.empty())
+                HIP_TRY(hipModuleGetFunction(&c.reduce_fn, p->module, c.reduce_name.c_str()));
+        }
+        return PROJ_OK;
+    };
+    if ((rc = bind())) {
+        if (p->code_cache != "hit") return rc;
+        // a cached module that lacks a kernel: compile afresh and replace the file
+        (void)hipGetLastError();
+        (void)hipModuleUnload(p->module);
+        p->module = nullptr;
+        p->code_cache = "stale";
+        if ((rc = compile_source(src, p->arch, name, &code))) return rc;
+        store_code();
+        p->code_bytes = code->size();
+        HIP_TRY(hipModuleLoadData(&p->module, code->data()));
+        if ((rc = bind())) return rc;
+    }
     if (p->pro) {
-        HIP_TRY(hipModuleGetFunction(&p->f_norm, p->module, "proj_rmsnorm_rows"));
         if (hipMalloc(&p->xn, (size_t)kMaxBlockRows * K * 2) != hipSuccess) {
             p->xn = nullptr;
             return set_error(PROJ_ENOMEM, "RMSNorm workspace of %lld bytes", (long long)kMaxBlockRows * K * 2);
         }
     }
-    for (Candidate& c : p->cands) {
-        HIP_TRY(hipModuleGetFunction(&c.fn, p->module, c.name.c_str()));
-        if (!c.reduce_name.empty()) HIP_TRY(hipModuleGetFunction(&c.reduce_fn, p->module, c.reduce_name.c_str()));
-    }
     char line[256];
-    snprintf(line, sizeof line, "[proj] %lldx%lld %s: %zu candidates compiled for %s in %.2f s (%zu bytes)",
-             (long long)N, (long long)K, dtype ? "bf16" : "f32", p->cands.size(), p->arch.c_str(), p->compile_s,
+    snprintf(line, sizeof line, "[proj] %lldx%lld %s: %zu candidates %s for %s in %.2f s (%zu bytes)",
+             (long long)N, (long long)K, dtype ? "bf16" : "f32", p->cands.size(),
+             p->code_cache == "hit" ? "loaded from the code cache" : "compiled", p->arch.c_str(), p->compile_s,
              p->code_bytes);
     plog(p.get(), line);
     if ((rc = tune_plan(p.get()))) return rc;

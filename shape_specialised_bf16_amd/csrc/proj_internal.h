@@ -126,6 +126,7 @@ struct proj_plan {
     hipFunction_t f_norm = nullptr;  // the module's separate norm kernel (proj_rmsnorm_rows)
     uint64_t key = 0;   // tuning-cache key: device, runtime and driver versions, emitted source
     std::string cache;  // tuning cache: "off", "miss", "hit", "stale" (a cached choice failed the gate)
+    std::string code_cache;  // compiled-module cache: "off", "miss", "hit", "stale" (the file did not load)
     std::string cache_path;
     int64_t NO = 0;     // columns of Y: N, or N/2 with the SwiGLU epilogue
     int device = -1;

@@ -48,3 +48,41 @@ def test_cache_miss_hit_and_stale(tmp_path, monkeypatch):
     # a different output type is a different key
     other = Plan(N, K, "bf16").describe()
     assert other["cache"] == "miss" and other["cache_path"] != path
+
+
+def test_compiled_module_cache(tmp_path, monkeypatch):
+    """With PROJ_CACHE_DIR the compiled module is kept under the plan's key: the
+    next plan of that key loads it instead of compiling; a file that is not a
+    loadable module is reported stale, compiled afresh and replaced; the plan
+    computes the same result either way."""
+    import numpy as np
+    import oracle
+    import synth
+    from shape_specialised_bf16_amd import Plan
+    N, K = 1024, 2048
+    W = synth.normal_bf16(120, 0, (N, K), 0.02)
+    X = synth.normal_bf16(120, 1, (37, K), 1.0)
+
+    def run(p):
+        Y = p.run(G.dev(X), G.dev(W))
+        G.check_against_oracle(Y, X, W, "f32", label=f"cached module {p.choice(37)}")
+        return G.host(Y)
+
+    monkeypatch.delenv("PROJ_CACHE_DIR", raising=False)
+    assert Plan(N, K, "f32").describe()["code_cache"] == "off"
+    monkeypatch.setenv("PROJ_CACHE_DIR", str(tmp_path))
+    p1 = Plan(N, K, "f32")
+    d1 = p1.describe()
+    assert d1["code_cache"] == "miss"
+    co = d1["cache_path"][:-len(".txt")] + ".co"
+    assert os.path.getsize(co) == d1["code_bytes"]
+    y1 = run(p1)
+    p2 = Plan(N, K, "f32")
+    assert p2.describe()["code_cache"] == "hit"
+    assert np.array_equal(run(p2).view(np.uint32), y1.view(np.uint32))
+    open(co, "wb").write(b"not a code object")
+    p3 = Plan(N, K, "f32")
+    assert p3.describe()["code_cache"] == "stale"
+    assert os.path.getsize(co) == d1["code_bytes"], "the stale file was not replaced"
+    assert np.array_equal(run(p3).view(np.uint32), y1.view(np.uint32))
+    G.log(f"  code cache: miss {d1['compile_s']:.2f} s, then hit and stale handled")

@@ -228,7 +228,7 @@ static float bf16_to_f(uint16_t b) { return bits_f((uint32_t)b << 16); }
 struct Tuner {
     proj_plan* p;
     hipStream_t st = nullptr;
-    hipFunction_t f_fill_probe = nullptr, f_fill_u32 = nullptr, f_ref = nullptr, f_ref_epi = nullptr,
+    hipFunction_t f_fill_probe = nullptr, f_fill_u32 = nullptr, f_ref = nullptr,
                   f_check = nullptr, f_probe = nullptr;
     void *Xr = nullptr, *Xi = nullptr, *Wr = nullptr, *Wi = nullptr, *Y = nullptr;
     // the weights as the candidates read them: Wr and Wi themselves, or their
@@ -299,7 +299,6 @@ struct Tuner {
         HIP_TRY(hipModuleGetFunction(&f_fill_probe, p->module, "proj_fill_probe"));
         HIP_TRY(hipModuleGetFunction(&f_fill_u32, p->module, "proj_fill_u32"));
         HIP_TRY(hipModuleGetFunction(&f_ref, p->module, "proj_ref_rows"));
-        HIP_TRY(hipModuleGetFunction(&f_ref_epi, p->module, "proj_ref_epilogue"));
         HIP_TRY(hipModuleGetFunction(&f_probe, p->module, "proj_probe_read"));
         HIP_TRY(hipModuleGetFunction(&f_check, p->module,
                                      p->dtype == PROJ_OUT_BF16 ? "proj_check_bf16" : "proj_check_f32"));
@@ -405,22 +404,6 @@ struct Tuner {
             int* rd = rows_d;
             void* args[] = {&x, &w, &rd, &nr, &r};
             HIP_TRY(hipModuleLaunchKernel(f_ref, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
-        }
-        HIP_TRY(hipStreamSynchronize(st));
-        return PROJ_OK;
-    }
-
-    // The plan's epilogue applied to the reference rows of both probes (after the
-    // self-check, which compares the plain sums).
-    int reference_epilogue(int nrows)
-    {
-        if (!p->epi) return PROJ_OK;
-        unsigned gx = (unsigned)std::min<int64_t>((nrows * p->NO + 255) / 256, 4096);
-        for (int pass = 0; pass < 2; ++pass) {
-            float* r = pass ? ref_i : ref_r;
-            int nr = nrows;
-            void* args[] = {&r, &nr};
-            HIP_TRY(hipModuleLaunchKernel(f_ref_epi, gx, 1, 1, 256, 1, 1, 0, st, args, nullptr));
         }
         HIP_TRY(hipStreamSynchronize(st));
         return PROJ_OK;
@@ -698,7 +681,6 @@ int tune_plan(proj_plan* p)
         }
         const int nrows = (int)rows.size();
         if ((rc = T.reference_norm(rows))) return rc;
-        if ((rc = T.reference_epilogue(nrows))) return rc;
 
         std::vector<int> ok;
         auto validate = [&](int ci) -> int {

@@ -162,3 +162,18 @@ def test_tuner_measures_fused_against_unfused():
         assert b["choice"] in t
         G.log(f"  bucket {b['lo']}..{b['hi']}: best fused {min(fused, key=t.get)} {min(t[n] for n in fused):.2f} us, "
               f"best unfused {min(unfused, key=t.get)} {min(t[n] for n in unfused):.2f} us -> {b['choice']}")
+
+
+@pytest.mark.parametrize("N,K,dtype", [(18432, 2560, "bf16"), (6144, 1024, "f32")])
+def test_gate_rejects_no_candidate(N, K, dtype):
+    """Every candidate computes the same SwiGLU up to the order of its sums, so
+    the load-time gate must pass them all: a rejection here means the gate's
+    allowance is tighter than the rounding the method permits (one bf16 ulp of
+    a gate sum moves silu(g)*u by more than one ulp of the output), which
+    would push whole row buckets onto the slow last-resort kernel."""
+    plan = G.plan(N, K, dtype, epilogue="swiglu")
+    d = plan.describe()
+    for b in d["buckets"]:
+        assert b["rejected"] == [], (b["lo"], b["hi"], b["rejected"])
+        assert b["choice"] != "gemm_plain", (b["lo"], b["hi"])
+        G.log(f"  {N}x{K} {dtype} bucket {b['lo']}..{b['hi']}: {len(b['timings_us'])} timed, -> {b['choice']}")

@@ -145,7 +145,9 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     //      Each entry also lists the K-split factors of its split-tail variants
     //      (whole tiles for all full rounds of workgroups, the remaining tiles
     //      split along K so the last round is not mostly idle).
-    // BST = ST + 1: one more LDS buffer for W than for X (W copies a k-tile further ahead)
+    // BST = ST + 1: one more LDS buffer for W than for X (W copies a k-tile further ahead).
+    // At a few hundred rows the GEMM streams W from HBM much as the GEMV does, and
+    // a 128 x 128 tile with four W buffers keeps more of it in flight per CU.
     struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[2]; int BST = 0; };
     const GT gts[] = {
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2}},
@@ -154,6 +156,7 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}, 4},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},
         {128, 128, 64, 2, 2, 2, 1, 8, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
+        {128, 128, 64, 3, 2, 2, 1, 8, 8, 1, {2, 4}, 4},
         {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 8, 8, 1, {}}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;

@@ -731,7 +731,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-prompt and 27B-layer legs")
-    ap.add_argument("--prefill-m", type=int, default=2048, choices=[512, 2048],
+    ap.add_argument("--prefill-m", type=int, default=2048, choices=[128, 512, 2048],
                     help="row count of the prefill GEMM in --mode profile-prefill")
     ap.add_argument("--mode", default="full", choices=["full", "profile-decode", "profile-prefill"],
                     help="profile-*: only that leg's dominant kernel and a calibration copy, for rocprofv3 "

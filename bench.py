@@ -122,9 +122,9 @@ def profile_mode(which: str, prefill_m: int = 2048, launches: int = 30):
     from shape_specialised_bf16_amd import Plan
 
     if which == "decode":
-        cfg, pi, M, dt = synth.CONFIGS[1], len(synth.CONFIGS[1].projections) - 1, 1, "f32"
+        cfg, pi, M, dt = synth.workload("decode_0.8b_layer_m1"), len(synth.workload("decode_0.8b_layer_m1").projections) - 1, 1, "f32"
     else:
-        cfg, pi, M, dt = synth.CONFIGS[2], 2, prefill_m, "bf16"
+        cfg, pi, M, dt = synth.workload("prefill_4b_layer"), 2, prefill_m, "bf16"
     p = cfg.projections[pi]
     plan = Plan(p.N, p.K, dt)
     W = upload(synth.weights(cfg, pi))
@@ -154,7 +154,7 @@ def time_decode(steps: int, warmup: int):
     import synth
     from shape_specialised_bf16_amd import Plan
 
-    cfg = synth.CONFIGS[1]
+    cfg = synth.workload("decode_0.8b_layer_m1")
     projs = cfg.projections
     log(f"decode workload {cfg.name}: " + ", ".join(f"{p.name} {p.K}->{p.N}" for p in projs))
     plans, Ws, Xs, Ys, host = [], [], [], [], []
@@ -254,7 +254,7 @@ def time_prefill(reps: int = 20):
     import synth
     from shape_specialised_bf16_amd import Plan
 
-    cfg = synth.CONFIGS[2]
+    cfg = synth.workload("prefill_4b_layer")
     out = {}
     plans = [Plan(p.N, p.K, "bf16") for p in cfg.projections]
     Wh = [synth.weights(cfg, i) for i in range(len(cfg.projections))]
@@ -323,7 +323,7 @@ def time_long_prompt(reps: int = 5):
     import synth
     from shape_specialised_bf16_amd import Plan
 
-    cfg = synth.CONFIGS[3]
+    cfg = synth.workload("long_prompt_4b_8192x1024")
     rows_total, block = cfg.extra["prompt_rows"], cfg.extra["block"]
     layer = [p for p in cfg.projections if p.name != "head"]
     head = [p for p in cfg.projections if p.name == "head"][0]
@@ -373,7 +373,7 @@ def time_27b(steps: int = 500, reps: int = 5):
     import synth
     from shape_specialised_bf16_amd import Plan
 
-    cfg = synth.CONFIGS[4]
+    cfg = synth.workload("layer_27b")
     projs = cfg.projections
     plans = [Plan(p.N, p.K, "bf16") for p in projs]
     Wh = [synth.weights(cfg, i) for i in range(len(projs))]
@@ -443,8 +443,9 @@ def time_swiglu(steps: int = 1000, reps: int = 20):
     stream = torch.cuda.current_stream()
     sh = __import__("ctypes").c_void_p(stream.cuda_stream)
     out = {}
-    for key, cfg_no, M, dt in (("decode_gate_up_08b_m1", 1, 1, "f32"), ("prefill_gate_up_4b_m2048", 2, 2048, "bf16")):
-        cfg = synth.CONFIGS[cfg_no]
+    for key, wl, M, dt in (("decode_gate_up_08b_m1", "decode_0.8b_layer_m1", 1, "f32"),
+                           ("prefill_gate_up_4b_m2048", "prefill_4b_layer", 2048, "bf16")):
+        cfg = synth.workload(wl)
         pi = [p.name for p in cfg.projections].index("gate_up")
         p = cfg.projections[pi]
         fused = ssb.Plan(p.N, p.K, dt, epilogue="swiglu")
@@ -519,15 +520,16 @@ def time_rmsnorm(steps: int = 1000):
     stream = torch.cuda.current_stream()
     sh = __import__("ctypes").c_void_p(stream.cuda_stream)
     out = {}
-    for key, cfg_no, pname, dt in (("decode_qkv_08b_m1", 1, "qkv", "f32"), ("decode_head_08b_m1", 1, "head", "f32"),
-                                   ("decode_qkv_27b_m1", 4, "qkv", "bf16")):
-        cfg = synth.CONFIGS[cfg_no]
+    for key, wl, pname, dt in (("decode_qkv_08b_m1", "decode_0.8b_layer_m1", "qkv", "f32"),
+                               ("decode_head_08b_m1", "decode_0.8b_layer_m1", "head", "f32"),
+                               ("decode_qkv_27b_m1", "layer_27b", "qkv", "bf16")):
+        cfg = synth.workload(wl)
         pi = [p.name for p in cfg.projections].index(pname)
         p = cfg.projections[pi]
         normp = ssb.Plan(p.N, p.K, dt, rmsnorm_eps=eps)
         plain = ssb.Plan(p.N, p.K, dt)
         Wh, Xh = synth.weights(cfg, pi), synth.activations(cfg, pi, 1)
-        gh = (1.0 + 0.25 * np.random.default_rng(cfg_no * 10 + pi).standard_normal(p.K)).astype(np.float32)
+        gh = (1.0 + 0.25 * np.random.default_rng(cfg.no * 10 + pi).standard_normal(p.K)).astype(np.float32)
         W, X, g = upload(Wh), upload(Xh), torch.from_numpy(gh).cuda()
         copies = max(1, -(-ROTATE_BYTES // (W.numel() * 2)))
         Wrot = [W] + [W.clone() for _ in range(copies - 1)]
@@ -601,7 +603,7 @@ def time_packed(steps: int = 1000, reps: int = 20, rounds: int = 3):
     out = {"workload": "packed weights (128-row panels of 128 x 64 blocks) vs row-major, same shapes, "
                        "each layout on its own tuned plan"}
     # ---- decode step, M = 1
-    cfg = synth.CONFIGS[1]
+    cfg = synth.workload("decode_0.8b_layer_m1")
     projs = cfg.projections
     pr = [Plan(p.N, p.K, "f32") for p in projs]
     pk = [Plan(p.N, p.K, "f32", packed=True) for p in projs]
@@ -677,9 +679,9 @@ def time_packed(steps: int = 1000, reps: int = 20, rounds: int = 3):
                         packed_over_rows=round(tr_all / tp_all, 3), projections=per)
         log(f"  packed {label}: {out[key]['packed']} TFLOP/s vs row-major {out[key]['rows']}")
 
-    cfg4 = synth.CONFIGS[2]
+    cfg4 = synth.workload("prefill_4b_layer")
     prefill(cfg4, range(len(cfg4.projections)), 2048, reps, "prefill_4b_m2048", "4B layer M=2048")
-    cfg27 = synth.CONFIGS[4]
+    cfg27 = synth.workload("layer_27b")
     gu = [i for i, p in enumerate(cfg27.projections) if p.N == max(q.N for q in cfg27.projections)]
     prefill(cfg27, gu, 8192, 5, "gate_up_27b_m8192", "27B gate/up M=8192")
     return out

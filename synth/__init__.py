@@ -98,6 +98,15 @@ CONFIGS = (
            notes="27B-like layer, weights with 1% outliers x10"),
 )
 
+_BY_NAME = {c.name: c for c in CONFIGS}
+
+
+def workload(name: str) -> Config:
+    """The workload of that name (single_1024x1024, decode_0.8b_layer_m1,
+    prefill_4b_layer, long_prompt_4b_8192x1024, layer_27b)."""
+    return _BY_NAME[name]
+
+
 # Extra shape printed by the pages: the 0.8B gate/up projection 1024 -> 7168
 # ("#002 le meme compilateur sur un GPU", section "Emettre pour un GPU").
 PAGES_GATE_UP_08B = Projection("gate_up_pages", 7168, 1024)

@@ -15,15 +15,14 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 
-def _proj_cases(cfg_no):
-    cfg = synth.CONFIGS[cfg_no]
-    return [(cfg_no, i) for i in range(len(cfg.projections))]
+def _proj_cases(wl):
+    return [(wl, i) for i in range(len(synth.workload(wl).projections))]
 
 
-@pytest.mark.parametrize("cfg_no,pi", _proj_cases(1))
-def test_decode_08b_layer_and_head_m1(cfg_no, pi):
+@pytest.mark.parametrize("wl,pi", _proj_cases("decode_0.8b_layer_m1"))
+def test_decode_08b_layer_and_head_m1(wl, pi):
     """0.8B-like decode step: QKV, out, gate/up, down and the 151936-row head at M=1."""
-    cfg = synth.CONFIGS[cfg_no]
+    cfg = synth.workload(wl)
     p = cfg.projections[pi]
     W = synth.weights(cfg, pi)
     X = synth.activations(cfg, pi, 1)
@@ -32,11 +31,11 @@ def test_decode_08b_layer_and_head_m1(cfg_no, pi):
     G.check_against_oracle(Y, X, W, "f32", label=f"{p.name} {p.N}x{p.K} {plan.choice(1)}")
 
 
-@pytest.mark.parametrize("cfg_no,pi", _proj_cases(2))
+@pytest.mark.parametrize("wl,pi", _proj_cases("prefill_4b_layer"))
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_prefill_4b_layer(cfg_no, pi, dtype):
+def test_prefill_4b_layer(wl, pi, dtype):
     """4B-like layer at M = 128, 512, 2048 with an NaN-filled guard row."""
-    cfg = synth.CONFIGS[cfg_no]
+    cfg = synth.workload(wl)
     p = cfg.projections[pi]
     W = synth.weights(cfg, pi)
     Wd = G.dev(W)
@@ -56,7 +55,7 @@ def test_long_prompt_blocks_and_head():
     """8192 prompt rows as 8 blocks of 1024 through each 4B-like projection, then
     the 151936 x 2560 head on the last row only (caller-side block driver)."""
     import torch
-    cfg = synth.CONFIGS[3]
+    cfg = synth.workload("long_prompt_4b_8192x1024")
     rows_total, block = cfg.extra["prompt_rows"], cfg.extra["block"]
     for pi, p in enumerate(cfg.projections):
         W = synth.weights(cfg, pi)
@@ -75,11 +74,11 @@ def test_long_prompt_blocks_and_head():
         G.check_against_oracle(Y, X, W, "f32", rows=rows, label=f"{p.name} {p.N}x{p.K} blocks of 1024")
 
 
-@pytest.mark.parametrize("cfg_no,pi", _proj_cases(4))
-def test_27b_layer(cfg_no, pi):
+@pytest.mark.parametrize("wl,pi", _proj_cases("layer_27b"))
+def test_27b_layer(wl, pi):
     """27B-like layer (weights with 1% outliers x10) at M = 1 (all rows) and
     M = 8192 (sampled rows)."""
-    cfg = synth.CONFIGS[cfg_no]
+    cfg = synth.workload(wl)
     p = cfg.projections[pi]
     W = synth.weights(cfg, pi)
     Wd = G.dev(W)

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M", [1, 16])
 def test_single_projection_1024(M, dtype):
-    cfg = synth.CONFIGS[0]
+    cfg = synth.workload("single_1024x1024")
     W = synth.weights(cfg, 0)
     X = synth.activations(cfg, 0, M)
     p = G.plan(1024, 1024, dtype)

@@ -84,7 +84,7 @@ def test_folded_norm_equals_unfused(N, K, dtype):
 def test_tuned_decode_projections_and_choice():
     """The 0.8B-like QKV and the head with the norm prologue, tuned, at M = 1;
     the plan records whether the folded or the unfused variant won."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.workload("decode_0.8b_layer_m1")
     for name in ("qkv", "head"):
         pi = [p.name for p in cfg.projections].index(name)
         p = cfg.projections[pi]
@@ -99,7 +99,7 @@ def test_tuned_decode_projections_and_choice():
 
 
 def test_tuned_prefill_with_norm():
-    cfg = synth.CONFIGS[2]
+    cfg = synth.workload("prefill_4b_layer")
     pi = [p.name for p in cfg.projections].index("qkv")
     p = cfg.projections[pi]
     W = synth.weights(cfg, pi)

@@ -120,7 +120,7 @@ def test_unfused_activation_kernel(dtype):
 
 
 def test_decode_gate_up_08b_tuned():
-    cfg = synth.CONFIGS[1]
+    cfg = synth.workload("decode_0.8b_layer_m1")
     pi = [p.name for p in cfg.projections].index("gate_up")
     p = cfg.projections[pi]
     W = synth.weights(cfg, pi)
@@ -134,7 +134,7 @@ def test_decode_gate_up_08b_tuned():
 
 @pytest.mark.parametrize("M", [512, 2048])
 def test_prefill_gate_up_4b_tuned(M):
-    cfg = synth.CONFIGS[2]
+    cfg = synth.workload("prefill_4b_layer")
     pi = [p.name for p in cfg.projections].index("gate_up")
     p = cfg.projections[pi]
     W = synth.weights(cfg, pi)

@@ -144,15 +144,17 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     //      4 rows for 64-byte rows (BK = 32).
     //      Each entry also lists the K-split factors of its split-tail variants
     //      (whole tiles for all full rounds of workgroups, the remaining tiles
-    //      split along K so the last round is not mostly idle).
+    //      split along K so the last round is not mostly idle; a factor that does
+    //      not divide the k-tile count gives pieces of two lengths, e.g. three or
+    //      six pieces for the 40 tail tiles of 2560-column shapes at M = 512).
     // BST = ST + 1: one more LDS buffer for W than for X (W copies a k-tile further ahead).
     // At a few hundred rows the GEMM streams W from HBM much as the GEMV does, and
     // a 128 x 128 tile with four W buffers keeps more of it in flight per CU.
-    struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[2]; int BST = 0; };
+    struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[5]; int BST = 0; };
     const GT gts[] = {
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2}},
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3},
-        {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
+        {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}, 4},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},
         {128, 128, 64, 2, 2, 2, 1, 8, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
@@ -188,8 +190,8 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         }
         for (int SK : {1, 2, 4, 8})
             if (SK <= g.maxSK && K % (g.BK * SK) == 0) add(SK, 1);
-        for (int TL : g.tails)
-            if (TL > 1 && (K / g.BK) % TL == 0) add(1, TL);
+        for (int TL : g.tails)   // pieces of at least two k-tiles (KT / TL or one more)
+            if (TL > 1 && K % g.BK == 0 && K / g.BK >= 2 * TL) add(1, TL);
     }
 
     // ---- plain kernel, any shape (K % 8 == 0)

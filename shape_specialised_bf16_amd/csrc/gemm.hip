@@ -35,8 +35,9 @@
 //  * TAILS > 1 (data-parallel with a split tail): of the T tiles, the largest
 //    multiple of ROUND (the workgroups the device runs at once) that leaves a
 //    remainder runs as whole tiles; each of the rem remaining tiles is split
-//    TAILS ways along K, so the last round is filled with rem*TAILS shorter
-//    pieces instead of rem long ones.  Pieces write f32 partials into
+//    TAILS ways along K (piece z: k-tiles [z*KT/TAILS, (z+1)*KT/TAILS), so the
+//    pieces differ by at most one k-tile), and the last round is filled with
+//    rem*TAILS shorter pieces instead of rem long ones.  Pieces write f32 partials into
 //    ws[piece][BM*BN]; tail_reduce adds them in ascending split order.
 // Both reductions use a fixed order, so results do not depend on which block
 // finishes first.
@@ -129,10 +130,12 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
     static_assert(STAGES >= 2 && STAGES <= 4, "2..4 buffers");
     static_assert(K % (SK * BK) == 0, "K splits are whole k-tiles");
-    static_assert(TAILS == 1 || (SK == 1 && ROUND > 0 && (K / BK) % TAILS == 0), "tail pieces are whole k-tiles");
+    static_assert(TAILS == 1 || (SK == 1 && ROUND > 0 && K % BK == 0 && K / BK >= TAILS), "tail pieces are whole k-tiles");
     constexpr long KS = K / SK;
     constexpr long KT = KS / BK;                      // k-tiles of a whole (split-K) tile
-    constexpr long KT_TAIL = KT / TAILS;              // k-tiles of a tail piece
+    // tail piece z takes k-tiles [z*KT/TAILS, (z+1)*KT/TAILS): KT_TAIL of them, or
+    // one more when TAILS does not divide KT
+    constexpr long KT_TAIL = KT / TAILS;
     constexpr int WTM = BM / WM, WTN = BN / WN;       // wave sub-tile
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -209,7 +212,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
         piece = (long)blockIdx.x - n_full;
         pid = n_full + piece / TAILS;
         z = (int)(piece % TAILS);
-        kbeg = (long)z * (K / TAILS);
+        kbeg = ((long)z * KT / TAILS) * BK;
     } else {
         pid = xcd_remap(blockIdx.x, n_full);
         z = blockIdx.y;
@@ -351,7 +354,8 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     // ---- the k loop over NKT k-tiles (a compile-time count: KT for a whole
-    //      tile, KT_TAIL for a tail piece).  Tile t lives in buffer t % STAGES.
+    //      tile, KT_TAIL or KT_TAIL + 1 for a tail piece).  Tile t lives in buffer
+    //      t % STAGES.
     //      The barrier that publishes tile kt+1 (and frees tile kt's buffer)
     //      sits before the last 16-wide k step of tile kt: after it, each wave
     //      reads the first operand fragments of tile kt+1 while the MFMAs of
@@ -497,7 +501,13 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     };
     if constexpr (TAILS > 1) {
         if (tail) {
-            kloop(ic<KT_TAIL>{});
+            if constexpr (KT % TAILS == 0) {
+                kloop(ic<KT_TAIL>{});
+            } else {
+                // uniform across the workgroup; each count its own unrolled loop
+                if (((long)(z + 1) * KT / TAILS) - ((long)z * KT / TAILS) == KT_TAIL) kloop(ic<KT_TAIL>{});
+                else kloop(ic<KT_TAIL + 1>{});
+            }
             float* part = ws + piece * ((long)BM * BN);
 #pragma unroll
             for (int i = 0; i < TM; ++i)

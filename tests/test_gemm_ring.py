@@ -193,8 +193,8 @@ def test_ring_waits_are_exact_for_every_tile_count(cfg):
     assert c["WAIT0"] <= 63 and c["WAITK"] <= 63, "wait counts fit the vmcnt field"
     KT = K // SK // BK
     counts = set(range(1, min(KT, 3 * c["PERIOD"] + 2) + 1)) | {KT}
-    if TAILS > 1:
-        counts.add(KT // TAILS)
+    if TAILS > 1:                                 # a tail piece: KT // TAILS k-tiles or one more
+        counts |= {KT // TAILS, -(-KT // TAILS)}
     for nkt in sorted(counts):
         replay(nkt, ST, DMA, BST, IA, IB, BK // 16)
 

@@ -154,6 +154,7 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     const GT gts[] = {
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2}},
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3},
+        {192, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3},
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}, 4},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},

@@ -125,6 +125,12 @@ proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
  * many rows of N values as fit 256 MiB, at most 8192), then the activation
  * kernel -- and the load-time tuner picks between fused and unfused per row
  * bucket, the fusion being an option measured at load (same page and section).
+ * The tuner's gate holds a SwiGLU candidate to bit equality on the integer
+ * probe and, on the random probe, to an allowance derived from the plain
+ * projection's f32 rule on g and u carried through silu (Lipschitz constant
+ * 1.1) plus the bf16 roundings of g, u and Y: candidates sum g and u in
+ * different orders, and one bf16 step of g near a rounding boundary moves
+ * silu(g) * u by more than one bf16 step of Y.
  *
  * PROJ_PRO_RMSNORM: X is normalised first, row by row, as by proj_rmsnorm with
  * epsilon `norm_eps` (a constant of the generated code) and the norm weights

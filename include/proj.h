@@ -66,7 +66,9 @@ enum {
  * {1}, {2..16}, {17..128}, {129..512}, {513..1024}, {1025..2048}, {2049..8192},
  * validates every candidate kernel on synthetic probe inputs (full and partial
  * block, NaN-sentinel output, integer probe bit-exact) against a plain
- * reference kernel, times the ones that pass and keeps the fastest: the
+ * reference kernel on sampled rows and, on the integer probe, against the
+ * plain kernel's whole output (an order-independent hash of every element),
+ * times the ones that pass and keeps the fastest: the
  * load-time tuner with its correctness gate of "#004 the same compiler on
  * Apple's chips", sections "Catching up on prefill" and "The night the engine
  * chose wrong".  Blocks for seconds.

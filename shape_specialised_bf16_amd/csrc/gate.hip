@@ -72,8 +72,35 @@ struct CheckStats {
     u32 guard;        // elements of rows >= M that no longer hold the sentinel
     u32 max_err;      // f32 bits of max |y - ref| over listed rows
     u32 max_ref;      // f32 bits of max |ref| over listed rows
-    u32 pad[3];
+    u32 pad;
+    u64 hash;         // proj_hash_out: hash of every output element of rows < M
 };
+
+// SplitMix64 finaliser (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014): a bijective 64-bit mixer.
+__device__ __forceinline__ u64 mix64(u64 z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Order-independent hash of the first n output elements: the sum mod 2^64 of
+// mix64(index, bits) over the elements.  Equal outputs hash equally whatever
+// the launch order; a differing element changes the sum unless mixes cancel,
+// which the mixer makes vanishingly unlikely.  Used on the integer probe, where
+// every candidate's output must equal the plain kernel's bit for bit.
+extern "C" __global__ __launch_bounds__(256) void proj_hash_out(const void* __restrict__ Y, long n,
+                                                                CheckStats* __restrict__ st)
+{
+    u64 h = 0;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+        const u64 v = OUT_SEL == OUT_BF16 ? (u64)reinterpret_cast<const u16*>(Y)[i]
+                                          : (u64)reinterpret_cast<const u32*>(Y)[i];
+        h += mix64(((u64)i << 32) ^ v ^ 0x9E3779B97F4A7C15ull);
+    }
+    if (h) atomicAdd(&st->hash, h);
+}
 
 template <int OUT>
 __device__ __forceinline__ float load_out(const void* Y, long i)

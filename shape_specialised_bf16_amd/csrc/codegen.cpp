@@ -159,8 +159,8 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}, 4},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},
         {128, 128, 64, 2, 2, 2, 1, 8, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
-        {128, 128, 64, 3, 2, 2, 1, 8, 8, 1, {2, 4}, 4},
-        {128, 64, 64, 3, 2, 2, 1, 8, 8, 1, {2, 4}, 4},
+        {128, 128, 64, 3, 2, 2, 1, 8, 8, 1, {2, 3, 4, 6}, 4},
+        {128, 64, 64, 3, 2, 2, 1, 8, 8, 1, {2, 3, 4, 6}, 4},
         {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 8, 8, 1, {}}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;

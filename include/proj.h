@@ -18,7 +18,7 @@
  *     created with PROJ_W_PACKED (the packed layout of proj_pack_weights).  X
  *     and W hold bf16 bit patterns; Y holds f32 (PROJ_OUT_F32) or bf16
  *     (PROJ_OUT_BF16).  All three must be 16-byte aligned; Y must not overlap
- *     X or W.
+ *     X or W (both checked: PROJ_EINVAL).
  *   - Work is enqueued on `stream` (a HIP stream of the plan's device, or NULL
  *     for the null stream) and the call returns without synchronising and
  *     without allocating.

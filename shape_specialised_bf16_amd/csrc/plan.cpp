@@ -995,6 +995,14 @@ int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, in
     if (!X || !W || !Y) return set_error(PROJ_EINVAL, "null pointer (X=%p W=%p Y=%p)", X, W, (void*)Y);
     if (((uintptr_t)X | (uintptr_t)W | (uintptr_t)Y) & 15)
         return set_error(PROJ_EINVAL, "X, W and Y must be 16-byte aligned (X=%p W=%p Y=%p)", X, W, (void*)Y);
+    // Y is written while X and W are still read (by other workgroups): no overlap
+    const uintptr_t x0 = (uintptr_t)X, w0 = (uintptr_t)W, y0 = (uintptr_t)Y;
+    const uintptr_t x1 = x0 + (uintptr_t)M * (uintptr_t)p->K * 2u;
+    const uintptr_t w1 = w0 + (uintptr_t)p->N * (uintptr_t)p->K * 2u;
+    const uintptr_t y1 = y0 + (uintptr_t)M * (uintptr_t)p->NO * (p->dtype == PROJ_OUT_BF16 ? 2u : 4u);
+    if ((y0 < x1 && x0 < y1) || (y0 < w1 && w0 < y1))
+        return set_error(PROJ_EINVAL, "Y [%p, %p) overlaps X [%p, %p) or W [%p, %p)", (void*)y0, (void*)y1,
+                         (void*)x0, (void*)x1, (void*)w0, (void*)w1);
     int cur = -1;
     HIP_TRY(hipGetDevice(&cur));
     if (cur != p->device)

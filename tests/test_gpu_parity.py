@@ -183,6 +183,10 @@ def test_wrong_arguments_are_rejected():
         p.run_ptr(X.data_ptr(), W.data_ptr(), Y.data_ptr(), -1, None)
     with pytest.raises(ProjError, match="null"):
         p.run_ptr(0, W.data_ptr(), Y.data_ptr(), 4, None)
+    with pytest.raises(ProjError, match="overlaps"):               # Y on top of W's last rows
+        p.run_ptr(X.data_ptr(), W.data_ptr(), W.data_ptr() + 1020 * 1024 * 2, 4, None)
+    with pytest.raises(ProjError, match="overlaps"):               # Y on top of X
+        p.run_ptr(X.data_ptr(), W.data_ptr(), X.data_ptr(), 4, None)
     with pytest.raises(ValueError):
         p.run(X, W[:512])
 

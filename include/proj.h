@@ -245,6 +245,27 @@ int proj_emit_source(int64_t N, int64_t K, int dtype, const char* arch, char* bu
 int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int flags, float norm_eps, const char* arch, char* buf,
                         size_t cap, size_t* needed);
 
+/*
+ * Emit and compile, for device architecture `arch` (NULL: "gfx950"), every
+ * module a plan for (N, K, dtype, flags, norm_eps) would load -- the same
+ * sources and the same hipRTC options as proj_plan_create_ex -- without a GPU
+ * and without keeping the code.  *seconds (if not NULL) receives the wall
+ * time.  PROJ_OK, PROJ_EINVAL for arguments proj_plan_create_ex would reject,
+ * or PROJ_ECOMPILE with hipRTC's log in proj_last_error().  The compilation
+ * step alone: the pages report it separately from the tuning measurements
+ * ("#004 the same compiler on Apple's chips", section "So, does it start up
+ * more slowly?").
+ *
+ * Compilation (here and in proj_plan_create_ex) runs in up to PROJ_RTC_JOBS
+ * (default: the CPUs the process may use, at most 16) child processes of the
+ * helper proj_rtc installed beside the library, one per module, since hipRTC
+ * compiles one program at a time per process.  Without the helper, or with
+ * PROJ_RTC_JOBS=0, the modules are compiled one after another in the calling
+ * process, by whichever hipRTC library it has loaded.
+ */
+int proj_compile_only(int64_t N, int64_t K, int dtype, int flags, float norm_eps, const char* arch,
+                      double* seconds);
+
 /* JSON text (host buffer) describing the plan: shape, candidates, per-bucket
  * choice and timings, the tuner log, compile and tuning seconds.  Same size
  * protocol as proj_emit_source. */

@@ -20,7 +20,7 @@ import ctypes
 import json
 import os
 
-__all__ = ["Plan", "ProjError", "emit_source", "probe_read", "round_bf16", "pack_weights", "swiglu", "rmsnorm",
+__all__ = ["Plan", "ProjError", "emit_source", "compile_only", "probe_read", "round_bf16", "pack_weights", "swiglu", "rmsnorm",
            "LIB_PATH", "OUT_F32", "OUT_BF16", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "proj_plan_describe", "proj_plan_num_candidates", "proj_plan_candidate_name",
     "proj_plan_candidate_max_m", "proj_run_candidate", "proj_plan_choice", "proj_probe_read",
     "proj_round_bf16", "proj_plan_create_ex", "proj_emit_source_ex", "proj_swiglu", "proj_run_ex",
-    "proj_run_candidate_ex", "proj_rmsnorm", "proj_pack_weights", "proj_run_packed",
+    "proj_run_candidate_ex", "proj_rmsnorm", "proj_pack_weights", "proj_run_packed", "proj_compile_only",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -101,6 +101,9 @@ _lib.proj_pack_weights.argtypes = [_i64, _i64, _p, _p, _p]
 _lib.proj_pack_weights.restype = ctypes.c_int
 _lib.proj_run_packed.argtypes = [_p, _p, _p, _p, _i64, _p, _p]
 _lib.proj_run_packed.restype = ctypes.c_int
+_lib.proj_compile_only.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_char_p,
+                                   ctypes.POINTER(ctypes.c_double)]
+_lib.proj_compile_only.restype = ctypes.c_int
 
 
 class ProjError(RuntimeError):
@@ -139,6 +142,17 @@ def emit_source(N: int, K: int, dtype: str = "f32", arch: str = "gfx950", epilog
     fusion = _epi_code(epilogue) | (PRO_RMSNORM if rmsnorm_eps is not None else 0) | (W_PACKED if packed else 0)
     return _text(_lib.proj_emit_source_ex, N, K, _dtype_code(dtype), fusion,
                  float(rmsnorm_eps or 0.0), arch.encode())
+
+
+def compile_only(N: int, K: int, dtype: str = "f32", arch: str = "gfx950", epilogue=None, rmsnorm_eps=None,
+                 packed: bool = False) -> float:
+    """Compile every module of the plan (N, K, dtype[, ...]) for `arch` without
+    a GPU (proj_compile_only); returns the seconds it took."""
+    fusion = _epi_code(epilogue) | (PRO_RMSNORM if rmsnorm_eps is not None else 0) | (W_PACKED if packed else 0)
+    sec = ctypes.c_double(0.0)
+    _check(_lib.proj_compile_only(N, K, _dtype_code(dtype), fusion, float(rmsnorm_eps or 0.0), arch.encode(),
+                                  ctypes.byref(sec)), "proj_compile_only")
+    return sec.value
 
 
 def _dtype_code(dtype) -> int:

@@ -1,5 +1,6 @@
 // api.cpp -- the extern "C" entry points declared in include/proj.h.
 #include <algorithm>
+#include <chrono>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -92,7 +93,7 @@ static std::string describe(const proj_plan* p)
       << "\", \"norm_eps\": " << p->eps << ", \"layout\": \"" << (p->wpack ? "packed" : "rows")
       << "\", \"dtype\": \"" << (p->dtype ? "bf16" : "f32")
       << "\", \"arch\": \"" << p->arch << "\", \"device\": " << p->device << ", \"compile_s\": " << p->compile_s
-      << ", \"tune_s\": " << p->tune_s << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
+      << ", \"tune_s\": " << p->tune_s << ", \"modules\": " << p->modules.size() << ", \"code_bytes\": " << p->code_bytes << ", \"ws_bytes\": " << p->ws_bytes
       << ", \"swiglu_intermediate_rows\": " << p->gu_rows
       << ", \"cache\": \"" << p->cache << "\", \"code_cache\": \"" << p->code_cache << "\", \"cache_path\": \""
       << json_escape(p->cache_path) << "\""
@@ -205,6 +206,27 @@ int proj_emit_source_ex(int64_t N, int64_t K, int dtype, int fusion, float norm_
     return copy_text(emit_source(N, K, dtype, a, kDefaultCUs, enumerate_candidates(N, K, kDefaultCUs, fusion),
                                  fusion, (fusion & PROJ_PRO_RMSNORM) ? norm_eps : 0.f),
                      buf, cap, needed);
+}
+
+int proj_compile_only(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, const char* arch, double* seconds)
+{
+    g_last_error.clear();
+    if (seconds) *seconds = 0;
+    int rc = proj_emit_source_ex(N, K, dtype, fusion, norm_eps, arch, nullptr, 0, nullptr);
+    if (rc) return rc;
+    const std::string a = (arch && *arch) ? arch : "gfx950";
+    std::vector<Candidate> cands = enumerate_candidates(N, K, kDefaultCUs, fusion);
+    const std::vector<std::string> srcs =
+        emit_module_sources(N, K, dtype, a, kDefaultCUs, cands, fusion,
+                            (fusion & PROJ_PRO_RMSNORM) ? norm_eps : 0.f, kMaxModules);
+    char name[96];
+    snprintf(name, sizeof name, "proj_%lldx%lld_%s_flags%d", (long long)N, (long long)K, dtype ? "bf16" : "f32",
+             fusion);
+    const auto t0 = std::chrono::steady_clock::now();
+    std::vector<std::shared_ptr<std::vector<char>>> codes;
+    rc = compile_sources(srcs, a, name, &codes);
+    if (seconds) *seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    return rc;
 }
 
 int proj_plan_describe(const proj_plan* plan, char* buf, size_t cap, size_t* needed)

@@ -8,6 +8,7 @@
 // index, per-candidate trip counts and strides -- appears in the emitted text
 // as a literal; a candidate is only emitted when its tiles divide the shape, so
 // no kernel carries remainder code for N or K.  Only M stays a run-time value.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <sstream>
@@ -216,16 +217,14 @@ std::string emit_support_source()
     return s;
 }
 
-std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
-                        const std::vector<Candidate>& cands, int fusion, float norm_eps)
+// The shape prelude: the constants of (N, K, dtype, fusion) as literals, then
+// the device helpers and kernel templates every module of the plan shares.
+static std::string emit_prelude(int64_t N, int64_t K, int dtype, const std::string& arch, int cus, int fusion,
+                                float norm_eps)
 {
-    const char* out = dtype == 1 ? "OUT_BF16" : "OUT_F32";
     const int epi = fusion & 1, wpack = (fusion & 4) ? 1 : 0;
     char eps_lit[64];
     snprintf(eps_lit, sizeof eps_lit, "%a", (double)norm_eps);
-    // how the candidate comments below describe the weight stream
-    const std::string wdesc = wpack ? std::string("weights in 16 KiB panel blocks")
-                                    : fmt("weight row stride %lld B", (long long)(2 * K));
     std::ostringstream s;
     s << "// Generated by libproj for Y[M," << N << "] = X[M," << K << "] . W[" << N << "," << K
       << "]^T, output " << (dtype == 1 ? "bf16" : "f32") << ", target " << arch
@@ -249,68 +248,138 @@ std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch
     s << kKernelsHeadSrc << "\n";
     s << kGemvSrc << "\n";
     s << kGemmSrc << "\n";
+    return s.str();
+}
+
+// The extern "C" wrapper(s) of one candidate: its template instantiated with
+// literal arguments, plus its second-pass kernel.  A split-K reduce kernel is
+// shared by the candidates of one split factor: `reduce_emitted` (indexed by
+// SK) records which the module already holds.
+static void emit_wrappers(std::ostringstream& s, const Candidate& c, int64_t N, int64_t K, int dtype, int wpack,
+                          bool reduce_emitted[9])
+{
+    const char* out = dtype == 1 ? "OUT_BF16" : "OUT_F32";
+    // how the candidate comments below describe the weight stream
+    const std::string wdesc = wpack ? std::string("weights in 16 KiB panel blocks")
+                                    : fmt("weight row stride %lld B", (long long)(2 * K));
+    const char* sig = "(const u16* __restrict__ X, const u16* __restrict__ W, void* __restrict__ Y, "
+                      "float* __restrict__ ws, const float* __restrict__ gamma, int M)";
+    switch (c.fam) {
+    case Family::GemvValu: {
+        const int64_t chs = K / 8 / c.S;
+        s << "// " << c.name << ": " << c.R << " row(s)/wave, K split " << c.S << " ways, "
+          << chs << " blocks/slice = " << chs / 64 << " trip(s) of 64 lanes + " << chs % 64
+          << " tail lanes, " << wdesc << "\n";
+        s << "static_assert(K_BLOCKS16 / " << c.S << " / 64 == " << chs / 64 << ", \"trip count\");\n";
+        s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_valu<"
+          << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out << ", "
+          << c.P << ", " << c.PRO << ", " << c.E << ">(X, W, Y, gamma, M); }\n";
+        break;
+    }
+    case Family::GemvMfma: {
+        const int64_t batches = K / c.S / (32 * c.U);
+        s << "// " << c.name << ": 16 rows/wave on mfma_16x16x32_bf16, K split " << c.S << " ways, "
+          << batches << " batch(es) of " << c.U << " MFMA steps, " << wdesc << ", next 16-row weight block at +"
+          << (wpack ? 16 * 64 * 2 : 32 * K) << " B\n";
+        s << "static_assert(K / " << c.S << " / " << 32 * c.U << " == " << batches << ", \"trip count\");\n";
+        s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_mfma<"
+          << c.S << ", " << c.U << ", " << c.NT << ", " << out << ">(X, W, Y, M); }\n";
+        break;
+    }
+    case Family::Gemm: {
+        const int64_t kt = K / c.SK / c.BK;
+        s << "// " << c.name << ": " << c.BM << "x" << c.BN << " tile, " << c.WM * c.WN << " waves, "
+          << c.ST << " LDS buffers of " << (c.BM + c.BN) * c.BK * 2 << " B, K split " << c.SK << " ways, "
+          << kt << " k-tile(s) of " << c.BK << ", " << N / c.BN << " tile column(s), " << wdesc << "\n";
+        s << "static_assert(K / " << c.SK << " / " << c.BK << " == " << kt << ", \"trip count\");\n";
+        s << "extern \"C\" __global__ __launch_bounds__(" << c.threads << ") void " << c.name << sig
+          << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.BK << ", " << c.ST << ", " << c.WM << ", "
+          << c.WN << ", " << c.SK << ", " << c.GM << ", " << c.SWZ << ", " << out << ", " << c.DMA << ", "
+          << c.TAILS << ", " << c.ROUND << ", " << c.E << ", " << c.BST << ">(X, W, Y, ws, M); }\n";
+        if (c.TAILS > 1) {
+            s << "// " << c.reduce_name << ": tail tiles of " << c.name << ", " << c.TAILS
+              << " pieces each, rounds of " << c.ROUND << " workgroups\n";
+            s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.reduce_name
+              << "(const float* __restrict__ ws, void* __restrict__ Y, int M)\n{ tail_reduce<" << c.BM << ", "
+              << c.BN << ", " << c.TAILS << ", " << c.ROUND << ", " << c.GM << ", " << out << ">(ws, Y, M); }\n";
+        }
+        if (c.SK > 1 && !reduce_emitted[c.SK]) {
+            reduce_emitted[c.SK] = true;
+            s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.reduce_name
+              << "(const float* __restrict__ ws, void* __restrict__ Y, int M)\n{ splitk_reduce<" << c.SK
+              << ", " << out << ">(ws, Y, M); }\n";
+        }
+        break;
+    }
+    case Family::Plain:
+        s << "// gemm_plain: one thread per output, " << K / 8 << " blocks of 16 bytes per dot product\n";
+        s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig
+          << "\n{ gemm_plain<" << out << ", " << c.E << ">(X, W, Y, M); }\n";
+        break;
+    }
+}
+
+static const char* const kCandidatesBanner = "// ===================== candidates for this shape =====================\n";
+
+std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
+                        const std::vector<Candidate>& cands, int fusion, float norm_eps)
+{
+    std::ostringstream s;
+    s << emit_prelude(N, K, dtype, arch, cus, fusion, norm_eps);
     s << kGateSrc << "\n";
     s << kSupportSrc << "\n";
-    s << "// ===================== candidates for this shape =====================\n";
+    s << kCandidatesBanner;
     bool reduce_emitted[9] = {};    // split-K reduce kernels already emitted, by SK (at most 8)
-    for (const Candidate& c : cands) {
-        const char* sig = "(const u16* __restrict__ X, const u16* __restrict__ W, void* __restrict__ Y, "
-                          "float* __restrict__ ws, const float* __restrict__ gamma, int M)";
-        switch (c.fam) {
-        case Family::GemvValu: {
-            const int64_t chs = K / 8 / c.S;
-            s << "// " << c.name << ": " << c.R << " row(s)/wave, K split " << c.S << " ways, "
-              << chs << " blocks/slice = " << chs / 64 << " trip(s) of 64 lanes + " << chs % 64
-              << " tail lanes, " << wdesc << "\n";
-            s << "static_assert(K_BLOCKS16 / " << c.S << " / 64 == " << chs / 64 << ", \"trip count\");\n";
-            s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_valu<"
-              << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out << ", "
-              << c.P << ", " << c.PRO << ", " << c.E << ">(X, W, Y, gamma, M); }\n";
-            break;
-        }
-        case Family::GemvMfma: {
-            const int64_t batches = K / c.S / (32 * c.U);
-            s << "// " << c.name << ": 16 rows/wave on mfma_16x16x32_bf16, K split " << c.S << " ways, "
-              << batches << " batch(es) of " << c.U << " MFMA steps, " << wdesc << ", next 16-row weight block at +"
-              << (wpack ? 16 * 64 * 2 : 32 * K) << " B\n";
-            s << "static_assert(K / " << c.S << " / " << 32 * c.U << " == " << batches << ", \"trip count\");\n";
-            s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_mfma<"
-              << c.S << ", " << c.U << ", " << c.NT << ", " << out << ">(X, W, Y, M); }\n";
-            break;
-        }
-        case Family::Gemm: {
-            const int64_t kt = K / c.SK / c.BK;
-            s << "// " << c.name << ": " << c.BM << "x" << c.BN << " tile, " << c.WM * c.WN << " waves, "
-              << c.ST << " LDS buffers of " << (c.BM + c.BN) * c.BK * 2 << " B, K split " << c.SK << " ways, "
-              << kt << " k-tile(s) of " << c.BK << ", " << N / c.BN << " tile column(s), " << wdesc << "\n";
-            s << "static_assert(K / " << c.SK << " / " << c.BK << " == " << kt << ", \"trip count\");\n";
-            s << "extern \"C\" __global__ __launch_bounds__(" << c.threads << ") void " << c.name << sig
-              << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.BK << ", " << c.ST << ", " << c.WM << ", "
-              << c.WN << ", " << c.SK << ", " << c.GM << ", " << c.SWZ << ", " << out << ", " << c.DMA << ", "
-              << c.TAILS << ", " << c.ROUND << ", " << c.E << ", " << c.BST << ">(X, W, Y, ws, M); }\n";
-            if (c.TAILS > 1) {
-                s << "// " << c.reduce_name << ": tail tiles of " << c.name << ", " << c.TAILS
-                  << " pieces each, rounds of " << c.ROUND << " workgroups\n";
-                s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.reduce_name
-                  << "(const float* __restrict__ ws, void* __restrict__ Y, int M)\n{ tail_reduce<" << c.BM << ", "
-                  << c.BN << ", " << c.TAILS << ", " << c.ROUND << ", " << c.GM << ", " << out << ">(ws, Y, M); }\n";
-            }
-            if (c.SK > 1 && !reduce_emitted[c.SK]) {
-                reduce_emitted[c.SK] = true;
-                s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.reduce_name
-                  << "(const float* __restrict__ ws, void* __restrict__ Y, int M)\n{ splitk_reduce<" << c.SK
-                  << ", " << out << ">(ws, Y, M); }\n";
-            }
-            break;
-        }
-        case Family::Plain:
-            s << "// gemm_plain: one thread per output, " << K / 8 << " blocks of 16 bytes per dot product\n";
-            s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig
-              << "\n{ gemm_plain<" << out << ", " << c.E << ">(X, W, Y, M); }\n";
-            break;
-        }
-    }
+    for (const Candidate& c : cands) emit_wrappers(s, c, N, K, dtype, (fusion & 4) ? 1 : 0, reduce_emitted);
     return s.str();
+}
+
+// Rough relative compile cost of a candidate's wrappers (hipRTC time of one
+// instantiation, measured: a tiled GEMM ~0.6 s, a 16-row vector GEMV ~0.7 s,
+// a one-row GEMV ~0.25 s, an MFMA GEMV ~0.12 s), used to balance the modules.
+static int compile_cost(const Candidate& c)
+{
+    switch (c.fam) {
+    case Family::Gemm: return 6 + (c.TAILS > 1 ? 1 : 0);
+    case Family::GemvValu: return c.MMAX > 1 ? 7 : 3;
+    case Family::GemvMfma: return 2;
+    case Family::Plain: default: return 1;
+    }
+}
+
+std::vector<std::string> emit_module_sources(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
+                                             std::vector<Candidate>& cands, int fusion, float norm_eps,
+                                             int max_modules)
+{
+    const std::string prelude = emit_prelude(N, K, dtype, arch, cus, fusion, norm_eps);
+    const int G = std::max(1, std::min<int>(max_modules, (int)cands.size()));
+    // longest-first onto the least loaded module; module 0 also carries the
+    // support kernels (validation gate, probes, pack, norm, activation)
+    std::vector<int> order(cands.size());
+    for (size_t i = 0; i < cands.size(); ++i) order[i] = (int)i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return compile_cost(cands[a]) > compile_cost(cands[b]); });
+    std::vector<int> load(G, 0);
+    load[0] = 5;
+    for (int i : order) {
+        int g = 0;
+        for (int j = 1; j < G; ++j)
+            if (load[j] < load[g]) g = j;
+        cands[i].module = g;
+        load[g] += compile_cost(cands[i]);
+    }
+    std::vector<std::string> out;
+    for (int g = 0; g < G; ++g) {
+        std::ostringstream s;
+        s << prelude;
+        if (g == 0) s << kGateSrc << "\n" << kSupportSrc << "\n";
+        s << kCandidatesBanner;
+        bool reduce_emitted[9] = {};
+        for (const Candidate& c : cands)
+            if (c.module == g) emit_wrappers(s, c, N, K, dtype, (fusion & 4) ? 1 : 0, reduce_emitted);
+        out.push_back(s.str());
+    }
+    return out;
 }
 
 }  // namespace proj

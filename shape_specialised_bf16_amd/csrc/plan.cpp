@@ -14,6 +14,13 @@
 // the acceptance rule is the elementwise tolerance of the numerical contract,
 // with an integer probe that must match bit for bit.
 #include <hip/hiprtc.h>
+#include <dlfcn.h>
+#include <fcntl.h>
+#include <sched.h>
+#include <spawn.h>
+#include <sys/stat.h>
+#include <sys/wait.h>
+#include <unistd.h>
 
 #include <algorithm>
 #include <chrono>
@@ -31,6 +38,9 @@
 
 #include "proj.h"
 #include "proj_internal.h"
+#include "rtc.h"
+
+extern char** environ;
 
 namespace proj {
 
@@ -74,47 +84,181 @@ static int env_int(const char* name, int dflt)
 static std::mutex g_cache_mu;
 static std::map<std::string, std::shared_ptr<std::vector<char>>> g_code_cache;
 
+// The compile helper beside libproj.so ("" if it is not there).
+static std::string helper_path()
+{
+    Dl_info info;
+    if (!dladdr((void*)&helper_path, &info) || !info.dli_fname) return "";
+    std::string lib = info.dli_fname;
+    const size_t slash = lib.rfind('/');
+    const std::string h = (slash == std::string::npos ? std::string(".") : lib.substr(0, slash)) + "/proj_rtc";
+    return access(h.c_str(), X_OK) == 0 ? h : "";
+}
+
+// Compile helpers run at once: PROJ_RTC_JOBS, else the CPUs this process may
+// run on, at most 16.  0: compile in this process.
+static int rtc_jobs()
+{
+    if (const char* v = getenv("PROJ_RTC_JOBS"))
+        if (*v) return std::max(0, atoi(v));
+    cpu_set_t set;
+    int n = 1;
+    if (sched_getaffinity(0, sizeof set, &set) == 0) n = CPU_COUNT(&set);
+    return std::max(1, std::min(16, n));
+}
+
+static std::string read_file(const std::string& path)
+{
+    std::ifstream f(path, std::ios::binary);
+    return std::string((std::istreambuf_iterator<char>(f)), std::istreambuf_iterator<char>());
+}
+
+static int compile_error(const std::string& name, std::string log)
+{
+    if (log.size() > 1800) log = log.substr(0, 1800) + "...";
+    return set_error(PROJ_ECOMPILE, "hipRTC compile of %s failed: %s", name.c_str(), log.c_str());
+}
+
+// The sources `todo` (indexes into srcs) compiled by proj_rtc child processes,
+// at most `jobs` at a time, in a private temporary directory.  Returns
+// PROJ_OK, PROJ_ECOMPILE, or 1 if the helpers could not be used at all (the
+// caller then compiles in this process).
+static int compile_in_children(const std::vector<std::string>& srcs, const std::vector<size_t>& todo,
+                               const std::string& arch, const std::string& name, const std::string& helper,
+                               int jobs, std::vector<std::shared_ptr<std::vector<char>>>* codes)
+{
+    const char* tmpdir = getenv("TMPDIR");
+    std::string templ = std::string(tmpdir && *tmpdir ? tmpdir : "/tmp") + "/proj-rtc-XXXXXX";
+    std::vector<char> dirbuf(templ.begin(), templ.end());
+    dirbuf.push_back('\0');
+    if (!mkdtemp(dirbuf.data())) return 1;
+    const std::string dir = dirbuf.data();
+    struct Job {
+        size_t idx;
+        std::string src, out, log;
+        pid_t pid = -1;
+    };
+    std::vector<Job> js;
+    for (size_t i = 0; i < todo.size(); ++i) {
+        Job j;
+        j.idx = todo[i];
+        const std::string base = dir + "/" + name + ".m" + std::to_string(todo[i]);
+        j.src = base + ".hip";
+        j.out = base + ".co";
+        j.log = base + ".log";
+        js.push_back(j);
+    }
+    auto cleanup = [&]() {
+        for (const Job& j : js) {
+            std::remove(j.src.c_str());
+            std::remove(j.out.c_str());
+            std::remove(j.log.c_str());
+            std::remove((j.out + ".tmp").c_str());
+        }
+        rmdir(dir.c_str());
+    };
+    for (Job& j : js) {
+        std::ofstream f(j.src, std::ios::binary);
+        if (!f || !f.write(srcs[j.idx].data(), (std::streamsize)srcs[j.idx].size())) {
+            f.close();
+            cleanup();
+            return 1;
+        }
+    }
+    // wait for one child (EINTR retried); true if it wrote its code object
+    auto finish = [&](Job& j) -> bool {
+        int status = 0;
+        pid_t r;
+        do r = waitpid(j.pid, &status, 0);
+        while (r < 0 && errno == EINTR);
+        const bool exited_ok = r == j.pid ? (WIFEXITED(status) && WEXITSTATUS(status) == 0) : true;
+        j.pid = -1;
+        return exited_ok && access(j.out.c_str(), R_OK) == 0;
+    };
+    int rc = PROJ_OK;
+    bool spawn_failed = false;
+    size_t next = 0, done = 0;
+    std::vector<size_t> running;
+    while (done < js.size()) {
+        while (!spawn_failed && rc == PROJ_OK && next < js.size() && (int)running.size() < jobs) {
+            Job& j = js[next];
+            posix_spawn_file_actions_t fa;
+            posix_spawn_file_actions_init(&fa);
+            posix_spawn_file_actions_addopen(&fa, 1, j.log.c_str(), O_WRONLY | O_CREAT | O_TRUNC, 0600);
+            posix_spawn_file_actions_adddup2(&fa, 1, 2);
+            std::string a0 = helper, a1 = arch;
+            char* argv[] = {&a0[0], &a1[0], &j.src[0], &j.out[0], nullptr};
+            const int e = posix_spawn(&j.pid, helper.c_str(), &fa, nullptr, argv, environ);
+            posix_spawn_file_actions_destroy(&fa);
+            if (e != 0) {
+                j.pid = -1;
+                spawn_failed = true;
+                break;
+            }
+            running.push_back(next++);
+        }
+        if (running.empty()) break;
+        Job& j = js[running.front()];
+        running.erase(running.begin());
+        ++done;
+        if (finish(j)) {
+            const std::string co = read_file(j.out);
+            (*codes)[j.idx] = std::make_shared<std::vector<char>>(co.begin(), co.end());
+        } else if (rc == PROJ_OK) {
+            rc = compile_error(name + " module " + std::to_string(j.idx), read_file(j.log));
+        }
+    }
+    for (size_t r : running) finish(js[r]);
+    cleanup();
+    if (rc != PROJ_OK) return rc;
+    // a spawn failure leaves some sources uncompiled: the caller compiles them here
+    return spawn_failed ? 1 : PROJ_OK;
+}
+
+int compile_sources(const std::vector<std::string>& srcs, const std::string& arch, const std::string& name,
+                    std::vector<std::shared_ptr<std::vector<char>>>* codes)
+{
+    codes->assign(srcs.size(), nullptr);
+    std::vector<size_t> todo;
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        for (size_t i = 0; i < srcs.size(); ++i) {
+            auto it = g_code_cache.find(arch + "\n" + srcs[i]);
+            if (it != g_code_cache.end()) (*codes)[i] = it->second;
+            else todo.push_back(i);
+        }
+    }
+    // The helper compiles with the hipRTC installed with ROCm; this process
+    // may have bound another (the one of the framework that loaded libproj).
+    // One compiler for every module: the helper whenever it is there.
+    const int jobs = rtc_jobs();
+    if (!todo.empty() && jobs > 0) {
+        const std::string helper = helper_path();
+        if (!helper.empty()) {
+            const int rc = compile_in_children(srcs, todo, arch, name, helper, jobs, codes);
+            if (rc < 0) return rc;
+        }
+    }
+    for (size_t i : todo) {
+        if ((*codes)[i]) continue;
+        auto buf = std::make_shared<std::vector<char>>();
+        std::string log;
+        if (rtc_compile(srcs[i], arch, name, buf.get(), &log) != 0)
+            return compile_error(srcs.size() > 1 ? name + " module " + std::to_string(i) : name, log);
+        (*codes)[i] = buf;
+    }
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (size_t i : todo) g_code_cache[arch + "\n" + srcs[i]] = (*codes)[i];
+    return PROJ_OK;
+}
+
 int compile_source(const std::string& src, const std::string& arch, const char* name,
                    std::shared_ptr<std::vector<char>>* code)
 {
-    const std::string key = arch + "\n" + src;
-    {
-        std::lock_guard<std::mutex> lk(g_cache_mu);
-        auto it = g_code_cache.find(key);
-        if (it != g_code_cache.end()) {
-            *code = it->second;
-            return PROJ_OK;
-        }
-    }
-    hiprtcProgram prog;
-    if (hiprtcCreateProgram(&prog, src.c_str(), name, 0, nullptr, nullptr) != HIPRTC_SUCCESS)
-        return set_error(PROJ_ECOMPILE, "hiprtcCreateProgram failed");
-    const std::string arch_opt = "--offload-arch=" + arch;
-    // -packed-fp32-ops: no packed f32 ALU instructions in any kernel.
-    const char* opts[] = {arch_opt.c_str(), "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-                          "-packed-fp32-ops"};
-    static_assert(sizeof opts / sizeof opts[0] == 7, "keep kCompileOptions in step with the options");
-    hiprtcResult r = hiprtcCompileProgram(prog, (int)(sizeof opts / sizeof opts[0]), opts);
-    if (r != HIPRTC_SUCCESS) {
-        size_t ls = 0;
-        hiprtcGetProgramLogSize(prog, &ls);
-        std::string log(ls, '\0');
-        if (ls) hiprtcGetProgramLog(prog, &log[0]);
-        hiprtcDestroyProgram(&prog);
-        if (log.size() > 1800) log = log.substr(0, 1800) + "...";
-        return set_error(PROJ_ECOMPILE, "hipRTC compile of %s failed: %s", name, log.c_str());
-    }
-    size_t cs = 0;
-    hiprtcGetCodeSize(prog, &cs);
-    auto buf = std::make_shared<std::vector<char>>(cs);
-    hiprtcGetCode(prog, buf->data());
-    hiprtcDestroyProgram(&prog);
-    {
-        std::lock_guard<std::mutex> lk(g_cache_mu);
-        g_code_cache[key] = buf;
-    }
-    *code = buf;
-    return PROJ_OK;
+    std::vector<std::shared_ptr<std::vector<char>>> codes;
+    const int rc = compile_sources({src}, arch, name, &codes);
+    if (rc == PROJ_OK) *code = codes[0];
+    return rc;
 }
 
 int device_arch(int dev, std::string* arch, int* cus)
@@ -562,9 +706,6 @@ static bool whole_elf64(const std::vector<char>& buf)
     return ph <= n && phe * phn <= n - ph && sh <= n && she * shn <= n - sh;
 }
 
-// The hipRTC options of compile_source, as text: part of the cache key.
-static const char* const kCompileOptions = "-O3 -std=c++17 -Xclang -target-feature -Xclang -packed-fp32-ops";
-
 static int cache_key(proj_plan* p, const std::string& src)
 {
     hipDeviceProp_t prop;
@@ -573,8 +714,19 @@ static int cache_key(proj_plan* p, const std::string& src)
     HIP_TRY(hipRuntimeGetVersion(&rt));
     HIP_TRY(hipDriverGetVersion(&drv));
     char head[512];
-    snprintf(head, sizeof head, "%s|cus=%d|runtime=%d|driver=%d|options=%s|", prop.gcnArchName,
-             prop.multiProcessorCount, rt, drv, kCompileOptions);
+    // which compiler: the helper (its file size and time identify the build)
+    // or the hipRTC loaded in this process (its version)
+    std::string compiler = "in-process";
+    const std::string helper = rtc_jobs() > 0 ? helper_path() : "";
+    struct stat hs;
+    if (!helper.empty() && stat(helper.c_str(), &hs) == 0) {
+        compiler = "helper:" + std::to_string((long long)hs.st_size) + ":" + std::to_string((long long)hs.st_mtime);
+    } else {
+        int ma = 0, mi = 0;
+        if (hiprtcVersion(&ma, &mi) == HIPRTC_SUCCESS) compiler += ":" + std::to_string(ma) + "." + std::to_string(mi);
+    }
+    snprintf(head, sizeof head, "%s|cus=%d|runtime=%d|driver=%d|options=%s|compiler=%s|", prop.gcnArchName,
+             prop.multiProcessorCount, rt, drv, kRtcOptionText, compiler.c_str());
     p->key = fnv1a(fnv1a(0xcbf29ce484222325ull, head), src);
     return PROJ_OK;
 }
@@ -849,7 +1001,8 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
             if (p->ws) (void)hipFree(p->ws);
             if (p->gu) (void)hipFree(p->gu);
             if (p->xn) (void)hipFree(p->xn);
-            if (p->module) (void)hipModuleUnload(p->module);
+            for (hipModule_t m : p->modules)
+                if (m) (void)hipModuleUnload(m);
         }
     } release{p.get()};
     p->N = N;
@@ -867,89 +1020,134 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
     for (int b = 0; b < kNumBuckets; ++b) p->choice[b] = -1, p->choice_us[b] = -1;
 
     p->cands = enumerate_candidates(N, K, cus, fusion);
+    // the whole translation unit keys the caches and is what PROJ_DUMP_DIR
+    // writes; it is compiled as modules, each holding some candidates
     const std::string src = emit_source(N, K, dtype, p->arch, cus, p->cands, fusion, p->eps);
+    const std::vector<std::string> msrcs =
+        emit_module_sources(N, K, dtype, p->arch, cus, p->cands, fusion, p->eps, kMaxModules);
     if ((rc = cache_key(p.get(), src))) return rc;
     const double t0 = now_s();
-    std::shared_ptr<std::vector<char>> code;
+    std::vector<std::shared_ptr<std::vector<char>>> codes;
     char name[96];
-    snprintf(name, sizeof name, "proj_%lldx%lld_%s%s%s%s.hip", (long long)N, (long long)K, dtype ? "bf16" : "f32",
+    snprintf(name, sizeof name, "proj_%lldx%lld_%s%s%s%s", (long long)N, (long long)K, dtype ? "bf16" : "f32",
              epi ? "_swiglu" : "", p->pro ? "_rmsnorm" : "", p->wpack ? "_panels" : "");
-    // With PROJ_CACHE_DIR, the compiled module is kept beside the tuned choices
-    // under the same key (device, runtime and driver versions, compile options,
-    // emitted source): a later plan of the same key loads it instead of
-    // compiling.  A file that does not load is compiled afresh and replaced.
-    std::string co_path;
+    // With PROJ_CACHE_DIR, the compiled modules are kept beside the tuned
+    // choices under the same key (device, runtime and driver versions, compile
+    // options, emitted source): a later plan of the same key loads them
+    // instead of compiling.  Files that do not load are compiled afresh and
+    // replaced.
+    std::string co_base;
     if (const char* dir = getenv("PROJ_CACHE_DIR")) {
         if (*dir) {
             char file[64];
-            snprintf(file, sizeof file, "/proj-%016llx.co", (unsigned long long)p->key);
-            co_path = std::string(dir) + file;
+            snprintf(file, sizeof file, "/proj-%016llx", (unsigned long long)p->key);
+            co_base = std::string(dir) + file;
         }
     }
-    p->code_cache = co_path.empty() ? "off" : "miss";
-    if (!co_path.empty()) {
-        std::ifstream f(co_path, std::ios::binary);
-        if (f) {
-            auto buf = std::make_shared<std::vector<char>>((std::istreambuf_iterator<char>(f)),
+    auto co_path = [&](size_t g) { return co_base + ".m" + std::to_string(g) + ".co"; };
+    auto unload_all = [&]() {
+        for (hipModule_t m : p->modules)
+            if (m) (void)hipModuleUnload(m);
+        p->modules.clear();
+        p->module = nullptr;
+    };
+    p->code_cache = co_base.empty() ? "off" : "miss";
+    if (!co_base.empty()) {
+        std::vector<std::shared_ptr<std::vector<char>>> cached(msrcs.size());
+        bool all = true, any = false;
+        for (size_t g = 0; g < msrcs.size(); ++g) {
+            std::ifstream f(co_path(g), std::ios::binary);
+            if (!f) { all = false; continue; }
+            any = true;
+            cached[g] = std::make_shared<std::vector<char>>((std::istreambuf_iterator<char>(f)),
                                                             std::istreambuf_iterator<char>());
-            if (whole_elf64(*buf) && hipModuleLoadData(&p->module, buf->data()) == hipSuccess) {
-                code = buf;
+            if (!whole_elf64(*cached[g])) all = false;
+        }
+        if (all) {
+            for (size_t g = 0; g < msrcs.size() && all; ++g) {
+                hipModule_t m = nullptr;
+                if (hipModuleLoadData(&m, cached[g]->data()) != hipSuccess) {
+                    (void)hipGetLastError();
+                    all = false;
+                } else {
+                    p->modules.push_back(m);
+                }
+            }
+            if (all) {
+                codes = cached;
                 p->code_cache = "hit";
             } else {
-                (void)hipGetLastError();
-                p->module = nullptr;
-                p->code_cache = "stale";
+                unload_all();
             }
         }
+        if (!all && any) p->code_cache = "stale";
     }
-    // write the compiled module to the cache file (a temporary file renamed
-    // into place, so readers never see a partial one)
+    // write the compiled modules to the cache (temporary files renamed into
+    // place, so readers never see a partial one)
     auto store_code = [&]() {
-        if (co_path.empty()) return;
-        const std::string tmp = co_path + ".tmp";
-        bool ok = false;
-        {
-            std::ofstream f(tmp, std::ios::binary);
-            ok = f && f.write(code->data(), code->size());
+        if (co_base.empty()) return;
+        for (size_t g = 0; g < codes.size(); ++g) {
+            const std::string tmp = co_path(g) + ".tmp";
+            bool ok = false;
+            {
+                std::ofstream f(tmp, std::ios::binary);
+                ok = f && f.write(codes[g]->data(), (std::streamsize)codes[g]->size());
+            }
+            if (!ok || std::rename(tmp.c_str(), co_path(g).c_str()) != 0) std::remove(tmp.c_str());
         }
-        if (!ok || std::rename(tmp.c_str(), co_path.c_str()) != 0) std::remove(tmp.c_str());
     };
-    if (!code) {
-        if ((rc = compile_source(src, p->arch, name, &code))) return rc;
+    auto load_all = [&]() -> int {
+        for (size_t g = 0; g < codes.size(); ++g) {
+            hipModule_t m = nullptr;
+            HIP_TRY(hipModuleLoadData(&m, codes[g]->data()));
+            p->modules.push_back(m);
+        }
+        p->module = p->modules[0];
+        return PROJ_OK;
+    };
+    if (codes.empty()) {
+        if ((rc = compile_sources(msrcs, p->arch, name, &codes))) return rc;
         store_code();
     }
     p->compile_s = now_s() - t0;
-    p->code_bytes = code->size();
+    p->code_bytes = 0;
+    for (const auto& c : codes) p->code_bytes += c->size();
     if (const char* dir = getenv("PROJ_DUMP_DIR")) {
         if (*dir) {
-            std::string base = std::string(dir) + "/" + name;
-            std::ofstream(base, std::ios::binary) << src;
-            std::ofstream(base + "." + p->arch + ".co", std::ios::binary).write(code->data(), code->size());
+            const std::string base = std::string(dir) + "/" + name;
+            std::ofstream(base + ".hip", std::ios::binary) << src;
+            for (size_t g = 0; g < codes.size(); ++g)
+                std::ofstream(base + ".m" + std::to_string(g) + "." + p->arch + ".co", std::ios::binary)
+                    .write(codes[g]->data(), (std::streamsize)codes[g]->size());
         }
     }
-    if (!p->module) HIP_TRY(hipModuleLoadData(&p->module, code->data()));
-    // every kernel the plan launches, from the loaded module
+    if (p->modules.empty()) {
+        if ((rc = load_all())) return rc;
+    } else {
+        p->module = p->modules[0];
+    }
+    // every kernel the plan launches, from the loaded modules
     auto bind = [&]() -> int {
         HIP_TRY(hipModuleGetFunction(&p->f_pack, p->module, "proj_pack_panels"));
         if (p->pro) HIP_TRY(hipModuleGetFunction(&p->f_norm, p->module, "proj_rmsnorm_rows"));
         for (Candidate& c : p->cands) {
-            HIP_TRY(hipModuleGetFunction(&c.fn, p->module, c.name.c_str()));
+            HIP_TRY(hipModuleGetFunction(&c.fn, p->modules[c.module], c.name.c_str()));
             if (!c.reduce_name.empty())
-                HIP_TRY(hipModuleGetFunction(&c.reduce_fn, p->module, c.reduce_name.c_str()));
+                HIP_TRY(hipModuleGetFunction(&c.reduce_fn, p->modules[c.module], c.reduce_name.c_str()));
         }
         return PROJ_OK;
     };
     if ((rc = bind())) {
         if (p->code_cache != "hit") return rc;
-        // a cached module that lacks a kernel: compile afresh and replace the file
+        // cached modules that lack a kernel: compile afresh and replace the files
         (void)hipGetLastError();
-        (void)hipModuleUnload(p->module);
-        p->module = nullptr;
+        unload_all();
         p->code_cache = "stale";
-        if ((rc = compile_source(src, p->arch, name, &code))) return rc;
+        if ((rc = compile_sources(msrcs, p->arch, name, &codes))) return rc;
         store_code();
-        p->code_bytes = code->size();
-        HIP_TRY(hipModuleLoadData(&p->module, code->data()));
+        p->code_bytes = 0;
+        for (const auto& c : codes) p->code_bytes += c->size();
+        if ((rc = load_all())) return rc;
         if ((rc = bind())) return rc;
     }
     if (p->pro) {
@@ -959,8 +1157,8 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
         }
     }
     char line[256];
-    snprintf(line, sizeof line, "[proj] %lldx%lld %s: %zu candidates %s for %s in %.2f s (%zu bytes)",
-             (long long)N, (long long)K, dtype ? "bf16" : "f32", p->cands.size(),
+    snprintf(line, sizeof line, "[proj] %lldx%lld %s: %zu candidates in %zu modules %s for %s in %.2f s (%zu bytes)",
+             (long long)N, (long long)K, dtype ? "bf16" : "f32", p->cands.size(), p->modules.size(),
              p->code_cache == "hit" ? "loaded from the code cache" : "compiled", p->arch.c_str(), p->compile_s,
              p->code_bytes);
     plog(p.get(), line);
@@ -982,7 +1180,8 @@ void destroy_plan(proj_plan* p)
     if (p->ws) (void)hipFree(p->ws);
     if (p->gu) (void)hipFree(p->gu);
     if (p->xn) (void)hipFree(p->xn);
-    if (p->module) (void)hipModuleUnload(p->module);
+    for (hipModule_t m : p->modules)
+        if (m) (void)hipModuleUnload(m);
     if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
     delete p;
 }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <memory>
 #include <string>
 #include <algorithm>
 #include <vector>
@@ -40,6 +41,7 @@ struct Candidate {
     int TAILS = 1;   // >1: whole tiles plus a tail split TAILS ways along K
     int ROUND = 0;   // workgroups the device runs at once (CU count x blocks per CU)
 
+    int module = 0;            // index of the compiled module that holds it
     std::string name;          // extern "C" wrapper name in the generated module
     std::string reduce_name;   // split-K reduce kernel (empty if SK == 1)
     int threads = 256;
@@ -92,6 +94,23 @@ std::vector<Candidate> enumerate_candidates(int64_t N, int64_t K, int cus, int f
 std::string emit_source(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
                         const std::vector<Candidate>& cands, int fusion = 0, float norm_eps = 0.f);
 
+// The same translation unit cut into at most `max_modules` modules that hipRTC
+// compiles independently (in parallel processes): each module holds the
+// prelude and the wrappers of some candidates, module 0 also the support
+// kernels.  Sets each candidate's `module`.  The cut depends only on the
+// candidate list and max_modules.
+std::vector<std::string> emit_module_sources(int64_t N, int64_t K, int dtype, const std::string& arch, int cus,
+                                             std::vector<Candidate>& cands, int fusion, float norm_eps,
+                                             int max_modules);
+constexpr int kMaxModules = 16;
+
+// Compile HIP sources for `arch` with hipRTC, one code object each, in up to
+// PROJ_RTC_JOBS child processes (proj_rtc, beside libproj.so) when there are
+// several, else in this process; code objects already compiled in this
+// process are reused.  PROJ_ECOMPILE with hipRTC's log on failure.
+int compile_sources(const std::vector<std::string>& srcs, const std::string& arch, const std::string& name,
+                    std::vector<std::shared_ptr<std::vector<char>>>* codes);
+
 // Compute units assumed when no device is queried (MI355X).
 constexpr int kDefaultCUs = 256;
 
@@ -131,7 +150,8 @@ struct proj_plan {
     int64_t NO = 0;     // columns of Y: N, or N/2 with the SwiGLU epilogue
     int device = -1;
     std::string arch;
-    hipModule_t module = nullptr;
+    hipModule_t module = nullptr;          // modules[0]: the support kernels and some candidates
+    std::vector<hipModule_t> modules;      // every compiled module of the plan
     std::vector<proj::Candidate> cands;
     int choice[proj::kNumBuckets];
     double choice_us[proj::kNumBuckets];

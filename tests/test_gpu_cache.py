@@ -51,10 +51,11 @@ def test_cache_miss_hit_and_stale(tmp_path, monkeypatch):
 
 
 def test_compiled_module_cache(tmp_path, monkeypatch):
-    """With PROJ_CACHE_DIR the compiled module is kept under the plan's key: the
-    next plan of that key loads it instead of compiling; a file that is not a
-    loadable module is reported stale, compiled afresh and replaced; the plan
-    computes the same result either way."""
+    """With PROJ_CACHE_DIR the compiled modules are kept under the plan's key
+    (one file per module): the next plan of that key loads them instead of
+    compiling; a file that is not a loadable module makes the set stale, so it
+    is compiled afresh and replaced; the plan computes the same result either
+    way."""
     import numpy as np
     import oracle
     import synth
@@ -74,8 +75,12 @@ def test_compiled_module_cache(tmp_path, monkeypatch):
     p1 = Plan(N, K, "f32")
     d1 = p1.describe()
     assert d1["code_cache"] == "miss"
-    co = d1["cache_path"][:-len(".txt")] + ".co"
-    assert os.path.getsize(co) == d1["code_bytes"]
+    base = d1["cache_path"][:-len(".txt")]
+    files = [f"{base}.m{g}.co" for g in range(d1["modules"])]
+    assert d1["modules"] > 1
+    assert sum(os.path.getsize(f) for f in files) == d1["code_bytes"]
+    co = files[-1]
+    size_last = os.path.getsize(co)
     y1 = run(p1)
     p2 = Plan(N, K, "f32")
     assert p2.describe()["code_cache"] == "hit"
@@ -83,6 +88,6 @@ def test_compiled_module_cache(tmp_path, monkeypatch):
     open(co, "wb").write(b"not a code object")
     p3 = Plan(N, K, "f32")
     assert p3.describe()["code_cache"] == "stale"
-    assert os.path.getsize(co) == d1["code_bytes"], "the stale file was not replaced"
+    assert os.path.getsize(co) == size_last, "the stale file was not replaced"
     assert np.array_equal(run(p3).view(np.uint32), y1.view(np.uint32))
     G.log(f"  code cache: miss {d1['compile_s']:.2f} s, then hit and stale handled")

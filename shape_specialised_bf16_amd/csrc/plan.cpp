@@ -37,6 +37,7 @@
 #include <sstream>
 
 #include "proj.h"
+#include "gate_rule.h"
 #include "proj_internal.h"
 #include "rtc.h"
 
@@ -355,11 +356,6 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
 }
 
 // ---------------------------------------------------------------- the tuner
-struct CheckStats {
-    uint32_t bad, unwritten, guard, max_err, max_ref, pad;
-    uint64_t hash;   // of the whole output (rows < M) on the integer probe
-};
-
 static float bits_f(uint32_t u)
 {
     float f;
@@ -874,18 +870,11 @@ int tune_plan(proj_plan* p)
                     CheckStats cs{};
                     int r2 = T.run_and_check(c, M, integer != 0, nrows, &cs);
                     if (r2) return r2;
-                    const bool differs = integer && have_base && cs.hash != base_hash;
-                    if (cs.bad || cs.unwritten || cs.guard || differs) {
-                        snprintf(line, sizeof line,
-                                 "[autotune] proj %lldx%lld %lld rows at %lld: wrong against ref, never picked: %s "
-                                 "(%lld rows%s: max err %.3e of %.3e; %u outside tolerance, %u unwritten, %u "
-                                 "written past M%s)",
-                                 (long long)p->N, (long long)p->K, (long long)br.hi, (long long)br.hi,
-                                 c.name.c_str(), (long long)M, integer ? ", integer probe" : "",
-                                 bits_f(cs.max_err), bits_f(cs.max_ref), cs.bad, cs.unwritten, cs.guard,
-                                 differs ? "; whole output differs from the plain kernel's" : "");
-                        plog(p, line);
-                        p->rejected[b].push_back({ci, line});
+                    const std::string why =
+                        gate_reject_line(cs, integer != 0, have_base, base_hash, p->N, p->K, br.hi, c.name, M);
+                    if (!why.empty()) {
+                        plog(p, why);
+                        p->rejected[b].push_back({ci, why});
                         return 1;
                     }
                 }

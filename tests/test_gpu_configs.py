@@ -51,27 +51,40 @@ def test_prefill_4b_layer(wl, pi, dtype):
                       (0x7FC1 if dtype == "bf16" else 0x7FC00001)), "row M was written"
 
 
-def test_long_prompt_blocks_and_head():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_long_prompt_blocks_and_head(dtype):
     """8192 prompt rows as 8 blocks of 1024 through each 4B-like projection, then
-    the 151936 x 2560 head on the last row only (caller-side block driver)."""
+    the 151936 x 2560 head on the last row only (caller-side block driver).
+    bf16 is the configuration the benchmark times: bf16 plans for the four
+    projections at M = 1024 per call, the f32 head plan at M = 1.  Sampled rows
+    cover every block's first and last row, the 256-row tile edges inside a
+    block and random rows."""
     import torch
     cfg = synth.workload("long_prompt_4b_8192x1024")
     rows_total, block = cfg.extra["prompt_rows"], cfg.extra["block"]
+    rows = set()
+    for b in range(rows_total // block):
+        rows.update({b * block, b * block + block - 1})
+    rows.update({255, 256, 511, 512, 767, 768, 1025, 4097, 5000})
+    rng = np.random.default_rng(1024)
+    rows.update(int(r) for r in rng.integers(0, rows_total, size=4))
+    rows = sorted(rows)
     for pi, p in enumerate(cfg.projections):
         W = synth.weights(cfg, pi)
-        plan = G.plan(p.N, p.K, "f32")
         if p.name == "head":
+            plan = G.plan(p.N, p.K, "f32")
             X = synth.activations(cfg, pi, 1)
             Y = plan.run(G.dev(X), G.dev(W))
             G.check_against_oracle(Y, X, W, "f32", label=f"head {p.N}x{p.K} {plan.choice(1)}")
             continue
+        plan = G.plan(p.N, p.K, dtype)
         X = synth.activations(cfg, pi, rows_total)
         Xd, Wd = G.dev(X), G.dev(W)
-        Y = torch.empty((rows_total, p.N), dtype=torch.float32, device="cuda")
+        Y = G.empty_out(rows_total, p.N, dtype)
         for b in range(rows_total // block):
             plan.run(Xd[b * block:(b + 1) * block], Wd, Y[b * block:(b + 1) * block])
-        rows = sorted({0, 1023, 1024, 4095, 4096, 5000, 8191})
-        G.check_against_oracle(Y, X, W, "f32", rows=rows, label=f"{p.name} {p.N}x{p.K} blocks of 1024")
+        G.check_against_oracle(Y, X, W, dtype, rows=rows,
+                               label=f"{p.name} {p.N}x{p.K} blocks of {block} ({plan.choice(block)})")
 
 
 @pytest.mark.parametrize("wl,pi", _proj_cases("layer_27b"))

@@ -187,6 +187,30 @@ int proj_run_ex(const proj_plan* plan, const void* X, const void* W, void* Y, in
                 hipStream_t stream);
 
 /*
+ * proj_run_ex for callers that cannot allocate device memory while they run:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same kernels, same results bit for bit, same arguments and
+ * errors as proj_run_ex (row-major W; gamma for a PROJ_PRO_RMSNORM plan), but
+ * the workspace of the tuned kernel for M -- split-K and split-tail partials,
+ * the normalised rows of an unfused RMSNorm candidate, the N-column
+ * intermediate of an unfused SwiGLU candidate -- comes from a static device
+ * array of the library, 64 MiB per GPU, instead of from the plan; the call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * The array is looked up on a device once, when the first plan is created
+ * there, and is held until the process ends.  A call whose kernel needs more
+ * than 64 MiB at its M (e.g. split tails of the widest shapes at thousands of
+ * rows) returns PROJ_EINVAL naming the bytes needed, with nothing enqueued:
+ * use fewer rows per call.  Nothing in the array needs to start at zero: every
+ * kernel writes the partials it reads.  All proj_run_noalloc calls on one GPU
+ * share its array, so calls that overlap on the device (different streams
+ * without ordering, overlapping graph replays) race; calls on one stream are
+ * ordered.  They do not share the plan's own workspace, so they do not race
+ * with proj_run / proj_run_ex calls of the plan.
+ */
+int proj_run_noalloc(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, const float* gamma,
+                     hipStream_t stream);
+
+/*
  * Load-time weight repacking.  Enqueue the copy of the row-major weights W
  * [N, K] (bf16 bit patterns) into Wp, the same N * K values in the packed
  * layout: W is cut into panels of 128 consecutive rows, each panel is stored

@@ -42,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "proj_plan_candidate_max_m", "proj_run_candidate", "proj_plan_choice", "proj_probe_read",
     "proj_round_bf16", "proj_plan_create_ex", "proj_emit_source_ex", "proj_swiglu", "proj_run_ex",
     "proj_run_candidate_ex", "proj_rmsnorm", "proj_pack_weights", "proj_run_packed", "proj_compile_only",
+    "proj_run_noalloc",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -101,6 +102,8 @@ _lib.proj_pack_weights.argtypes = [_i64, _i64, _p, _p, _p]
 _lib.proj_pack_weights.restype = ctypes.c_int
 _lib.proj_run_packed.argtypes = [_p, _p, _p, _p, _i64, _p, _p]
 _lib.proj_run_packed.restype = ctypes.c_int
+_lib.proj_run_noalloc.argtypes = [_p, _p, _p, _p, _i64, _p, _p]
+_lib.proj_run_noalloc.restype = ctypes.c_int
 _lib.proj_compile_only.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_char_p,
                                    ctypes.POINTER(ctypes.c_double)]
 _lib.proj_compile_only.restype = ctypes.c_int
@@ -263,6 +266,16 @@ class Plan:
         M, Y = self._prep(X, W, Y)
         _check(_lib.proj_run_ex(self._h, X.data_ptr(), W.data_ptr(), Y.data_ptr(), M, self._gamma(gamma),
                                 _stream_handle(stream)), "proj_run_ex")
+        return Y
+
+    def run_noalloc(self, X, W, Y, stream=None, gamma=None):
+        """run() through proj_run_noalloc: the kernels' workspace is the
+        library's static scratch, and nothing is allocated (Y must be given)."""
+        if Y is None:
+            raise ValueError("run_noalloc: Y must be given (nothing is allocated)")
+        M, Y = self._prep(X, W, Y)
+        _check(_lib.proj_run_noalloc(self._h, X.data_ptr(), W.data_ptr(), Y.data_ptr(), M, self._gamma(gamma),
+                                     _stream_handle(stream)), "proj_run_noalloc")
         return Y
 
     def run_packed(self, X, Wp, Y=None, stream=None, gamma=None):

@@ -20,7 +20,7 @@ int device_arch(int dev, std::string* arch, int* cus);
 int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, proj_plan** out);
 void destroy_plan(proj_plan* p);
 int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream,
-             const float* gamma, bool packed);
+             const float* gamma, bool packed, bool noalloc = false);
 int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M);
 int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y,
                      int64_t M, hipStream_t stream, const float* gamma);
@@ -154,6 +154,12 @@ int proj_run_packed(const proj_plan* plan, const void* X, const void* Wp, void* 
                     hipStream_t stream)
 {
     return run_plan(plan, X, Wp, Y, M, stream, gamma, true);
+}
+
+int proj_run_noalloc(const proj_plan* plan, const void* X, const void* W, void* Y, int64_t M, const float* gamma,
+                     hipStream_t stream)
+{
+    return run_plan(plan, X, W, Y, M, stream, gamma, false, true);
 }
 
 int proj_pack_weights(int64_t N, int64_t K, const void* W, void* Wp, hipStream_t stream)

@@ -298,34 +298,50 @@ static LaunchGeom geom(const Candidate& c, int64_t N, int64_t NO, int64_t M)
     }
 }
 
-// Enqueue candidate c for one block of M <= c.max_m rows.
-int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y,
-                     int64_t M, hipStream_t stream, const float* gamma)
+// The plan's own workspace.
+static Workspace plan_workspace(const proj_plan* p)
+{
+    Workspace w;
+    w.ws = (float*)p->ws;
+    w.ws_bytes = p->ws_bytes;
+    w.xn = p->xn;
+    w.xn_rows = p->xn ? kMaxBlockRows : 0;
+    w.gu = p->gu;
+    w.gu_rows = p->gu_rows;
+    return w;
+}
+
+// Enqueue candidate c for one block of M <= c.max_m rows, with workspace wk.
+static int launch_candidate_ws(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y,
+                               int64_t M, hipStream_t stream, const float* gamma, const Workspace& wk)
 {
     if (M > c.max_m) return set_error(PROJ_EINVAL, "M=%lld exceeds %s's limit of %lld rows",
                                       (long long)M, c.name.c_str(), (long long)c.max_m);
-    if (c.ws_bytes(M, p->N) > p->ws_bytes)
-        return set_error(PROJ_EINVAL, "%s needs %zu bytes of split-K workspace at M=%lld, plan has %zu",
-                         c.name.c_str(), c.ws_bytes(M, p->N), (long long)M, p->ws_bytes);
-    if (c.UF && M > p->gu_rows)
-        return set_error(PROJ_EINVAL, "%s needs %lld rows of the SwiGLU intermediate, plan has %lld", c.name.c_str(),
-                         (long long)M, (long long)p->gu_rows);
+    if (c.ws_bytes(M, p->N) > wk.ws_bytes)
+        return set_error(PROJ_EINVAL, "%s needs %zu bytes of split-K workspace at M=%lld, has %zu",
+                         c.name.c_str(), c.ws_bytes(M, p->N), (long long)M, wk.ws_bytes);
+    if (c.UF && M > wk.gu_rows)
+        return set_error(PROJ_EINVAL, "%s needs %lld rows of the SwiGLU intermediate, has %lld", c.name.c_str(),
+                         (long long)M, (long long)wk.gu_rows);
+    if (p->pro && !c.PRO && M > wk.xn_rows)
+        return set_error(PROJ_EINVAL, "%s needs %lld rows of normalised X, has %lld", c.name.c_str(),
+                         (long long)M, (long long)wk.xn_rows);
     const LaunchGeom g = geom(c, p->N, p->NO, M);
     const void* x = X;
     const void* w = W;
-    void* y = c.UF ? p->gu : Y;    // unfused SwiGLU: the N-column projection goes to the intermediate
-    float* ws = (float*)p->ws;
+    void* y = c.UF ? wk.gu : Y;    // unfused SwiGLU: the N-column projection goes to the intermediate
+    float* ws = wk.ws;
     const float* gam = gamma;
     int m = (int)M;
     if (p->pro && !c.PRO) {
         // unfused: the norm kernel writes the normalised rows into the workspace
         const void* xin = X;
-        void* xo = p->xn;
+        void* xo = wk.xn;
         long kk = (long)p->K;
         float eps = p->eps;
         void* nargs[] = {&xin, &gam, &xo, &kk, &eps};
         HIP_TRY(hipModuleLaunchKernel(p->f_norm, (unsigned)M, 1, 1, 256, 1, 1, 0, stream, nargs, nullptr));
-        x = p->xn;
+        x = wk.xn;
     }
     void* args[] = {&x, &w, &y, &ws, &gam, &m};
     HIP_TRY(hipModuleLaunchKernel(c.fn, g.gx, g.gy, 1, g.threads, 1, 1, 0, stream, args, nullptr));
@@ -345,13 +361,47 @@ int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, cons
     }
     if (c.UF) {
         // the separate activation kernel: Y[M, N/2] = silu(gate) * up of the intermediate
-        const void* gsrc = p->gu;
+        const void* gsrc = wk.gu;
         void* h = Y;
         long mm = (long)M, nn = (long)p->N;
         void* sargs[] = {&gsrc, &h, &mm, &nn};
         const unsigned gx = (unsigned)std::min<int64_t>(65536, (M * (p->N / 2) + 255) / 256);
         HIP_TRY(hipModuleLaunchKernel(p->f_swiglu, gx, 1, 1, 256, 1, 1, 0, stream, sargs, nullptr));
     }
+    return PROJ_OK;
+}
+
+int launch_candidate(const proj_plan* p, const Candidate& c, const void* X, const void* W, void* Y, int64_t M,
+                     hipStream_t stream, const float* gamma)
+{
+    return launch_candidate_ws(p, c, X, W, Y, M, stream, gamma, plan_workspace(p));
+}
+
+// The workspace candidate c needs at M rows, carved from the static scratch:
+// split partials, then normalised rows, then the SwiGLU intermediate, each
+// starting on a 256-byte boundary.  PROJ_EINVAL if it does not fit.
+static int scratch_workspace(const proj_plan* p, const Candidate& c, int64_t M, Workspace* wk)
+{
+    void* base = nullptr;
+    int rc = scratch_address(p->device, &base);
+    if (rc) return rc;
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const size_t ws = up(c.ws_bytes(M, p->N));
+    const size_t xn = (p->pro && !c.PRO) ? up((size_t)M * p->K * 2) : 0;
+    const size_t gu = c.UF ? up((size_t)M * p->N * (p->dtype == PROJ_OUT_BF16 ? 2 : 4)) : 0;
+    const size_t cap = scratch_capacity();
+    if (ws + xn + gu > cap)
+        return set_error(PROJ_EINVAL,
+                         "proj_run_noalloc: %s needs %zu bytes of scratch at M=%lld (partials %zu, normalised rows "
+                         "%zu, SwiGLU intermediate %zu); the static scratch holds %zu: use fewer rows per call",
+                         c.name.c_str(), ws + xn + gu, (long long)M, ws, xn, gu, cap);
+    char* b = (char*)base;
+    wk->ws = ws ? (float*)b : nullptr;
+    wk->ws_bytes = ws;
+    wk->xn = xn ? b + ws : nullptr;
+    wk->xn_rows = xn ? M : 0;
+    wk->gu = gu ? b + ws + xn : nullptr;
+    wk->gu_rows = gu ? M : 0;
     return PROJ_OK;
 }
 
@@ -1008,6 +1058,17 @@ int create_plan(int64_t N, int64_t K, int dtype, int fusion, float norm_eps, pro
     if ((rc = device_arch(p->device, &p->arch, &cus))) return rc;
     for (int b = 0; b < kNumBuckets; ++b) p->choice[b] = -1, p->choice_us[b] = -1;
 
+    {
+        // set-up of the static scratch on this device (proj_run_noalloc), with
+        // the device current; a failure here only matters to proj_run_noalloc,
+        // which looks again and reports it
+        void* sp = nullptr;
+        if (scratch_address(p->device, &sp) != PROJ_OK) {
+            plog(p.get(), "[proj] static scratch not available: " + g_last_error);
+            g_last_error.clear();
+            (void)hipGetLastError();
+        }
+    }
     p->cands = enumerate_candidates(N, K, cus, fusion);
     // the whole translation unit keys the caches and is what PROJ_DUMP_DIR
     // writes; it is compiled as modules, each holding some candidates
@@ -1199,7 +1260,7 @@ int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, in
 }
 
 int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t M, hipStream_t stream,
-             const float* gamma, bool packed)
+             const float* gamma, bool packed, bool noalloc)
 {
     if (p && p->wpack != (packed ? 1 : 0))
         return set_error(PROJ_EINVAL, packed ? "this plan reads row-major weights: use proj_run or proj_run_ex"
@@ -1209,11 +1270,21 @@ int run_plan(const proj_plan* p, const void* X, const void* W, void* Y, int64_t 
     if (p->pro && !gamma) return set_error(PROJ_EINVAL, "this plan has the RMSNorm prologue: gamma is required");
     if (p->pro && ((uintptr_t)gamma & 15)) return set_error(PROJ_EINVAL, "gamma must be 16-byte aligned");
     const size_t ysz = p->dtype == PROJ_OUT_BF16 ? 2 : 4;
+    if (noalloc) {
+        // every block must fit the scratch before anything is enqueued
+        for (int64_t off = 0; off < M; off += kMaxBlockRows) {
+            const int64_t m = std::min<int64_t>(kMaxBlockRows, M - off);
+            Workspace wk;
+            if ((rc = scratch_workspace(p, p->cands[p->choice[bucket_of(m)]], m, &wk))) return rc;
+        }
+    }
     for (int64_t off = 0; off < M; off += kMaxBlockRows) {
         const int64_t m = std::min<int64_t>(kMaxBlockRows, M - off);
         const Candidate& c = p->cands[p->choice[bucket_of(m)]];
-        rc = launch_candidate(p, c, (const char*)X + (size_t)off * p->K * 2, W, (char*)Y + (size_t)off * p->NO * ysz,
-                              m, stream, gamma);
+        Workspace wk = plan_workspace(p);
+        if (noalloc && (rc = scratch_workspace(p, c, m, &wk))) return rc;
+        rc = launch_candidate_ws(p, c, (const char*)X + (size_t)off * p->K * 2, W, (char*)Y + (size_t)off * p->NO * ysz,
+                                 m, stream, gamma, wk);
         if (rc) return rc;
     }
     return PROJ_OK;

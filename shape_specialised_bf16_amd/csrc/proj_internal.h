@@ -128,6 +128,25 @@ extern const char* const kSupportSrc;
 // Bucket index for M >= 1 (M > kMaxBlockRows maps to the last bucket).
 int bucket_of(int64_t M);
 
+// Device memory a launch may use besides X, W and Y: the f32 partials of a
+// split-K or split-tail GEMM (`ws`), the normalised rows of an unfused
+// RMSNorm candidate (`xn`) and the N-column projection of an unfused SwiGLU
+// candidate (`gu`).  Either the plan's own buffers, allocated when the plan
+// is created, or pieces of the library's static scratch (proj_run_noalloc).
+struct Workspace {
+    float* ws = nullptr;
+    size_t ws_bytes = 0;
+    void* xn = nullptr;
+    int64_t xn_rows = 0;
+    void* gu = nullptr;
+    int64_t gu_rows = 0;
+};
+
+// The static scratch (scratch.hip): its size, and its address on `device`
+// (looked up once per device, with that device current).
+size_t scratch_capacity();
+int scratch_address(int device, void** ptr);
+
 }  // namespace proj
 
 struct proj_plan {

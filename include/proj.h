@@ -89,8 +89,8 @@ enum {
  * every cached choice through the same validation gate instead of timing
  * candidates, and tunes afresh any bucket whose cached choice is unknown or
  * fails the gate (the cache the pages propose, and doubt because machine state
- * drifts: "#004 the same compiler on Apple's chips", section "Reproducing at
- * home").  The compiled module is kept under the same key (<dir>/proj-<key>.co,
+ * drifts: "#004 the same compiler on Apple's chips", section "So, does it start
+ * up more slowly?").  The compiled module is kept under the same key (<dir>/proj-<key>.co,
  * the key also covering the compile options), so such a plan skips hipRTC as
  * well; a file that does not load is compiled afresh and replaced.
  * proj_plan_describe reports "cache" and "code_cache": off, miss, hit or stale.
@@ -100,10 +100,10 @@ proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
 /*
  * Like proj_plan_create, with work folded into the plan's kernels or with
  * weights in the packed layout; `flags` is PROJ_EPI_NONE or an OR of the flags
- * below.  The pages fold exactly these two
- * ("#004 the same compiler on Apple's chips", section "Decode": the norms into
- * the projection that follows them, the SwiGLU into the gate_up projection),
- * each with the same bits as the kernels it replaces.
+ * below.  The pages fuse exactly these two: each RMSNorm into the projection
+ * after it and the SwiGLU activation into the gate_up projection, with results
+ * identical bit for bit to the unfused kernels ("#004 the same compiler on
+ * Apple's chips", section "Decode").
  *
  * PROJ_EPI_SWIGLU: W is a fused gate_up matrix, rows [0, N/2) the gate
  * projection and rows [N/2, N) the up projection (N even), and the plan's Y is
@@ -117,7 +117,7 @@ proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);
  * while writing N/2 columns instead of N and skipping one launch and the round
  * trip of the N-column intermediate: the SwiGLU folded into the gate_up
  * projection of "#004 the same compiler on Apple's chips", section "Decode"
- * (each fusion gives the same bits as the kernels it replaces), and of "#002
+ * (a fusion there changes no output bit), and of "#002
  * le meme compilateur sur un GPU", section "Emettre pour un GPU" (the
  * activation fused with the projection that produces its input).  The fused
  * candidates come from the kernel families that have the epilogue (vector

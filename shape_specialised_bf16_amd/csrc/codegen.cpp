@@ -68,16 +68,21 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     const int64_t CH = K / 8;  // 16-byte chunks per row
 
     // ---- vector-ALU GEMV: (R rows per wave, S waves splitting K), MMAX rows of X
-    struct VG { int R, S, MMAX, NT; };
+    struct VG { int R, S, MMAX, NT, NW; };
     // (listed in order of preference: the tuner keeps an earlier candidate unless
-    //  a later one is clearly faster)
-    const VG vgs[] = {{2, 1, 1, 1}, {1, 1, 1, 1}, {4, 1, 1, 1}, {2, 1, 1, 0},
-                      {1, 4, 1, 1}, {2, 4, 1, 1}, {1, 1, 16, 1}, {2, 1, 16, 1}, {1, 4, 16, 1}};
+    //  a later one is clearly faster).  NW: waves per block; 5 and 8 make a whole
+    //  number of blocks per CU where 4 does not (5120 rows in waves of 2 rows:
+    //  640 blocks of 4 waves, 2.5 per CU; 512 blocks of 5 waves, 2 per CU).
+    const VG vgs[] = {{2, 1, 1, 1, 4}, {1, 1, 1, 1, 4}, {4, 1, 1, 1, 4}, {2, 1, 1, 0, 4},
+                      {1, 4, 1, 1, 4}, {2, 4, 1, 1, 4}, {1, 1, 16, 1, 4}, {2, 1, 16, 1, 4}, {1, 4, 16, 1, 4},
+                      {2, 1, 1, 1, 5}, {1, 1, 1, 1, 5}, {4, 1, 1, 1, 5}, {2, 1, 1, 1, 8}, {1, 2, 1, 1, 8}};
     for (const VG& v : vgs) {
         if (CH % v.S) continue;
         if (epi && v.R % 2) continue;   // the fused epilogue pairs gate and up rows in a wave
-        const int RG = 4 / v.S;
+        const int RG = v.NW / v.S;
         if (N % (v.R * RG)) continue;
+        // other wave counts only where they change the block count per CU
+        if (v.NW != 4 && (N / (v.R * RG)) % cus != 0) continue;
         const int64_t trips = CH / v.S / 64;
         int U = 1;
         for (int u : {4, 2}) {
@@ -85,10 +90,11 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         }
         Candidate c;
         c.fam = Family::GemvValu;
-        c.R = v.R; c.S = v.S; c.MMAX = v.MMAX; c.U = U; c.NT = v.NT;
-        c.threads = 256;
+        c.R = v.R; c.S = v.S; c.MMAX = v.MMAX; c.U = U; c.NT = v.NT; c.NW = v.NW;
+        c.threads = 64 * v.NW;
         c.max_m = v.MMAX;
-        c.name = fmt("gemv_valu_r%d_s%d_m%d_u%d_nt%d", c.R, c.S, c.MMAX, c.U, c.NT);
+        const std::string wsuf = v.NW != 4 ? fmt("_w%d", v.NW) : std::string();
+        c.name = fmt("gemv_valu_r%d_s%d_m%d_u%d_nt%d", c.R, c.S, c.MMAX, c.U, c.NT) + wsuf;
         out.push_back(c);
         // the same with pipelined batches: the largest U that still leaves a
         // wave two batches or more
@@ -99,7 +105,7 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
             if (Up) {
                 c.U = Up;
                 c.P = 1;
-                c.name = fmt("gemv_valu_r%d_s%d_m%d_u%d_nt%d_p", c.R, c.S, c.MMAX, c.U, c.NT);
+                c.name = fmt("gemv_valu_r%d_s%d_m%d_u%d_nt%d_p", c.R, c.S, c.MMAX, c.U, c.NT) + wsuf;
                 out.push_back(c);
             }
         }
@@ -111,7 +117,7 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     if (pro) {
         const size_t n = out.size();
         for (size_t i = 0; i < n; ++i)
-            if (out[i].fam == Family::GemvValu && out[i].MMAX == 1) {
+            if (out[i].fam == Family::GemvValu && out[i].MMAX == 1 && out[i].NW == 4) {
                 Candidate c = out[i];
                 c.PRO = 1;
                 c.name += "_nf";
@@ -162,7 +168,17 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         {128, 128, 64, 2, 2, 2, 1, 8, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
         {128, 128, 64, 3, 2, 2, 1, 8, 8, 1, {2, 3, 4, 6}, 4},
         {128, 64, 64, 3, 2, 2, 1, 8, 8, 1, {2, 3, 4, 6}, 4},
-        {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 8, 8, 1, {}}};
+        {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 8, 8, 1, {}},
+        // tiles 160 or 192 wide make whole rounds of 256 CUs where the power-of-two
+        // widths leave part of a round: 5120 columns at 2048 rows are 8 x 32
+        // tiles of 256 x 160, 2560 columns 16 x 16 tiles of 128 x 160, 18432
+        // columns 8 x 96 tiles of 256 x 192 (160 = five 32-column MFMA blocks:
+        // one wave column, so four waves of 64 x 160 or 32 x 160)
+        {256, 160, 64, 2, 4, 1, 1, 1, 8, 1, {2}, 3}, {128, 160, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 4},
+        {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 3},
+        // four X and five W buffers: more k-tiles in flight per workgroup for the
+        // few-hundred-row blocks, whose copies wait on HBM
+        {128, 128, 64, 4, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5}, {128, 64, 64, 4, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
         if (wpack && 64 % g.BK) continue;  // panel layout: a k-tile inside one 64-value block
@@ -271,9 +287,9 @@ static void emit_wrappers(std::ostringstream& s, const Candidate& c, int64_t N, 
           << chs << " blocks/slice = " << chs / 64 << " trip(s) of 64 lanes + " << chs % 64
           << " tail lanes, " << wdesc << "\n";
         s << "static_assert(K_BLOCKS16 / " << c.S << " / 64 == " << chs / 64 << ", \"trip count\");\n";
-        s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.name << sig << "\n{ gemv_valu<"
-          << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out << ", "
-          << c.P << ", " << c.PRO << ", " << c.E << ">(X, W, Y, gamma, M); }\n";
+        s << "extern \"C\" __global__ __launch_bounds__(" << 64 * c.NW << ") void " << c.name << sig
+          << "\n{ gemv_valu<" << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out
+          << ", " << c.P << ", " << c.PRO << ", " << c.E << ", " << c.NW << ">(X, W, Y, gamma, M); }\n";
         break;
     }
     case Family::GemvMfma: {

@@ -52,9 +52,9 @@ __device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc)
 }
 
 // SwiGLU of one gate/up pair, silu(g) * u with silu(g) = g / (1 + e^-g), in
-// f32 ("#004 the same compiler on Apple's chips", section "Decode": the SwiGLU
-// folded into the gate_up projection gives the same bits as the separate
-// kernels).  With a bf16 output, g and u are first rounded to bf16 -- the
+// f32 ("#004 the same compiler on Apple's chips", section "Decode": fusing
+// the activation into the gate_up kernel must not change a single output bit
+// against the two separate kernels).  With a bf16 output, g and u are first rounded to bf16 -- the
 // values the projection alone would store -- and the store rounds the product
 // once more; so the fused epilogue and the separate activation kernel run the
 // same operations on the same values.
@@ -71,8 +71,9 @@ __device__ __forceinline__ float swiglu(float g, float u)
 }
 
 // RMSNorm of one bf16 row x[0..K) by a whole block of 256 threads ("#004 the
-// same compiler on Apple's chips", section "Decode": the norm folded into the
-// projection that follows it, with the same bits as the separate kernels).
+// same compiler on Apple's chips", section "Decode": the norm moved inside the
+// next projection's kernel, its output bit-identical to the separate norm
+// kernel followed by the projection).
 // The sum of squares has one fixed order: thread t adds x[k]^2 for k = t,
 // t + 256, ... ascending with f32 FMA, then the 256 partials are added by
 // pairwise halving in LDS; every kernel that normalises a row calls this, so

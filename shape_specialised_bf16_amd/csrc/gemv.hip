@@ -28,28 +28,31 @@
 // With the RMSNorm prologue (PRO == 1, M = 1 only) the block first
 // normalises the X row into LDS with the same dev::rms_scale_block and
 // dev::rms_apply as the separate norm kernel (gamma f32 [K], epsilon NORM_EPS),
-// then reads X from there: the norm folded into the projection that follows
-// it ("#004 the same compiler on Apple's chips", section "Decode").  Each
+// then reads X from there: the norm run inside the next projection's kernel
+// ("#004 the same compiler on Apple's chips", section "Decode").  Each
 // block re-reads the K-element row, the extra traffic the pages name as the
 // reason the fused norm loses on larger models.
 //
-// Block: 256 threads = 4 waves = (4/S) row groups x S K-slices.
-// Grid:  N / (R * 4/S) blocks.
+// Block: NW waves = (NW/S) row groups x S K-slices (NW = 4 by default; other
+// counts let the grid be a whole number of blocks per CU, e.g. 5 waves of 2
+// rows make 512 blocks of 5120 rows: two per CU, all resident at once).
+// Grid:  N / (R * NW/S) blocks.
 // ---------------------------------------------------------------------------
-template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0, int PRO = 0, int E = 0>
+template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0, int PRO = 0, int E = 0, int NW = 4>
 __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* __restrict__ W,
                                           void* __restrict__ Y, const float* __restrict__ gamma, int M)
 {
     constexpr long NO = E ? N / 2 : N;          // columns of Y
     static_assert(PRO == 0 || MMAX == 1, "the fused norm prologue serves M = 1");
-    static_assert(4 % S == 0, "S divides the 4 waves of a block");
+    static_assert(PRO == 0 || NW == 4, "the norm prologue's block reduction takes 256 threads");
+    static_assert(NW % S == 0 && NW >= 1 && NW <= 16, "S divides the NW waves of a block");
     constexpr long CH = K / 8;                  // 16-byte chunks per row
     static_assert(K % 8 == 0 && CH % S == 0, "K slice must be whole chunks");
     constexpr long CHS = CH / S;                // chunks per K-slice
     constexpr long TRIPS = CHS / 64;            // full 64-lane trips per slice
     constexpr int TAIL = (int)(CHS % 64);       // lanes busy in the last, partial trip
     static_assert(U >= 1 && TRIPS % U == 0, "U divides the trip count");
-    constexpr int RG = 4 / S;
+    constexpr int RG = NW / S;
     static_assert(N % (R * RG) == 0, "blocks tile N exactly");
     constexpr int V = R * MMAX;
     constexpr int LV = dev::log2_of<V>::value;
@@ -170,7 +173,7 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
             if (writer && m < M) dev::store1<OUT>(Y, (long)m * NO + n0 + r, sum);
         }
     } else {
-        __shared__ float red[4][V];
+        __shared__ float red[NW][V];
         if (writer) red[wave][idx] = sum;
         __syncthreads();
         if (s == 0 && writer && m < M && (!E || r < R / 2)) {

@@ -4,9 +4,9 @@
 // The tuner follows "#004 the same compiler on Apple's chips" (blog series "On
 // descend d'un cran"): at load time several variants of each kernel are
 // measured per matrix shape and the fastest is kept (section "Catching up on
-// prefill"), but only after each candidate has been run once against a kernel
-// already trusted, on a full block and on a partial block with the output
-// cleared beforehand, and rejected -- with a log line -- when it departs from it
+// prefill"), but a variant is first compared with a kernel known to be right,
+// with the output cleared beforehand, at the bucket's whole block size and at
+// a smaller row count, and a variant that disagrees is logged and never used
 // (section "The night the engine chose wrong").  Here the trusted kernel is a
 // plain one-thread-per-output reference that is itself checked against exact
 // integer arithmetic on the host; the output is cleared to a NaN sentinel
@@ -282,7 +282,7 @@ struct LaunchGeom {
 static LaunchGeom geom(const Candidate& c, int64_t N, int64_t NO, int64_t M)
 {
     switch (c.fam) {
-    case Family::GemvValu: return {(unsigned)(N / (c.R * (4 / c.S))), 1u, 256u};
+    case Family::GemvValu: return {(unsigned)(N / (c.R * (c.NW / c.S))), 1u, (unsigned)(64 * c.NW)};
     case Family::GemvMfma: return {(unsigned)(N / (16 * (4 / c.S))), 1u, 256u};
     case Family::Gemm: {
         if (c.TAILS > 1) {
@@ -722,8 +722,8 @@ static void plog(proj_plan* p, const std::string& line)
 // ---------------------------------------------------------------- tuning cache
 // The choices of a tuned plan, kept in a text file per key (the persistent
 // tuning cache the pages propose -- and doubt, because the machine's state
-// drifts -- in "#004 the same compiler on Apple's chips", section "Reproducing
-// at home").  The key hashes the device (full architecture name, CU count),
+// drifts -- in "#004 the same compiler on Apple's chips", section "So, does it
+// start up more slowly?").  The key hashes the device (full architecture name, CU count),
 // the HIP runtime and driver versions and the complete emitted source, which
 // fixes the shape, output type, epilogue and every candidate's code; so a
 // library or driver change is a different key.  On a hit every cached choice
@@ -977,12 +977,40 @@ int tune_plan(proj_plan* p)
                 double us = 0;
                 if ((rc = T.time_candidate(p->cands[ci], Mfull, reps, &us))) return rc;
                 p->timings[b].push_back({ci, us});
-                // A later candidate must beat the current pick by 4 %: timing
-                // noise between near-equal variants (a few %) then does not flip
-                // the choice from one load to the next (earlier = preferred).
-                if (best_us < 0 || us < best_us * 0.96) {
+                if (best_us < 0 || us < best_us) {
                     best_us = us;
                     best = ci;
+                }
+            }
+            // Finalists: the (at most four) candidates within 5 % of the fastest,
+            // timed again in three interleaved rounds, so that a drifting clock
+            // weighs on all of them alike; the lowest median of the rounds wins,
+            // and a later candidate must beat an earlier one by 1 % (near-equal
+            // variants then do not flip the choice from one load to the next).
+            std::vector<std::pair<double, int>> fin;
+            for (const auto& t : p->timings[b])
+                if (t.second <= best_us * 1.05) fin.push_back({t.second, t.first});
+            std::sort(fin.begin(), fin.end());
+            if (fin.size() > 4) fin.resize(4);
+            if (fin.size() > 1) {
+                std::sort(fin.begin(), fin.end(), [](const std::pair<double, int>& a, const std::pair<double, int>& c) {
+                    return a.second < c.second;   // list order
+                });
+                std::vector<std::vector<double>> rt(fin.size());
+                for (int round = 0; round < 3; ++round)
+                    for (size_t f = 0; f < fin.size(); ++f) {
+                        double us = 0;
+                        if ((rc = T.time_candidate(p->cands[fin[f].second], Mfull, reps, &us))) return rc;
+                        rt[f].push_back(us);
+                    }
+                best_us = -1;
+                for (size_t f = 0; f < fin.size(); ++f) {
+                    std::sort(rt[f].begin(), rt[f].end());
+                    const double med = rt[f][1];
+                    if (best_us < 0 || med < best_us * 0.99) {
+                        best_us = med;
+                        best = fin[f].second;
+                    }
                 }
             }
             std::ostringstream os;

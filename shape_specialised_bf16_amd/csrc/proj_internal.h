@@ -27,6 +27,7 @@ struct Candidate {
     Family fam = Family::Plain;
     // GEMV parameters
     int R = 1, S = 1, MMAX = 1, U = 1, NT = 1;
+    int NW = 4;      // waves per block of the vector GEMV (NW / S row groups)
     int P = 0;       // 1: software-pipelined batches of U trips (vector GEMV, M = 1)
     int PRO = 0;     // 1: RMSNorm folded into the kernel (vector GEMV, M = 1)
     // SwiGLU plans: E = 1, the activation fused into the kernel's epilogue (Y has

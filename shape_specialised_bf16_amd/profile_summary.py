@@ -8,6 +8,14 @@
         of each kernel's last N dispatches (a benchmark's timed rounds come after
         its warm-up launches of the same kernel).
 
+    python -m shape_specialised_bf16_amd.profile_summary counters <dir> --kernel NAME [--last N]
+        per-launch medians (over the kernel's last N dispatches) of every counter
+        of a ``--pmc ... --kernel-trace`` run, the kernel's duration from the same
+        run, and what they imply: the engine clock GRBM_GUI_ACTIVE / duration
+        (GRBM_GUI_ACTIVE counts busy cycles of each XCD's graphics engine, summed
+        over the XCDs), and with SQ_VALU_MFMA_BUSY_CYCLES the share of SIMD cycles
+        (CUs x 4 SIMDs x busy cycles of one XCD) that the matrix units were busy.
+
     python -m shape_specialised_bf16_amd.profile_summary traffic --fetch <dir> --write <dir>
             --kernel NAME --calib NAME --calib-bytes B [--out profiles/traffic.json --key KEY]
         HBM bytes per launch of kernel NAME from two ``--pmc FETCH_SIZE`` /
@@ -108,6 +116,27 @@ def _per_launch(vals, name, last):
     return statistics.median(v)
 
 
+def counters(path, kernel, last=5, cus=256, xcds=8):
+    """Medians of every counter over the kernel's last `last` dispatches, its
+    duration, and the derived clock and matrix-unit busy share."""
+    csvs = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not csvs:
+        raise SystemExit(f"no counter output under {path}")
+    names = sorted({r["Counter_Name"] for r in csv.DictReader(open(csvs[0]))})
+    out = {n: _per_launch(_counter(path, n), kernel, last) for n in names}
+    durs = [(b - a) / 1e3 for name, _, a, b, _, _ in _dispatches(path) if name.strip() == kernel][-last:]
+    if durs:
+        out["duration_us"] = statistics.median(durs)
+    if "GRBM_GUI_ACTIVE" in out and durs:
+        cyc = out["GRBM_GUI_ACTIVE"] / xcds              # busy cycles of one XCD's engine
+        out["clock_ghz"] = cyc / (out["duration_us"] * 1e3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in out:
+            out["mfma_busy_share"] = out["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * 4)
+        if "SQ_BUSY_CYCLES" in out:
+            out["sq_busy_share"] = out["SQ_BUSY_CYCLES"] / (cyc * xcds)
+    return out
+
+
 def traffic(fetch_dir, write_dir, kernel, calib, calib_bytes, last=5):
     f = _counter(fetch_dir, "FETCH_SIZE")
     w = _counter(write_dir, "WRITE_SIZE")
@@ -132,6 +161,10 @@ def main(argv=None):
     s.add_argument("--match", default="")
     s.add_argument("--stream", default="all", choices=["all", "last"])
     s.add_argument("--last", type=int, default=0, help="also the mean of each kernel's last N dispatches")
+    c = sub.add_parser("counters")
+    c.add_argument("path")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--last", type=int, default=5)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -147,6 +180,9 @@ def main(argv=None):
             tail = f"  last{a.last} {r['last_mean_us']:9.3f}" if a.last else ""
             print(f"{r['kernel'][:48]:48s} grid {r['grid']:10d} calls {r['calls']:5d}  mean {r['mean_us']:9.3f} us  "
                   f"min {r['min_us']:10.3f}  max {r['max_us']:10.3f}  total {r['total_us']:12.1f}{tail}")
+    elif a.cmd == "counters":
+        for k, v in counters(a.path, a.kernel, a.last).items():
+            print(f"{k:28s} {v:.6g}")
     else:
         r = traffic(a.fetch, a.write, a.kernel, a.calib, a.calib_bytes, a.last)
         r["source_sha"] = kernel_source_sha(a.kernel)

@@ -173,7 +173,8 @@ def test_swiglu_source_compiles_for_gfx950(tmp_path):
 def test_rmsnorm_module_has_folded_and_unfused_candidates():
     """With the RMSNorm prologue the epsilon is a literal of the module, every
     ordinary candidate is kept (it runs after the separate norm kernel) and
-    each M = 1 vector GEMV comes a second time with the norm folded in."""
+    each M = 1 vector GEMV of four waves per block (the norm's block reduction
+    takes 256 threads) comes a second time with the norm folded in."""
     src = ssb.emit_source(2048, 1024, "f32", rmsnorm_eps=1e-6)
     assert "constexpr float NORM_EPS = 0x1.0c6f7ap-20f;" in src        # 1e-6 as an f32, exactly
     names = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\(', src)
@@ -182,9 +183,10 @@ def test_rmsnorm_module_has_folded_and_unfused_candidates():
     assert plain <= set(names)
     folded = [n for n in names if n.endswith("_nf")]
     assert folded and all(n.startswith("gemv_valu") and "_m1_" in n for n in folded)
-    assert {n[:-3] for n in folded} == {n for n in plain if n.startswith("gemv_valu") and "_m1_" in n}
-    # the folded copies pass PRO = 1 (the template argument before the epilogue's)
-    assert "gemv_valu<" in src and ", 1, 0>(X, W, Y, gamma, M)" in src
+    assert {n[:-3] for n in folded} == {n for n in plain if n.startswith("gemv_valu") and "_m1_" in n
+                                        and not re.search(r"_w\d+$", n)}
+    # the folded copies pass PRO = 1 (the template argument before the epilogue's), NW = 4
+    assert "gemv_valu<" in src and ", 1, 0, 4>(X, W, Y, gamma, M)" in src
 
 
 def test_rmsnorm_and_swiglu_module_compiles(tmp_path):

@@ -1,9 +1,9 @@
 """The RMSNorm prologue folded into the projection (plans created with
 rmsnorm_eps, through proj_plan_create_ex with PROJ_PRO_RMSNORM), on the GPU.
 
-"#004 the same compiler on Apple's chips", section "Decode": the norm folded
-into the projection that follows it gives the same bits as the separate
-kernels, and whether it is used is measured at load time.  So: each folded
+"#004 the same compiler on Apple's chips", section "Decode": running the norm
+inside the next projection's kernel must reproduce the separate kernels bit for
+bit, and the load-time measurement decides whether it is used.  So: each folded
 ("_nf") candidate equals its unfused twin (the separate norm kernel, then the
 same kernel variant) bit for bit; both equal a plain plan's candidate run on
 proj_rmsnorm's output; and every result is within the derived allowance of

@@ -3,9 +3,9 @@ epilogue="swiglu", through proj_plan_create_ex), on the GPU.  Such a plan holds
 fused candidates and the plain candidates run unfused ("_uf"), the tuner
 choosing between them.
 
-"#004 the same compiler on Apple's chips", section "Decode": each fusion gives
-the same bits as the kernels it replaces, and is an option measured at load
-time.  So: every fused candidate must equal, bit for bit, the plain plan's
+"#004 the same compiler on Apple's chips", section "Decode": a fusion leaves
+every output bit as the separate kernels produce it, and whether to use it is
+decided by measurement at load time.  So: every fused candidate must equal, bit for bit, the plain plan's
 candidate of the same name followed by the separate activation kernel
 (proj_swiglu); and the fused result must be within the derived SwiGLU
 allowance of the oracle (oracle.swiglu of the fp64 product).

@@ -2,7 +2,7 @@
 fused norm prologue), each against something other than the oracle itself.
 
 The passage: "#004 the same compiler on Apple's chips", section "Decode" (the
-norm folded into the projection that follows it, same bits as the separate
+norm run inside the next projection's kernel, bit-identical to the separate
 kernels).  Reading: r = 1/sqrt(mean_k x_k^2 + eps), xn_k = x_k r gamma_k.
 """
 import numpy as np

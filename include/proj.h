@@ -244,8 +244,11 @@ int proj_pack_weights(int64_t N, int64_t K, const void* W, void* Wp, hipStream_t
 int proj_run_packed(const proj_plan* plan, const void* X, const void* Wp, void* Y, int64_t M, const float* gamma,
                     hipStream_t stream);
 
-/* Free the plan's module and workspace.  NULL-safe.  No launch of this plan may
- * still be pending on the device. */
+/* Free the plan's modules and workspace.  NULL-safe.  Waits first for all
+ * work queued on the plan's device to finish (hipDeviceSynchronize), so a
+ * launch of the plan still pending on any stream completes before its kernels
+ * and workspace go away; so it must not be called during a stream capture on
+ * that device. */
 void proj_plan_destroy(proj_plan* plan);
 
 /* Message of the last failure on the calling thread ("" if none).  The pointer
@@ -330,7 +333,8 @@ int proj_plan_choice(const proj_plan* plan, int64_t M);
  * same f32 operations and roundings as the PROJ_EPI_SWIGLU epilogue -- the
  * separate kernel that epilogue replaces ("#004 the same compiler on Apple's
  * chips", section "Decode").  N must be even; M == 0 or N == 0 is a no-op;
- * negative sizes, odd N, a bad dtype or null pointers give PROJ_EINVAL.
+ * negative sizes, odd N, a bad dtype, null pointers, G or H not aligned to
+ * the element size, or H overlapping G give PROJ_EINVAL.
  */
 int proj_swiglu(const void* G, void* H, int64_t M, int64_t N, int dtype, hipStream_t stream);
 
@@ -346,7 +350,8 @@ int proj_swiglu(const void* G, void* H, int64_t M, int64_t N, int dtype, hipStre
  * ("#004 the same compiler on Apple's chips", section "Decode").  Device
  * pointers owned by the caller; Xn must not overlap X.  M == 0 or K == 0 is a
  * no-op; negative sizes, a negative or non-finite eps, M >= 2^31 or null
- * pointers give PROJ_EINVAL.
+ * pointers, X or Xn not 2-byte aligned, gamma not 4-byte aligned, or Xn
+ * overlapping X or gamma give PROJ_EINVAL.
  */
 int proj_rmsnorm(const void* X, const float* gamma, void* Xn, int64_t M, int64_t K, float eps, hipStream_t stream);
 
@@ -368,7 +373,9 @@ int proj_probe_read(const void* buf, int64_t bytes, uint32_t never, void* sink, 
  * the projection epilogue uses (in: f32 device array, out: uint16 device
  * array).  Exposed so that the epilogue rounding can be checked on all 2^32
  * f32 patterns, as the pages check their GPU's f32 -> f16 conversion ("#004
- * the same compiler on Apple's chips", section "f16").
+ * the same compiler on Apple's chips", section "f16").  n == 0 is a no-op;
+ * negative n, null pointers, `in` not 4-byte or `out` not 2-byte aligned, or
+ * `out` overlapping `in` give PROJ_EINVAL.
  */
 int proj_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t stream);
 

@@ -63,6 +63,13 @@ static int support_module(SupportModule** out)
     return PROJ_OK;
 }
 
+// Whether [a, a + na) and [b, b + nb) share a byte.
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
 static int copy_text(const std::string& s, char* buf, size_t cap, size_t* needed)
 {
     if (needed) *needed = s.size() + 1;
@@ -319,17 +326,28 @@ int proj_rmsnorm(const void* X, const float* gamma, void* Xn, int64_t M, int64_t
     if (M == 0 || K == 0) return PROJ_OK;
     if (M > 0x7fffffff) return set_error(PROJ_EINVAL, "M=%lld: at most 2^31-1 rows", (long long)M);
     if (!X || !gamma || !Xn) return set_error(PROJ_EINVAL, "null pointer");
+    if (((uintptr_t)X | (uintptr_t)Xn) & 1 || (uintptr_t)gamma & 3)
+        return set_error(PROJ_EINVAL, "X and Xn must be 2-byte aligned, gamma 4-byte aligned");
+    const size_t xb = (size_t)M * (size_t)K * 2;
+    if (overlaps(Xn, xb, X, xb) || overlaps(Xn, xb, gamma, (size_t)K * 4))
+        return set_error(PROJ_EINVAL, "Xn overlaps X or gamma");
     SupportModule* sm = nullptr;
     int rc = support_module(&sm);
     if (rc) return rc;
-    const void* x = X;
-    const float* g = gamma;
-    void* xo = Xn;
-    long kk = (long)K;
-    float e2 = eps;
-    void* args[] = {&x, &g, &xo, &kk, &e2};
-    hipError_t e = hipModuleLaunchKernel(sm->rmsnorm, (unsigned)M, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
-    if (e != hipSuccess) return set_error(PROJ_EDEVICE, "rmsnorm launch: %s", hipGetErrorString(e));
+    // one block of 256 threads per row, at most 2^20 rows per launch (a launch
+    // holds fewer than 2^32 threads)
+    constexpr int64_t kRowsPerLaunch = (int64_t)1 << 20;
+    for (int64_t m0 = 0; m0 < M; m0 += kRowsPerLaunch) {
+        const int64_t rows = std::min(kRowsPerLaunch, M - m0);
+        const void* x = (const char*)X + (size_t)m0 * K * 2;
+        const float* g = gamma;
+        void* xo = (char*)Xn + (size_t)m0 * K * 2;
+        long kk = (long)K;
+        float e2 = eps;
+        void* args[] = {&x, &g, &xo, &kk, &e2};
+        hipError_t e = hipModuleLaunchKernel(sm->rmsnorm, (unsigned)rows, 1, 1, 256, 1, 1, 0, stream, args, nullptr);
+        if (e != hipSuccess) return set_error(PROJ_EDEVICE, "rmsnorm launch: %s", hipGetErrorString(e));
+    }
     return PROJ_OK;
 }
 
@@ -340,6 +358,11 @@ int proj_swiglu(const void* G, void* H, int64_t M, int64_t N, int dtype, hipStre
     if (dtype != PROJ_OUT_F32 && dtype != PROJ_OUT_BF16) return set_error(PROJ_EINVAL, "invalid dtype %d", dtype);
     if (M == 0 || N == 0) return PROJ_OK;
     if (!G || !H) return set_error(PROJ_EINVAL, "null pointer");
+    const size_t es = dtype == PROJ_OUT_BF16 ? 2 : 4;
+    if (((uintptr_t)G | (uintptr_t)H) & (es - 1))
+        return set_error(PROJ_EINVAL, "G and H must be aligned to their element size (%zu bytes)", es);
+    if (overlaps(G, (size_t)M * (size_t)N * es, H, (size_t)M * (size_t)(N / 2) * es))
+        return set_error(PROJ_EINVAL, "H overlaps G");
     SupportModule* sm = nullptr;
     int rc = support_module(&sm);
     if (rc) return rc;
@@ -359,6 +382,8 @@ int proj_round_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t strea
     if (n < 0) return set_error(PROJ_EINVAL, "n is negative");
     if (n == 0) return PROJ_OK;
     if (!in || !out) return set_error(PROJ_EINVAL, "null pointer");
+    if ((uintptr_t)in & 3 || (uintptr_t)out & 1) return set_error(PROJ_EINVAL, "in must be 4-byte, out 2-byte aligned");
+    if (overlaps(in, (size_t)n * 4, out, (size_t)n * 2)) return set_error(PROJ_EINVAL, "out overlaps in");
     SupportModule* sm = nullptr;
     int rc = support_module(&sm);
     if (rc) return rc;

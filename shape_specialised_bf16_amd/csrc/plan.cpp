@@ -742,7 +742,7 @@ static uint64_t fnv1a(uint64_t h, const std::string& s)
 // Whether buf holds a whole ELF64 image: the magic, and the program and section
 // header tables inside the buffer.  (hipModuleLoadData takes no size, so a
 // truncated or foreign cache file must not reach it.)
-static bool whole_elf64(const std::vector<char>& buf)
+bool whole_elf64(const std::vector<char>& buf)
 {
     if (buf.size() < 64 || memcmp(buf.data(), "\x7f" "ELF", 4) != 0 || buf[4] != 2) return false;
     auto u64 = [&](size_t o) { uint64_t v; memcpy(&v, buf.data() + o, 8); return v; };
@@ -778,7 +778,7 @@ static int cache_key(proj_plan* p, const std::string& src)
 }
 
 // Cached choice names per bucket ("" where absent); false if there is no usable file.
-static bool cache_read(const std::string& path, std::vector<std::string>* names)
+bool cache_read(const std::string& path, std::vector<std::string>* names)
 {
     std::ifstream f(path);
     if (!f) return false;
@@ -793,7 +793,7 @@ static bool cache_read(const std::string& path, std::vector<std::string>* names)
     return true;
 }
 
-static void cache_write(proj_plan* p)
+void cache_write(proj_plan* p)
 {
     const std::string tmp = p->cache_path + ".tmp";
     {
@@ -1255,6 +1255,9 @@ void destroy_plan(proj_plan* p)
     int cur = -1;
     (void)hipGetDevice(&cur);
     if (cur != p->device) (void)hipSetDevice(p->device);
+    // launches of this plan may still be pending on any stream of the device:
+    // they read its modules and workspace
+    (void)hipDeviceSynchronize();
     if (p->ws) (void)hipFree(p->ws);
     if (p->gu) (void)hipFree(p->gu);
     if (p->xn) (void)hipFree(p->xn);

@@ -143,12 +143,24 @@ struct Workspace {
     int64_t gu_rows = 0;
 };
 
+// The persistent tuning cache (plan.cpp): whether a buffer holds a whole ELF64
+// image (a code-object cache file is checked before it is loaded); the cached
+// choice names per bucket ("" where absent, false if the file is not a cache
+// file); the plan's choices written to its cache_path.
+bool whole_elf64(const std::vector<char>& buf);
+bool cache_read(const std::string& path, std::vector<std::string>* names);
+
 // The static scratch (scratch.hip): its size, and its address on `device`
 // (looked up once per device, with that device current).
 size_t scratch_capacity();
 int scratch_address(int device, void** ptr);
 
 }  // namespace proj
+
+struct proj_plan;
+namespace proj {
+void cache_write(proj_plan* p);
+}
 
 struct proj_plan {
     int64_t N = 0, K = 0;

@@ -67,3 +67,33 @@ def test_python_binding_rejects_bad_dtype():
     import shape_specialised_bf16_amd as ssb
     with pytest.raises(ValueError):
         ssb.emit_source(64, 64, "f16")
+
+
+def test_support_entry_points_check_alignment_and_overlap_before_any_gpu_call():
+    """proj_swiglu, proj_rmsnorm and proj_round_bf16 reject misaligned and
+    overlapping buffers (as include/proj.h states) before touching the device:
+    the addresses below are never dereferenced."""
+    import shape_specialised_bf16_amd as ssb
+    lib = ssb._lib
+    P = ctypes.c_void_p
+    base = 1 << 32
+    # SwiGLU: f32 G [4, 8] (128 B) and H [4, 4] (64 B)
+    assert lib.proj_swiglu(P(base), P(base + 64), 4, 8, 0, None) == -1          # H inside G
+    assert b"overlaps" in lib.proj_last_error()
+    assert lib.proj_swiglu(P(base + 2), P(base + 4096), 4, 8, 0, None) == -1    # f32 G on a 2-byte boundary
+    assert b"aligned" in lib.proj_last_error()
+    assert lib.proj_swiglu(P(base), P(base + 4097), 4, 8, 1, None) == -1        # bf16 H on an odd address
+    # RMSNorm: X [4, 64] bf16 (512 B), gamma 64 f32 (256 B)
+    g = P(base + 8192)
+    assert lib.proj_rmsnorm(P(base), g, P(base + 256), 4, 64, ctypes.c_float(1e-6), None) == -1   # Xn overlaps X
+    assert b"overlaps" in lib.proj_last_error()
+    assert lib.proj_rmsnorm(P(base), g, P(base + 8192 + 128), 4, 64, ctypes.c_float(1e-6), None) == -1  # Xn on gamma
+    assert lib.proj_rmsnorm(P(base + 1), g, P(base + 4096), 4, 64, ctypes.c_float(1e-6), None) == -1   # odd X
+    assert b"aligned" in lib.proj_last_error()
+    assert lib.proj_rmsnorm(P(base), P(base + 8194), P(base + 4096), 4, 64, ctypes.c_float(1e-6), None) == -1
+    # rounding: in 16 f32 (64 B), out 16 u16 (32 B)
+    assert lib.proj_round_bf16(P(base), P(base + 32), 16, None) == -1
+    assert b"overlaps" in lib.proj_last_error()
+    assert lib.proj_round_bf16(P(base + 2), P(base + 4096), 16, None) == -1
+    assert lib.proj_round_bf16(P(base), P(base + 4097), 16, None) == -1
+    assert b"aligned" in lib.proj_last_error()

@@ -68,32 +68,40 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     const int64_t CH = K / 8;  // 16-byte chunks per row
 
     // ---- vector-ALU GEMV: (R rows per wave, S waves splitting K), MMAX rows of X
-    struct VG { int R, S, MMAX, NT, NW; };
+    struct VG { int R, S, MMAX, NT, NW, KX = 1; };
     // (listed in order of preference: the tuner keeps an earlier candidate unless
     //  a later one is clearly faster).  NW: waves per block; 5 and 8 make a whole
     //  number of blocks per CU where 4 does not (5120 rows in waves of 2 rows:
     //  640 blocks of 4 waves, 2.5 per CU; 512 blocks of 5 waves, 2 per CU).
     const VG vgs[] = {{2, 1, 1, 1, 4}, {1, 1, 1, 1, 4}, {4, 1, 1, 1, 4}, {2, 1, 1, 0, 4},
                       {1, 4, 1, 1, 4}, {2, 4, 1, 1, 4}, {1, 1, 16, 1, 4}, {2, 1, 16, 1, 4}, {1, 4, 16, 1, 4},
-                      {2, 1, 1, 1, 5}, {1, 1, 1, 1, 5}, {4, 1, 1, 1, 5}, {2, 1, 1, 1, 8}, {1, 2, 1, 1, 8}};
+                      {2, 1, 1, 1, 5}, {1, 1, 1, 1, 5}, {4, 1, 1, 1, 5}, {2, 1, 1, 1, 8}, {1, 2, 1, 1, 8},
+                      // K split across 2, 4 or 8 workgroups (CUs), the partials added in a fixed order
+                      {2, 1, 1, 1, 4, 2}, {2, 1, 1, 1, 4, 4}, {1, 1, 1, 1, 4, 4}, {1, 1, 1, 1, 4, 8}};
     for (const VG& v : vgs) {
-        if (CH % v.S) continue;
+        if (CH % (v.S * v.KX)) continue;
+        // split across workgroups: long rows only (K >= 8192: a row's slices
+        // then still stream several KiB each), whole 64-lane trips per slice,
+        // the plain epilogue, and N % 4 == 0 for the 4-wide split-K sum
+        if (v.KX > 1 && (K < 8192 || epi || CH / v.KX < 64 || N % 4)) continue;
         if (epi && v.R % 2) continue;   // the fused epilogue pairs gate and up rows in a wave
         const int RG = v.NW / v.S;
         if (N % (v.R * RG)) continue;
         // other wave counts only where they change the block count per CU
         if (v.NW != 4 && (N / (v.R * RG)) % cus != 0) continue;
-        const int64_t trips = CH / v.S / 64;
+        const int64_t trips = CH / (v.S * v.KX) / 64;
         int U = 1;
         for (int u : {4, 2}) {
             if (trips > 0 && trips % u == 0 && u * v.R <= 8) { U = u; break; }
         }
         Candidate c;
         c.fam = Family::GemvValu;
-        c.R = v.R; c.S = v.S; c.MMAX = v.MMAX; c.U = U; c.NT = v.NT; c.NW = v.NW;
+        c.R = v.R; c.S = v.S; c.MMAX = v.MMAX; c.U = U; c.NT = v.NT; c.NW = v.NW; c.KX = v.KX;
+        if (v.KX > 1) c.reduce_name = fmt("splitk_reduce_sk%d", v.KX);
         c.threads = 64 * v.NW;
         c.max_m = v.MMAX;
-        const std::string wsuf = v.NW != 4 ? fmt("_w%d", v.NW) : std::string();
+        const std::string wsuf = (v.NW != 4 ? fmt("_w%d", v.NW) : std::string()) +
+                                 (v.KX > 1 ? fmt("_x%d", v.KX) : std::string());
         c.name = fmt("gemv_valu_r%d_s%d_m%d_u%d_nt%d", c.R, c.S, c.MMAX, c.U, c.NT) + wsuf;
         out.push_back(c);
         // the same with pipelined batches: the largest U that still leaves a
@@ -117,7 +125,7 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     if (pro) {
         const size_t n = out.size();
         for (size_t i = 0; i < n; ++i)
-            if (out[i].fam == Family::GemvValu && out[i].MMAX == 1 && out[i].NW == 4) {
+            if (out[i].fam == Family::GemvValu && out[i].MMAX == 1 && out[i].NW == 4 && out[i].KX == 1) {
                 Candidate c = out[i];
                 c.PRO = 1;
                 c.name += "_nf";
@@ -289,7 +297,14 @@ static void emit_wrappers(std::ostringstream& s, const Candidate& c, int64_t N, 
         s << "static_assert(K_BLOCKS16 / " << c.S << " / 64 == " << chs / 64 << ", \"trip count\");\n";
         s << "extern \"C\" __global__ __launch_bounds__(" << 64 * c.NW << ") void " << c.name << sig
           << "\n{ gemv_valu<" << c.R << ", " << c.S << ", " << c.MMAX << ", " << c.U << ", " << c.NT << ", " << out
-          << ", " << c.P << ", " << c.PRO << ", " << c.E << ", " << c.NW << ">(X, W, Y, gamma, M); }\n";
+          << ", " << c.P << ", " << c.PRO << ", " << c.E << ", " << c.NW << ", " << c.KX
+          << ">(X, W, Y, gamma, M, ws); }\n";
+        if (c.KX > 1 && !reduce_emitted[c.KX]) {   // the GEMM's split-K sum serves the split GEMV too
+            reduce_emitted[c.KX] = true;
+            s << "extern \"C\" __global__ __launch_bounds__(256) void " << c.reduce_name
+              << "(const float* __restrict__ ws, void* __restrict__ Y, int M)\n{ splitk_reduce<" << c.KX
+              << ", " << out << ">(ws, Y, M); }\n";
+        }
         break;
     }
     case Family::GemvMfma: {

@@ -33,22 +33,31 @@
 // block re-reads the K-element row, the extra traffic the pages name as the
 // reason the fused norm loses on larger models.
 //
+// With KX > 1 (M = 1) the K range is also split across workgroups, so across
+// CUs: block (g, x) sums slice x of K for its rows and writes the f32 partials
+// to ws[x][n]; a second kernel (splitk_reduce, the GEMM's) adds the KX
+// partials of each output in ascending x, a fixed order, so the result does
+// not depend on which block finished first.
+//
 // Block: NW waves = (NW/S) row groups x S K-slices (NW = 4 by default; other
 // counts let the grid be a whole number of blocks per CU, e.g. 5 waves of 2
 // rows make 512 blocks of 5120 rows: two per CU, all resident at once).
-// Grid:  N / (R * NW/S) blocks.
+// Grid:  N / (R * NW/S) x KX blocks.
 // ---------------------------------------------------------------------------
-template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0, int PRO = 0, int E = 0, int NW = 4>
+template <int R, int S, int MMAX, int U, int NT, int OUT, int P = 0, int PRO = 0, int E = 0, int NW = 4, int KX = 1>
 __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* __restrict__ W,
-                                          void* __restrict__ Y, const float* __restrict__ gamma, int M)
+                                          void* __restrict__ Y, const float* __restrict__ gamma, int M,
+                                          float* __restrict__ ws = nullptr)
 {
     constexpr long NO = E ? N / 2 : N;          // columns of Y
     static_assert(PRO == 0 || MMAX == 1, "the fused norm prologue serves M = 1");
     static_assert(PRO == 0 || NW == 4, "the norm prologue's block reduction takes 256 threads");
     static_assert(NW % S == 0 && NW >= 1 && NW <= 16, "S divides the NW waves of a block");
+    static_assert(KX == 1 || (MMAX == 1 && S == 1 && PRO == 0 && E == 0),
+                  "split across workgroups: M = 1, no in-block split, no fused prologue or epilogue");
     constexpr long CH = K / 8;                  // 16-byte chunks per row
-    static_assert(K % 8 == 0 && CH % S == 0, "K slice must be whole chunks");
-    constexpr long CHS = CH / S;                // chunks per K-slice
+    static_assert(K % 8 == 0 && CH % (S * KX) == 0, "K slice must be whole chunks");
+    constexpr long CHS = CH / (S * KX);         // chunks per K-slice
     constexpr long TRIPS = CHS / 64;            // full 64-lane trips per slice
     constexpr int TAIL = (int)(CHS % 64);       // lanes busy in the last, partial trip
     static_assert(U >= 1 && TRIPS % U == 0, "U divides the trip count");
@@ -65,10 +74,12 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
     const int s = wave % S;
     const int rg = wave / S;
     const long n0 = ((long)blockIdx.x * RG + rg) * (E ? R / 2 : R);   // first weight row = first output column
+    const int xk = KX > 1 ? (int)blockIdx.y : 0;                       // slice of K across workgroups
+    const long slice = (long)xk * S + s;
 
     // this lane's chunks of the slice; W row n, trip t: Wl + w_row(n) + t * W_TRIP
-    const u32x4* __restrict__ Wl = reinterpret_cast<const u32x4*>(W) + w_col(s * CHS + lane);
-    const u32x4* __restrict__ Xg = reinterpret_cast<const u32x4*>(X) + s * CHS + lane;
+    const u32x4* __restrict__ Wl = reinterpret_cast<const u32x4*>(W) + w_col(slice * CHS + lane);
+    const u32x4* __restrict__ Xg = reinterpret_cast<const u32x4*>(X) + slice * CHS + lane;
     __shared__ u32x4 xs[PRO ? CH : 1];         // the normalised X row
     __shared__ float red[PRO ? 256 : 1];
     if constexpr (PRO) {
@@ -165,7 +176,10 @@ __device__ __forceinline__ void gemv_valu(const u16* __restrict__ X, const u16* 
     const bool writer = (lane & ((64 >> LV) - 1)) == 0;
     const int r = idx / MMAX, m = idx % MMAX;
 
-    if constexpr (S == 1) {
+    if constexpr (KX > 1) {
+        // this slice's partials; splitk_reduce adds the KX slices
+        if (writer) ws[(long)xk * N + n0 + r] = sum;
+    } else if constexpr (S == 1) {
         if constexpr (E) {
             const float up = __shfl_down(sum, 32);      // value idx + (R/2)*MMAX
             if (writer && r < R / 2 && m < M) dev::store1<OUT>(Y, (long)m * NO + n0 + r, dev::swiglu<OUT>(sum, up));

@@ -282,7 +282,7 @@ struct LaunchGeom {
 static LaunchGeom geom(const Candidate& c, int64_t N, int64_t NO, int64_t M)
 {
     switch (c.fam) {
-    case Family::GemvValu: return {(unsigned)(N / (c.R * (c.NW / c.S))), 1u, (unsigned)(64 * c.NW)};
+    case Family::GemvValu: return {(unsigned)(N / (c.R * (c.NW / c.S))), (unsigned)c.KX, (unsigned)(64 * c.NW)};
     case Family::GemvMfma: return {(unsigned)(N / (16 * (4 / c.S))), 1u, 256u};
     case Family::Gemm: {
         if (c.TAILS > 1) {

@@ -28,6 +28,7 @@ struct Candidate {
     // GEMV parameters
     int R = 1, S = 1, MMAX = 1, U = 1, NT = 1;
     int NW = 4;      // waves per block of the vector GEMV (NW / S row groups)
+    int KX = 1;      // >1: the vector GEMV's K split across KX workgroups (M = 1)
     int P = 0;       // 1: software-pipelined batches of U trips (vector GEMV, M = 1)
     int PRO = 0;     // 1: RMSNorm folded into the kernel (vector GEMV, M = 1)
     // SwiGLU plans: E = 1, the activation fused into the kernel's epilogue (Y has
@@ -50,7 +51,9 @@ struct Candidate {
     hipFunction_t fn = nullptr;
     hipFunction_t reduce_fn = nullptr;
 
-    bool needs_ws() const { return fam == Family::Gemm && (SK > 1 || TAILS > 1); }
+    // partials in the workspace, which a second kernel sums (split-K or
+    // split-tail GEMM, GEMV split across workgroups)
+    bool needs_ws() const { return (fam == Family::Gemm && (SK > 1 || TAILS > 1)) || (fam == Family::GemvValu && KX > 1); }
     // Tiles, whole tiles and split tail tiles of a launch at M rows (the same
     // split as tail_split() in the device code).
     void tail_split(int64_t M, int64_t N, int64_t* T, int64_t* n_full, int64_t* rem) const
@@ -61,6 +64,7 @@ struct Candidate {
     }
     size_t ws_bytes(int64_t M, int64_t N) const
     {
+        if (fam == Family::GemvValu && KX > 1) return (size_t)KX * (size_t)M * (size_t)N * sizeof(float);
         if (fam != Family::Gemm) return 0;
         if (SK > 1) return (size_t)SK * (size_t)M * (size_t)N * sizeof(float);
         if (TAILS > 1) {
@@ -70,9 +74,11 @@ struct Candidate {
         }
         return 0;
     }
-    // Largest workspace any M up to max_rows can need.
+    // Largest workspace any M up to max_rows (and up to the candidate's own
+    // limit) can need.
     size_t ws_bound(int64_t max_rows, int64_t N) const
     {
+        max_rows = std::min(max_rows, max_m);
         if (TAILS > 1) {
             const int64_t T = ((max_rows + BM - 1) / BM) * (N / BN);
             return (size_t)std::min<int64_t>(T, ROUND) * TAILS * BM * BN * sizeof(float);

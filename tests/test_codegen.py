@@ -63,7 +63,7 @@ def test_no_runtime_shape_arguments():
     sigs = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void (gemv_\w+|gemm_\w+)(\([^)]*\))', src)
     assert len(sigs) >= 10
     for name, sig in sigs:
-        if name.endswith("_reduce"):        # second pass of a split tail: partials in, Y out
+        if name.endswith("_reduce") or name.startswith("splitk_reduce"):   # second pass: partials in, Y out
             assert sig == "(const float* __restrict__ ws, void* __restrict__ Y, int M)", name
             continue
         assert sig == ("(const u16* __restrict__ X, const u16* __restrict__ W, void* __restrict__ Y, "
@@ -77,12 +77,15 @@ def test_candidates_tile_the_shape(N, K):
     names = re.findall(r'extern "C" __global__ __launch_bounds__\(\d+\) void ((?:gemv|gemm)_\w+)\(', src)
     assert "gemm_plain" in names
     for n in names:
-        m = re.match(r"gemv_valu_r(\d+)_s(\d+)_m(\d+)_u(\d+)_nt(\d)", n)
+        m = re.match(r"gemv_valu_r(\d+)_s(\d+)_m(\d+)_u(\d+)_nt(\d)(?:_p)?(?:_w(\d+))?(?:_x(\d+))?(?:_nf)?$", n)
         if m:
-            R, S, MM, U, _ = map(int, m.groups())
-            assert (K // 8) % S == 0 and N % (R * (4 // S)) == 0
-            trips = K // 8 // S // 64
+            R, S, MM, U, _ = map(int, m.groups()[:5])
+            NW = int(m.group(6) or 4)          # waves per block
+            KX = int(m.group(7) or 1)          # K split across workgroups
+            assert (K // 8) % (S * KX) == 0 and N % (R * (NW // S)) == 0
+            trips = K // 8 // (S * KX) // 64
             assert trips % U == 0 or trips == 0
+            assert KX == 1 or (MM == 1 and trips >= 1)
             continue
         m = re.match(r"gemv_mfma_s(\d+)_u(\d+)_nt(\d)", n)
         if m:
@@ -184,9 +187,9 @@ def test_rmsnorm_module_has_folded_and_unfused_candidates():
     folded = [n for n in names if n.endswith("_nf")]
     assert folded and all(n.startswith("gemv_valu") and "_m1_" in n for n in folded)
     assert {n[:-3] for n in folded} == {n for n in plain if n.startswith("gemv_valu") and "_m1_" in n
-                                        and not re.search(r"_w\d+$", n)}
-    # the folded copies pass PRO = 1 (the template argument before the epilogue's), NW = 4
-    assert "gemv_valu<" in src and ", 1, 0, 4>(X, W, Y, gamma, M)" in src
+                                        and not re.search(r"_[wx]\d+$", n)}
+    # the folded copies pass PRO = 1 (the template argument before the epilogue's), NW = 4, KX = 1
+    assert "gemv_valu<" in src and ", 1, 0, 4, 1>(X, W, Y, gamma, M, ws)" in src
 
 
 def test_rmsnorm_and_swiglu_module_compiles(tmp_path):

@@ -1,4 +1,4 @@
-"""Workspace and launch sizing of the split GEMM candidates, checked on the CPU.
+"""Workspace and launch sizing of the split GEMM and split GEMV candidates, checked on the CPU.
 
 A plan allocates one workspace at creation, sized by Candidate::ws_bound over
 the largest block (8192 rows), and every launch writes split-K or split-tail
@@ -49,10 +49,17 @@ int main() {
             for (const Candidate& c : enumerate_candidates(N, K, 256, fusion)) {
                 if (!c.needs_ws()) continue;
                 const size_t bound = c.ws_bound(kMaxBlockRows, N);
-                for (long M = 1; M <= kMaxBlockRows; ++M) {
+                for (long M = 1; M <= c.max_m; ++M) {
                     // what the launch at M writes, from the grid the host launches
                     size_t need;
-                    if (c.SK > 1) {
+                    if (c.fam == Family::GemvValu) {
+                        // K split across KX workgroups: partials ws[x][n], one row of Y (M = 1)
+                        need = (size_t)c.KX * M * N * sizeof(float);
+                        if (c.KX < 2 || c.max_m != 1 || N % 4 || c.reduce_name.empty()) {
+                            std::printf("FAIL split GEMV %s\n", c.name.c_str());
+                            return 1;
+                        }
+                    } else if (c.SK > 1) {
                         need = (size_t)c.SK * M * N * sizeof(float);          // ws[z][M][N]
                     } else {
                         int64_t T, nf, rem;
@@ -110,6 +117,8 @@ def test_every_split_launch_fits_the_workspace_bound(tmp_path):
 
 
 @pytest.mark.parametrize("old,new", [
+    ("return (size_t)KX * (size_t)M * (size_t)N * sizeof(float);",             # one split GEMV slice forgotten
+     "return (size_t)(KX - 1) * (size_t)M * (size_t)N * sizeof(float);"),
     ("return (size_t)rem * TAILS * BM * BN * sizeof(float);",                  # a tail piece forgotten
      "return (size_t)rem * BM * BN * sizeof(float);"),
     ("return (size_t)std::min<int64_t>(T, ROUND) * TAILS * BM * BN * sizeof(float);",   # bound from half a round

@@ -441,6 +441,12 @@ def roofline_prefill(leg, M, sclk):
             r["frac_at_sampled_sclk"] = round(dom["tflops"] / mfma_peak_at(mhz), 4)
     r.update(kernel=dom["kernel"], shape=dom["shape"], M=M, mean_launch_us=dom["us"], algorithmic_bytes=nbytes,
              flop_per_byte=round(fl / nbytes, 1), traffic=traffic_for(f"{dom['kernel']}@{dom['shape']}m{M}"))
+    cnt = counters_for(f"{dom['kernel']}@{dom['shape']}m{M}")
+    if cnt and r["bound"] == "mfma":
+        # the clock the counters saw while this kernel ran (power-limited under
+        # MFMA load), and the dense peak at that clock
+        pk = mfma_peak_at(cnt["clock_ghz"] * 1e3)
+        r.update(counters=cnt, peak_at_counter_clock=round(pk, 1), frac_at_counter_clock=round(dom["tflops"] / pk, 4))
     return r
 
 
@@ -703,6 +709,24 @@ def traffic_for(key: str):
     return round(e["bytes_per_launch"])
 
 
+def counters_for(key: str):
+    """Engine clock and matrix-unit busy share of a kernel from the committed
+    rocprofv3 counter runs (GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES with
+    the kernel trace), if they were taken on the current kernel source and the
+    kernel ran long enough (>= 100 us) for its counter window to be the
+    kernel's own; else None."""
+    from shape_specialised_bf16_amd.profile_summary import kernel_source_sha
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        e = json.load(open(path)).get(key)
+    except Exception:
+        return None
+    if not e or e.get("source_sha") != kernel_source_sha(key.split("@")[0]) or e.get("duration_us", 0) < 100:
+        return None
+    return dict(clock_ghz=round(e["clock_ghz"], 3), mfma_busy_share=round(e["mfma_busy_share"], 3),
+                duration_us=round(e["duration_us"], 1))
+
+
 def probe_bandwidth():
     import torch
     import shape_specialised_bf16_amd as ssb
@@ -770,6 +794,62 @@ def cpu_baseline_prefill(rows: int = 64):
                        f"extrapolated to {full:.0f} s")
 
 
+def profile_graph08(steps: int = 60):
+    """The 0.8B-like decode step (QKV, out, gate/up, down, head at M = 1, f32 Y,
+    rotating weight copies) launched eagerly, then, after a pause, replayed as
+    one recorded HIP graph per rotation of the weight copies; for a
+    rocprofv3 --kernel-trace of the per-kernel durations and the gaps between
+    kernels in either mode (profile_summary steps)."""
+    import torch
+
+    import synth
+
+    cfg = synth.workload("decode_0.8b_layer_m1")
+    projs = cfg.projections
+    plans = Plans()
+    pl = [plans.get(p.N, p.K, "f32") for p in projs]
+    Xs = [upload(synth.activations(cfg, i, 1)) for i in range(len(projs))]
+    Ws = [upload(weights(cfg, i)) for i in range(len(projs))]
+    Ys = [torch.empty((1, p.N), dtype=torch.float32, device="cuda") for p in projs]
+    ncp = copies_for(sum(w.numel() * 2 for w in Ws))
+    Wrot = [[w] + [w.clone() for _ in range(ncp - 1)] for w in Ws]
+    sh = _stream_handle()
+
+    def step(s, h=sh):
+        for i in range(len(projs)):
+            pl[i].run_ptr(Xs[i].data_ptr(), Wrot[i][s % ncp].data_ptr(), Ys[i].data_ptr(), 1, h)
+
+    warm(step, DEVICE_WARM_MS)
+    for s in range(steps):
+        step(s)
+    torch.cuda.synchronize()
+    gs = torch.cuda.Stream()
+    gh = ctypes.c_void_p(gs.cuda_stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(g, stream=gs):
+            for c in range(ncp):
+                step(c, gh)
+    torch.cuda.synchronize()
+    time.sleep(0.05)
+    warm(lambda s: g.replay(), DEVICE_WARM_MS)
+    for _ in range(max(1, steps // ncp)):
+        g.replay()
+    torch.cuda.synchronize()
+    # the floor: a projection that reads almost nothing (64 x 64 weights), back to back
+    tiny = plans.get(64, 64, "f32")
+    tx, tw = upload(synth.normal_bf16(99, 0, (1, 64), 1.0)), upload(synth.normal_bf16(99, 1, (64, 64), 0.02))
+    ty = torch.empty((1, 64), dtype=torch.float32, device="cuda")
+    time.sleep(0.05)
+    for _ in range(200):
+        tiny.run_ptr(tx.data_ptr(), tw.data_ptr(), ty.data_ptr(), 1, sh)
+    torch.cuda.synchronize()
+    log(f"profile mode: 0.8B decode step, {steps} eager steps then {max(1, steps // ncp) * ncp} replayed "
+        f"({ncp} steps per graph): " + ", ".join(f"{p.name} {pl[i].choice(1)}" for i, p in enumerate(projs))
+        + f"; then 200 launches of a 64x64 projection ({tiny.choice(1)})")
+    plans.close()
+
+
 def profile_mode(which: str, M: int, launches: int = 30):
     """Only one dominant kernel at its bench configuration -- decode: the 27B-like
     gate/up GEMV (34816x5120, M=1, bf16 Y) on rotating weight copies; decode08:
@@ -816,7 +896,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the fusion and packed-layout legs")
     ap.add_argument("--prefill-m", type=int, default=2048, help="row count of the GEMM in the profile-prefill modes")
     ap.add_argument("--mode", default="full", choices=["full", "profile-decode", "profile-decode08", "profile-prefill",
-                                                       "profile-prefill27"],
+                                                       "profile-prefill27", "profile-graph08"],
                     help="profile-*: only that leg's dominant kernel and a calibration copy, for rocprofv3 "
                          "counter runs")
     args = ap.parse_args()
@@ -824,6 +904,9 @@ def main():
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the projection shards "
               "by output rows across GPUs but no multi-GPU path is built", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "profile-graph08":
+        profile_graph08()
+        return
     if args.mode != "full":
         profile_mode(args.mode.split("-")[1], args.prefill_m)
         return

@@ -16,6 +16,14 @@
         over the XCDs), and with SQ_VALU_MFMA_BUSY_CYCLES the share of SIMD cycles
         (CUs x 4 SIMDs x busy cycles of one XCD) that the matrix units were busy.
 
+    python -m shape_specialised_bf16_amd.profile_summary steps <dir> --period P [--phase-gap-us G]
+        a repeated sequence of P kernels (one step of a benchmark) in a
+        ``--kernel-trace`` run: the dispatches of the GPU's busiest stretches are
+        split into phases at idle gaps longer than G us, and in each phase the
+        last complete steps give, per position in the step, the median kernel
+        duration and the median gap from the end of the previous kernel to the
+        start of this one -- what the step spends in kernels and between them.
+
     python -m shape_specialised_bf16_amd.profile_summary traffic --fetch <dir> --write <dir>
             --kernel NAME --calib NAME --calib-bytes B [--out profiles/traffic.json --key KEY]
         HBM bytes per launch of kernel NAME from two ``--pmc FETCH_SIZE`` /
@@ -137,6 +145,39 @@ def counters(path, kernel, last=5, cus=256, xcds=8):
     return out
 
 
+def steps(path, period, phase_gap_us=1000.0, last=40):
+    """Per phase: [(kernel, median duration us, median gap before us)] over the
+    phase's last `last` complete steps of `period` kernels."""
+    rows = _dispatches(path)
+    phases, cur = [], []
+    for r in rows:
+        if cur and (r[2] - cur[-1][3]) / 1e3 > phase_gap_us:
+            phases.append(cur)
+            cur = []
+        cur.append(r)
+    if cur:
+        phases.append(cur)
+    out = []
+    for ph in phases:
+        n = len(ph) // period
+        if n < 4:
+            continue
+        # align on the step: the phase's last n * period dispatches
+        ph = ph[len(ph) - n * period:]
+        ph = ph[-min(last, n) * period:]
+        # only stretches that repeat the same kernels in the same order
+        if any(ph[i][0] != ph[i % period][0] or ph[i][5] != ph[i % period][5] for i in range(len(ph))):
+            continue
+        pos = []
+        for j in range(period):
+            d = [(ph[i][3] - ph[i][2]) / 1e3 for i in range(j, len(ph), period)]
+            g = [(ph[i][2] - ph[i - 1][3]) / 1e3 for i in range(max(j, 1), len(ph), period)]
+            pos.append((ph[j][0], statistics.median(d), statistics.median(g) if g else 0.0))
+        span = (ph[-1][3] - ph[0][2]) / 1e3 / (len(ph) / period)
+        out.append(dict(steps=len(ph) // period, step_us=span, positions=pos))
+    return out
+
+
 def traffic(fetch_dir, write_dir, kernel, calib, calib_bytes, last=5):
     f = _counter(fetch_dir, "FETCH_SIZE")
     w = _counter(write_dir, "WRITE_SIZE")
@@ -161,10 +202,17 @@ def main(argv=None):
     s.add_argument("--match", default="")
     s.add_argument("--stream", default="all", choices=["all", "last"])
     s.add_argument("--last", type=int, default=0, help="also the mean of each kernel's last N dispatches")
+    st = sub.add_parser("steps")
+    st.add_argument("path")
+    st.add_argument("--period", type=int, required=True)
+    st.add_argument("--phase-gap-us", type=float, default=1000.0)
+    st.add_argument("--last", type=int, default=40)
     c = sub.add_parser("counters")
     c.add_argument("path")
     c.add_argument("--kernel", required=True)
     c.add_argument("--last", type=int, default=5)
+    c.add_argument("--out")
+    c.add_argument("--key")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -180,9 +228,25 @@ def main(argv=None):
             tail = f"  last{a.last} {r['last_mean_us']:9.3f}" if a.last else ""
             print(f"{r['kernel'][:48]:48s} grid {r['grid']:10d} calls {r['calls']:5d}  mean {r['mean_us']:9.3f} us  "
                   f"min {r['min_us']:10.3f}  max {r['max_us']:10.3f}  total {r['total_us']:12.1f}{tail}")
+    elif a.cmd == "steps":
+        for k, ph in enumerate(steps(a.path, a.period, a.phase_gap_us, a.last)):
+            print(f"phase {k}: {ph['steps']} steps, {ph['step_us']:.2f} us per step (first kernel start to last end)")
+            for name, d, g in ph["positions"]:
+                print(f"    {name[:44]:44s} kernel {d:8.3f} us   gap before {g:7.3f} us")
+            tot_k = sum(d for _, d, _ in ph["positions"])
+            tot_g = sum(g for _, _, g in ph["positions"])
+            print(f"    sum: kernels {tot_k:.3f} us, gaps {tot_g:.3f} us")
     elif a.cmd == "counters":
-        for k, v in counters(a.path, a.kernel, a.last).items():
+        r = counters(a.path, a.kernel, a.last)
+        for k, v in r.items():
             print(f"{k:28s} {v:.6g}")
+        if a.out:
+            r["source_sha"] = kernel_source_sha(a.kernel)
+            d = json.load(open(a.out)) if os.path.exists(a.out) else {}
+            d[a.key or a.kernel] = r
+            with open(a.out, "w") as fh:
+                json.dump(d, fh, indent=1, sort_keys=True)
+                fh.write("\n")
     else:
         r = traffic(a.fetch, a.write, a.kernel, a.calib, a.calib_bytes, a.last)
         r["source_sha"] = kernel_source_sha(a.kernel)

@@ -52,3 +52,22 @@ def test_every_summary_gives_its_command():
             continue
         text = open(os.path.join(PROFILES, name)).read()
         assert "rocprofv3" in text and "bench.py" in text, name
+
+
+def _counter_entries():
+    p = os.path.join(PROFILES, "counters.json")
+    return sorted(json.load(open(p)).items()) if os.path.exists(p) else []
+
+
+@pytest.mark.parametrize("key,e", _counter_entries(), ids=[k for k, _ in _counter_entries()])
+def test_counter_entry_follows_from_its_raw_counts(key, e):
+    """The clock and matrix-unit busy share the benchmark quotes are what the
+    raw counters of the entry give (8 XCDs, 256 CUs of 4 SIMDs)."""
+    cyc = e["GRBM_GUI_ACTIVE"] / 8
+    assert e["clock_ghz"] == pytest.approx(cyc / (e["duration_us"] * 1e3), rel=1e-9)
+    assert e["mfma_busy_share"] == pytest.approx(e["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 256 * 4), rel=1e-9)
+    assert 0 < e["mfma_busy_share"] <= 1.0
+    m = re.fullmatch(r"(gemm_\w+)@(\d+)x(\d+)m\d+", key)
+    assert m, key
+    assert re.search(rf"void {m.group(1)}\(", ssb.emit_source(int(m.group(2)), int(m.group(3)), "bf16")), key
+    assert re.fullmatch(r"[0-9a-f]{16}", e["source_sha"])

@@ -437,11 +437,18 @@ struct Tuner {
     int64_t mmax = 0;
     static constexpr int64_t kGuardRows = 3;
 
+    // copies of the probe weights (in the candidates' layout) for the decode
+    // buckets' timing: one launch after another, each on the next copy, the
+    // copies together larger than the last-level cache (allocated on first use)
+    std::vector<void*> wrot;
+    void* wrot_buf = nullptr;
+
     ~Tuner()
     {
         for (void* q : {Xr, Xi, Wr, Wi, Y, (void*)ref_r, (void*)ref_i, (void*)rows_d, (void*)stats_d, flush,
                         (void*)gamma, Xnr, Xni, Wrp, Wip})
             if (q) (void)hipFree(q);
+        if (wrot_buf) (void)hipFree(wrot_buf);
         if (e0) (void)hipEventDestroy(e0);
         if (e1) (void)hipEventDestroy(e1);
         if (st) (void)hipStreamDestroy(st);
@@ -668,10 +675,62 @@ struct Tuner {
         return PROJ_OK;
     }
 
+    // At decode (M <= 16) the projections of a step run one after another, each
+    // reading weights no cache holds.  So a decode candidate is timed in that
+    // regime: launches back to back, each on the next of several weight copies
+    // that together exceed the 256 MB last-level cache (1 GiB); the median over `reps`
+    // rounds of the mean per launch.  (Timed one launch at a time after a cache
+    // flush instead, the ranking of near-equal GEMVs differed from the one
+    // measured back to back: a 10240x5120 GEMV with cached loads came out first
+    // and ran 6 % slower than the pick of the back-to-back timing.)
+    int time_decode(const Candidate& c, int64_t M, int reps, double* us)
+    {
+        const size_t wb = (size_t)p->N * p->K * 2;
+        if (wrot.empty()) {
+            // copies 256-byte aligned in one buffer of 1 GiB, at most 128 copies (weights
+            // under 8 MB then rotate through less: their launches are dominated by
+            // fixed costs, not by where the bytes come from)
+            const size_t wbs = (wb + 255) & ~(size_t)255;
+            const size_t n = std::min<size_t>(128, std::max<size_t>(2, (((size_t)1 << 30) + wbs - 1) / wbs));
+            if (hipMalloc(&wrot_buf, n * wbs) != hipSuccess) {
+                (void)hipGetLastError();
+                wrot_buf = nullptr;
+                return PROJ_ENOMEM;   // not enough memory: the caller times cold launches
+            }
+            for (size_t i = 0; i < n; ++i) {
+                wrot.push_back((char*)wrot_buf + i * wbs);
+                HIP_TRY(hipMemcpyAsync(wrot.back(), Wrc, wb, hipMemcpyDeviceToDevice, st));
+            }
+            HIP_TRY(hipStreamSynchronize(st));
+        }
+        const int n = (int)wrot.size();
+        int rc;
+        for (int i = 0; i < n; ++i)
+            if ((rc = launch_candidate(p, c, Xr, wrot[i], Y, M, st, gamma))) return rc;
+        std::vector<double> t;
+        for (int r = 0; r < reps; ++r) {
+            HIP_TRY(hipEventRecord(e0, st));
+            for (int i = 0; i < n; ++i)
+                if ((rc = launch_candidate(p, c, (i & 1) ? Xi : Xr, wrot[i], Y, M, st, gamma))) return rc;
+            HIP_TRY(hipEventRecord(e1, st));
+            HIP_TRY(hipEventSynchronize(e1));
+            float ms = 0;
+            HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+            t.push_back(ms * 1000.0 / n);
+        }
+        std::sort(t.begin(), t.end());
+        *us = t[t.size() / 2];
+        return PROJ_OK;
+    }
+
     // Median launch time in microseconds over `reps` launches at M rows.
     int time_candidate(const Candidate& c, int64_t M, int reps, double* us)
     {
         int rc;
+        if (M <= 16) {
+            rc = time_decode(c, M, reps, us);
+            if (rc != PROJ_ENOMEM) return rc;
+        }
         for (int i = 0; i < 2; ++i)
             if ((rc = launch_candidate(p, c, Xr, Wrc, Y, M, st, gamma))) return rc;
         std::vector<double> t;

@@ -23,7 +23,8 @@ Reported (one JSON line on stdout; progress on stderr):
                launches (an event pair each)
   prefill_27b_m8192  the same layer at M = 8192: TFLOP/s per projection and
                for the layer, against 2.5 PFLOP/s and against
-               256 CUs x 4096 flop/clk x the sclk sampled while it ran
+               256 CUs x 4096 flop/clk x the engine clock each kernel ran at,
+               read inside a probe copy of it (clock_probe)
                (roofline_prefill: its dominant GEMM)
   decode_08b   the 0.8B-like layer plus its 151936-row head at M = 1 (f32 Y):
                the same figures, and the step replayed as a HIP graph
@@ -33,7 +34,7 @@ Reported (one JSON line on stdout; progress on stderr):
   swiglu_epilogue, rmsnorm_prologue, packed_weights  the fused epilogue /
                prologue and the packed layout against their unfused / row-major
                forms (skipped with --no-extra)
-  clocks       sclk and mclk before and after, and sampled during the prefill legs
+  clocks       sclk and mclk before and after (board level)
   probe        HBM read-probe bandwidth (the pages' measured denominator)
   cpu_baseline the fp64 CPU oracle on the same decode step (bounded sample, all
                host cores up to 16), with a 64-row prefill sample of the M = 8192
@@ -49,7 +50,6 @@ import json
 import os
 import statistics
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -197,40 +197,6 @@ def clocks():
                 power_w=round(p / 1e6, 1) if p else None, temp_c=[(_hwmon(f"temp{i}_input") or 0) / 1e3 for i in (2, 3)])
 
 
-class SclkSampler:
-    """Samples the graphics clock (amd-smi, mean over the XCDs) while a leg runs."""
-
-    def __init__(self, period_s: float = 0.05):
-        self.period, self.samples, self.power, self._stop = period_s, [], [], threading.Event()
-        self._t = threading.Thread(target=self._run, daemon=True)
-
-    def _run(self):
-        while not self._stop.is_set():
-            g = _gfx_clocks()
-            if g:
-                self.samples.append(statistics.mean(g))
-            p = _hwmon("power1_input")
-            if p:
-                self.power.append(p / 1e6)
-            time.sleep(self.period)
-
-    def __enter__(self):
-        self._t.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        self._t.join()
-
-    def summary(self):
-        busy = [v for v in self.samples if v >= 1000]   # samples taken while the device was busy
-        if not busy:
-            return None
-        return dict(samples=len(busy), median_mhz=round(statistics.median(busy), 1), p10_mhz=round(pct(busy, 0.1), 1),
-                    p90_mhz=round(pct(busy, 0.9), 1),
-                    power_w_median=round(statistics.median(self.power), 1) if self.power else None)
-
-
 def mfma_peak_at(mhz):
     return CUS * FLOP_PER_CLK_PER_CU * mhz * 1e6 / 1e12 if mhz else None
 
@@ -241,6 +207,7 @@ class Plans:
 
     def __init__(self):
         self.d = {}
+        self.created = []   # plan creation (emit, compile, validate, tune), outside every timed region
 
     def get(self, N, K, dtype, **kw):
         from shape_specialised_bf16_amd import Plan
@@ -251,6 +218,10 @@ class Plans:
             d = self.d[key].describe()
             log(f"  plan {N}x{K} {dtype} {kw or ''}: {time.time() - t0:.1f} s "
                 f"(compile {d['compile_s']:.1f} s in {d['modules']} modules, tune {d['tune_s']:.1f} s)")
+            self.created.append(dict(shape=f"{N}x{K}", dtype=dtype, options=dict(kw) or None,
+                                     wall_s=round(time.time() - t0, 2), compile_s=round(d["compile_s"], 2),
+                                     tune_s=round(d["tune_s"], 2), modules=d["modules"],
+                                     code_cache=d.get("code_cache"), tuning_cache=d.get("cache")))
         return self.d[key]
 
     def close(self):
@@ -376,11 +347,29 @@ def decode_layer(plans, wl: str, dtype: str, steps: int, warmup: int, graph: boo
 
 
 # ---------------------------------------------------------------- prefill
-def prefill_layer(plans, wl: str, Ms, rounds: int = 5, sampler=None):
+def kernel_clock(N, K, name, X, Wrot, Y, M):
+    """The engine clock the tuned GEMM `name` runs at under its own load, read
+    inside a probe copy of it (shape_specialised_bf16_amd.clock_probe); None for
+    candidates the probe does not cover (split-K, split tail) or if it fails."""
+    from shape_specialised_bf16_amd import clock_probe
+    try:
+        r = clock_probe.measure(N, K, "bf16", name, X, Wrot, Y, M, launches=20, warm_s=0.1)
+    except (RuntimeError, ValueError, OSError) as e:
+        log(f"  clock probe of {name} at M={M}: {e}")
+        return None
+    if r:
+        log(f"  clock probe {name} {N}x{K} M={M}: {r['mhz_weighted']} MHz (workgroups p10 {r['mhz_p10']}, "
+            f"p90 {r['mhz_p90']}); probe copy {r['probe_tflops']} TFLOP/s")
+    return r
+
+
+def prefill_layer(plans, wl: str, Ms, rounds: int = 5, clock_from: int = 512):
     """Each projection of workload `wl` at each M (bf16 Y, weights rotating over
     >= 2 GiB of copies: a prompt block meets every weight after the other
     layers' weights have gone through the cache), steady state, sampled rows
-    checked against the oracle."""
+    checked against the oracle.  From M = `clock_from` rows (MFMA-bound) also
+    the engine clock each projection's kernel runs at and its fraction of the
+    dense peak at that clock."""
     import torch
 
     import synth
@@ -407,6 +396,13 @@ def prefill_layer(plans, wl: str, Ms, rounds: int = 5, sampler=None):
                             tflops=round(f / med / 1e6, 1), pct_peak=round(100 * f / med / 1e6 / MFMA_BF16_PEAK_TFS, 1),
                             rounds_us=dict(p10=round(pct(rs, 0.1), 2), p90=round(pct(rs, 0.9), 2)),
                             weight_copies_rotated=ncp))
+            if M >= clock_from:
+                kc = kernel_clock(p.N, p.K, plan.choice(M), X, Wrot, Y, M)
+                if kc:
+                    pk = mfma_peak_at(kc["mhz_weighted"])
+                    per[-1]["kernel_clock"] = {k: kc[k] for k in ("mhz_weighted", "mhz_p10", "mhz_p90", "probe_tflops")}
+                    per[-1]["peak_at_kernel_clock"] = round(pk, 1)
+                    per[-1]["frac_at_kernel_clock"] = round(f / med / 1e6 / pk, 4)
             del Wrot, X, Y
         tot = sum(x["us"] for x in per)
         dom = max(per, key=lambda x: x["us"])
@@ -414,13 +410,20 @@ def prefill_layer(plans, wl: str, Ms, rounds: int = 5, sampler=None):
                             pct_peak=round(100 * flops / tot / 1e6 / MFMA_BF16_PEAK_TFS, 1), projections=per,
                             dominant=dict(kernel=dom["kernel"], shape=f"{dom['N']}x{dom['K']}", us=dom["us"],
                                           tflops=dom["tflops"]))
+        if "peak_at_kernel_clock" in dom:
+            out[f"M{M}"]["dominant"].update(kernel_clock=dom["kernel_clock"], peak_at_kernel_clock=dom["peak_at_kernel_clock"],
+                                            frac_at_kernel_clock=dom["frac_at_kernel_clock"])
+        if all("peak_at_kernel_clock" in x for x in per):
+            # the layer's flops over what the dense peak at each kernel's own clock would do in the same time
+            cap = sum(x["peak_at_kernel_clock"] * 1e6 * x["us"] for x in per)
+            out[f"M{M}"]["pct_peak_at_kernel_clocks"] = round(100 * flops / cap, 1)
         log(f"  {wl} M={M}: {out[f'M{M}']['value']} TFLOP/s over the layer ({tot:.1f} us); "
             + ", ".join(f"{x['proj']} {x['tflops']}" for x in per))
         torch.cuda.empty_cache()
     return out
 
 
-def roofline_prefill(leg, M, sclk):
+def roofline_prefill(leg, M):
     """Roofline of a prefill leg's dominant kernel at M: MFMA-bound above the
     ridge point (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), HBM-bound below."""
     dom = leg[f"M{M}"]["dominant"]
@@ -435,18 +438,15 @@ def roofline_prefill(leg, M, sclk):
     else:
         r = dict(bound="mfma", achieved=dom["tflops"], peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
                  frac=round(dom["tflops"] / MFMA_BF16_PEAK_TFS, 4))
-        mhz = sclk["median_mhz"] if sclk else None
-        if mhz:
-            r["peak_at_sampled_sclk"] = round(mfma_peak_at(mhz), 1)
-            r["frac_at_sampled_sclk"] = round(dom["tflops"] / mfma_peak_at(mhz), 4)
+        if "peak_at_kernel_clock" in dom:
+            # the dense peak at the clock this kernel ran at (read inside it)
+            r.update(kernel_clock_mhz=dom["kernel_clock"]["mhz_weighted"], peak_at_kernel_clock=dom["peak_at_kernel_clock"],
+                     frac_at_kernel_clock=dom["frac_at_kernel_clock"])
     r.update(kernel=dom["kernel"], shape=dom["shape"], M=M, mean_launch_us=dom["us"], algorithmic_bytes=nbytes,
              flop_per_byte=round(fl / nbytes, 1), traffic=traffic_for(f"{dom['kernel']}@{dom['shape']}m{M}"))
     cnt = counters_for(f"{dom['kernel']}@{dom['shape']}m{M}")
     if cnt and r["bound"] == "mfma":
-        # the clock the counters saw while this kernel ran (power-limited under
-        # MFMA load), and the dense peak at that clock
-        pk = mfma_peak_at(cnt["clock_ghz"] * 1e3)
-        r.update(counters=cnt, peak_at_counter_clock=round(pk, 1), frac_at_counter_clock=round(dom["tflops"] / pk, 4))
+        r.update(counters=cnt)   # the committed counter run of this kernel (profiles/counters.json)
     return r
 
 
@@ -971,15 +971,10 @@ def main():
     torch.cuda.empty_cache()
 
     # ---- the same layer at M = 8192
-    with SclkSampler() as smp:
-        pf27 = prefill_layer(plans, "layer_27b", (8192,), rounds=5)
-    sclk27 = smp.summary()
+    pf27 = prefill_layer(plans, "layer_27b", (8192,), rounds=5)
     result["prefill_27b_m8192"] = dict(workload="layer_27b at M=8192, bf16 Y, weights rotating over >= 2 GiB",
-                                       **pf27["M8192"], sclk_during=sclk27)
-    result["roofline_prefill"] = roofline_prefill(pf27, 8192, sclk27)
-    pv = pf27["M8192"]["value"]
-    if sclk27:
-        result["prefill_27b_m8192"]["pct_peak_at_sampled_sclk"] = round(100 * pv / mfma_peak_at(sclk27["median_mhz"]), 1)
+                                       **pf27["M8192"])
+    result["roofline_prefill"] = roofline_prefill(pf27, 8192)
 
     # ---- the 0.8B-like layer and head at M = 1, and its graph replay
     d8 = decode_layer(plans, "decode_0.8b_layer_m1", "f32", args.steps, args.warmup, graph=True)
@@ -1001,24 +996,24 @@ def main():
 
     # ---- prefill: the 4B-like layer, and the long prompt
     if not args.no_prefill:
-        with SclkSampler() as smp4:
-            pf4 = prefill_layer(plans, "prefill_4b_layer", (128, 512, 2048), rounds=5)
-        s4 = smp4.summary()
+        pf4 = prefill_layer(plans, "prefill_4b_layer", (128, 512, 2048), rounds=5)
         result["prefill_4b"] = dict(workload="prefill_4b_layer: QKV 2560->5120, out 4096->2560, gate/up 2560->18432, "
-                                             "down 9216->2560, Y bf16, weights rotating over >= 2 GiB",
-                                    sclk_during=s4, **pf4)
+                                             "down 9216->2560, Y bf16, weights rotating over >= 2 GiB", **pf4)
         for M in (128, 512, 2048):
-            result["prefill_4b"][f"M{M}"]["roofline"] = roofline_prefill(pf4, M, s4)
+            result["prefill_4b"][f"M{M}"]["roofline"] = roofline_prefill(pf4, M)
         result["long_prompt"] = long_prompt(plans)
     if not args.no_extra:
         result["swiglu_epilogue"] = swiglu_leg(plans)
         result["rmsnorm_prologue"] = rmsnorm_leg(plans)
         result["packed_weights"] = packed_leg(plans)
     torch.cuda.synchronize()
+    cr = plans.created
+    result["plan_create"] = dict(plans=len(cr), total_s=round(sum(x["wall_s"] for x in cr), 1),
+                                 compile_s=round(sum(x["compile_s"] for x in cr), 1),
+                                 tune_s=round(sum(x["tune_s"] for x in cr), 1), per_plan=cr)
     plans.close()
     torch.cuda.empty_cache()
     clk["after"] = clocks()
-    clk["during_prefill_27b"] = sclk27
     result["clocks"] = clk
     result["probe"] = {"read_GBps": probe_bandwidth(), "kernel": "proj_probe_read", "bytes": 4 << 30}
     result["pct_probe"] = round(100 * value / result["probe"]["read_GBps"], 1)

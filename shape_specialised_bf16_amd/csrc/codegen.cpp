@@ -186,7 +186,13 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 3},
         // four X and five W buffers: more k-tiles in flight per workgroup for the
         // few-hundred-row blocks, whose copies wait on HBM
-        {128, 128, 64, 4, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5}, {128, 64, 64, 4, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5}};
+        {128, 128, 64, 4, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5}, {128, 64, 64, 4, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5},
+        // W rings two to four buffers deeper than X's: at 128-512 rows the W copies
+        // miss the L2 and wait ~2 us on HBM, and only W k-tiles already in flight
+        // cover that; X (shared by every tile-column) stays in the L2
+        {128, 128, 64, 3, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 6}, {128, 128, 64, 2, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5},
+        {128, 64, 64, 2, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 6}, {128, 160, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 5},
+        {256, 128, 64, 2, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}, 5}, {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 4}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
         if (wpack && 64 % g.BK) continue;  // panel layout: a k-tile inside one 64-value block

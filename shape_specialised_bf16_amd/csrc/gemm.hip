@@ -150,15 +150,16 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     // step kt; otherwise that of tile kt+STAGES-1 at the start of step kt.
     constexpr bool EARLY = DMA && STAGES == 2;
     constexpr int LEAD = EARLY ? STAGES : STAGES - 1;   // tiles in flight after the prologue
-    // BST == STAGES + 1: X (A) keeps STAGES buffers and W (B) gets one more of
-    // its own, so each W copy is issued one k-tile further ahead of its use
-    // (the copies of W are the ones that miss the L2).  BST == 0: X and W of a
-    // k-tile share one buffer.
+    // BST > STAGES: X (A) keeps STAGES buffers and W (B) gets BST of its own, so
+    // each W copy is issued BST - STAGES k-tiles further ahead of its use than
+    // X's (the copies of W are the ones that miss the L2: at a few hundred rows
+    // W streams from HBM and only the copies in flight hide its latency).
+    // BST == 0: X and W of a k-tile share one buffer.
     constexpr bool SPLIT = BST != 0;
-    static_assert(BST == 0 || (DMA && BST == STAGES + 1), "one extra W buffer on the global->LDS ring");
+    static_assert(BST == 0 || (DMA && BST > STAGES && BST <= 7), "W buffers beyond X's on the global->LDS ring");
     constexpr int NB = SPLIT ? BST : STAGES;          // W buffers
-    constexpr int LEAD_B = SPLIT ? LEAD + 1 : LEAD;   // k-tiles of W in flight after the prologue
-    constexpr int PERIOD = STAGES * (SPLIT ? BST : 1);  // ring positions before the buffer pattern repeats
+    constexpr int LEAD_B = SPLIT ? LEAD + BST - STAGES : LEAD;   // k-tiles of W in flight after the prologue
+    constexpr int PERIOD = SPLIT ? STAGES * BST / dev::gcd(STAGES, BST) : STAGES;  // ring positions before the buffer pattern repeats
     // copies younger than the ones waited for: at the prologue (after tile 0),
     // and in each step (after tile kt+1: with SPLIT, W of tile kt+2 goes out
     // right after X of tile kt+1)
@@ -170,9 +171,9 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     constexpr int KK = BK / 16;                       // MFMA k-steps per tile
 
     // X and W of ring position s: one array per buffer holding both (X first),
-    // or with SPLIT STAGES arrays of X and STAGES+1 of W (each buffer its own
-    // array in either case; 5 x 32 KiB for 256x256x64 over two buffers, 3 x 32
-    // + 4 x 16 KiB for 256x128x64 over three)
+    // or with SPLIT STAGES arrays of X and BST of W (each buffer its own array in
+    // either case; 5 x 32 KiB for 256x256x64 with two X and three W buffers,
+    // 3 x 16 + 6 x 16 KiB for 128x128x64 with three X and six W buffers)
     constexpr int SZ = SPLIT ? CA : STAGE;
     __shared__ u32x4 lds0[SZ];
     __shared__ u32x4 lds1[SZ];
@@ -183,12 +184,14 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     __shared__ u32x4 ldsb2[SPLIT ? CB : 1];
     __shared__ u32x4 ldsb3[SPLIT && BST > 3 ? CB : 1];
     __shared__ u32x4 ldsb4[SPLIT && BST > 4 ? CB : 1];
+    __shared__ u32x4 ldsb5[SPLIT && BST > 5 ? CB : 1];
+    __shared__ u32x4 ldsb6[SPLIT && BST > 6 ? CB : 1];
     auto buf = [&](int s) -> u32x4* { return s == 0 ? lds0 : s == 1 ? lds1 : s == 2 ? lds2 : lds3; };
     auto bufA = [&](int s) -> u32x4* { return buf(s % STAGES); };
     auto bufB = [&](int s) -> u32x4* {
         if constexpr (SPLIT) {
             const int t = s % NB;
-            return t == 0 ? ldsb0 : t == 1 ? ldsb1 : t == 2 ? ldsb2 : t == 3 ? ldsb3 : ldsb4;
+            return t == 0 ? ldsb0 : t == 1 ? ldsb1 : t == 2 ? ldsb2 : t == 3 ? ldsb3 : t == 4 ? ldsb4 : t == 5 ? ldsb5 : ldsb6;
         } else {
             return buf(s % STAGES) + CA;
         }

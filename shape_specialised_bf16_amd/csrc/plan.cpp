@@ -442,6 +442,7 @@ struct Tuner {
     // copies together larger than the last-level cache (allocated on first use)
     std::vector<void*> wrot;
     void* wrot_buf = nullptr;
+    int next_copy = 0;
 
     ~Tuner()
     {
@@ -675,15 +676,21 @@ struct Tuner {
         return PROJ_OK;
     }
 
-    // At decode (M <= 16) the projections of a step run one after another, each
-    // reading weights no cache holds.  So a decode candidate is timed in that
-    // regime: launches back to back, each on the next of several weight copies
-    // that together exceed the 256 MB last-level cache (1 GiB); the median over `reps`
-    // rounds of the mean per launch.  (Timed one launch at a time after a cache
-    // flush instead, the ranking of near-equal GEMVs differed from the one
-    // measured back to back: a 10240x5120 GEMV with cached loads came out first
-    // and ran 6 % slower than the pick of the back-to-back timing.)
-    int time_decode(const Candidate& c, int64_t M, int reps, double* us)
+    // The projections of a model run one after another, each on weights that no
+    // cache holds: a decode step streams every weight once, and a prompt block
+    // meets each layer's weights after the other layers' have gone through the
+    // 256 MB last-level cache.  So every candidate is timed in that regime:
+    // launches back to back, each on the next of several weight copies that
+    // together exceed that cache (1 GiB), in rounds of L launches -- all copies
+    // for a decode GEMV (M <= 16), about 0.5 ms of work (at least 2 launches)
+    // for a GEMM -- and the median over `reps` rounds of the mean per launch.
+    // (Timed one launch at a time after a cache flush instead, the ranking of
+    // near-equal kernels differed from the one measured back to back: a
+    // 10240x5120 GEMV with cached loads came out first and ran 6 % slower than
+    // the back-to-back pick, and a single launch of a 5120x2560 GEMM at 512 rows
+    // took 24 us where back to back on rotating weights it takes 29.5 us, on
+    // the same weights left in the last-level cache 21 us.)
+    int time_rotating(const Candidate& c, int64_t M, int reps, double* us)
     {
         const size_t wb = (size_t)p->N * p->K * 2;
         if (wrot.empty()) {
@@ -705,32 +712,50 @@ struct Tuner {
         }
         const int n = (int)wrot.size();
         int rc;
-        for (int i = 0; i < n; ++i)
-            if ((rc = launch_candidate(p, c, Xr, wrot[i], Y, M, st, gamma))) return rc;
-        std::vector<double> t;
-        for (int r = 0; r < reps; ++r) {
+        // the next copy to read: the rotation goes on across rounds and candidates
+        auto launch_next = [&](int i) -> int {
+            const int w = next_copy;
+            next_copy = (next_copy + 1) % n;
+            return launch_candidate(p, c, (i & 1) ? Xi : Xr, wrot[w], Y, M, st, gamma);
+        };
+        int L = n;
+        if (M > 16) {
+            // two launches estimate the time per launch; rounds of about 0.5 ms
             HIP_TRY(hipEventRecord(e0, st));
-            for (int i = 0; i < n; ++i)
-                if ((rc = launch_candidate(p, c, (i & 1) ? Xi : Xr, wrot[i], Y, M, st, gamma))) return rc;
+            for (int i = 0; i < 2; ++i)
+                if ((rc = launch_next(i))) return rc;
             HIP_TRY(hipEventRecord(e1, st));
             HIP_TRY(hipEventSynchronize(e1));
             float ms = 0;
             HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
-            t.push_back(ms * 1000.0 / n);
+            const double est = std::max(1.0, ms * 1000.0 / 2);
+            L = (int)std::min<double>(n, std::max(2.0, std::ceil(500.0 / est)));
+        }
+        for (int i = 0; i < L; ++i)   // one untimed round
+            if ((rc = launch_next(i))) return rc;
+        std::vector<double> t;
+        for (int r = 0; r < reps; ++r) {
+            HIP_TRY(hipEventRecord(e0, st));
+            for (int i = 0; i < L; ++i)
+                if ((rc = launch_next(i))) return rc;
+            HIP_TRY(hipEventRecord(e1, st));
+            HIP_TRY(hipEventSynchronize(e1));
+            float ms = 0;
+            HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+            t.push_back(ms * 1000.0 / L);
         }
         std::sort(t.begin(), t.end());
         *us = t[t.size() / 2];
         return PROJ_OK;
     }
 
-    // Median launch time in microseconds over `reps` launches at M rows.
+    // Median launch time in microseconds at M rows: back to back on rotating
+    // weights, or (if the copies do not fit in memory) one launch at a time
+    // after a cache flush.
     int time_candidate(const Candidate& c, int64_t M, int reps, double* us)
     {
-        int rc;
-        if (M <= 16) {
-            rc = time_decode(c, M, reps, us);
-            if (rc != PROJ_ENOMEM) return rc;
-        }
+        int rc = time_rotating(c, M, reps, us);
+        if (rc != PROJ_ENOMEM) return rc;
         for (int i = 0; i < 2; ++i)
             if ((rc = launch_candidate(p, c, Xr, Wrc, Y, M, st, gamma))) return rc;
         std::vector<double> t;

@@ -7,6 +7,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# The tests check what the tuned plans compute, not which candidate wins: half
+# the tuner's default timing rounds keeps the GPU session short.
+os.environ.setdefault("PROJ_TUNE_REPS", "5")
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")

@@ -20,6 +20,7 @@ the wait count have landed is the whole workgroup.  The wait counts are the
 kernel's constants; the test also checks that gemm.hip still defines them as
 modelled here.
 """
+import math
 import os
 import re
 
@@ -36,8 +37,8 @@ KERNEL_LINES = [
     "constexpr int LEAD = EARLY ? STAGES : STAGES - 1;",
     "constexpr bool SPLIT = BST != 0;",
     "constexpr int NB = SPLIT ? BST : STAGES;",
-    "constexpr int LEAD_B = SPLIT ? LEAD + 1 : LEAD;",
-    "constexpr int PERIOD = STAGES * (SPLIT ? BST : 1);",
+    "constexpr int LEAD_B = SPLIT ? LEAD + BST - STAGES : LEAD;",
+    "constexpr int PERIOD = SPLIT ? STAGES * BST / dev::gcd(STAGES, BST) : STAGES;",
     "constexpr int WAIT0 = (LEAD - 1) * IA + (LEAD_B - 1) * IB;",
     "constexpr int WAITK = (SPLIT ? IB : 0) + (DMA && !EARLY ? (STAGES - 2) * PER_TILE : 0);",
 ]
@@ -48,8 +49,8 @@ def ring_constants(STAGES, DMA, BST, IA, IB):
     LEAD = STAGES if EARLY else STAGES - 1
     SPLIT = BST != 0
     NB = BST if SPLIT else STAGES
-    LEAD_B = LEAD + 1 if SPLIT else LEAD
-    PERIOD = STAGES * (BST if SPLIT else 1)
+    LEAD_B = LEAD + BST - STAGES if SPLIT else LEAD
+    PERIOD = STAGES * BST // math.gcd(STAGES, BST) if SPLIT else STAGES
     WAIT0 = (LEAD - 1) * IA + (LEAD_B - 1) * IB
     WAITK = (IB if SPLIT else 0) + ((STAGES - 2) * (IA + IB) if DMA and not EARLY else 0)
     return dict(EARLY=EARLY, LEAD=LEAD, SPLIT=SPLIT, NB=NB, LEAD_B=LEAD_B, PERIOD=PERIOD,
@@ -182,6 +183,9 @@ def test_kernel_defines_the_modelled_constants():
 def test_configurations_cover_every_ring_kind():
     kinds = {(ST, DMA, BST > 0) for (_, _, _, ST, _, _, _, DMA, _, BST, _) in CONFIGS}
     assert {(2, 1, False), (2, 1, True), (3, 1, False), (3, 1, True), (2, 0, False)} <= kinds, kinds
+    # W rings deeper than X's by more than one buffer, on both ring kinds
+    deep = {(ST, BST - ST) for (_, _, _, ST, _, _, _, DMA, _, BST, _) in CONFIGS if BST > ST + 1}
+    assert any(st == 2 for st, _ in deep) and any(st == 3 for st, _ in deep), deep
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: "{}x{}x{}_st{}_w{}x{}_sk{}_dma{}_t{}_b{}_K{}".format(*c))
@@ -199,7 +203,7 @@ def test_ring_waits_are_exact_for_every_tile_count(cfg):
         replay(nkt, ST, DMA, BST, IA, IB, BK // 16)
 
 
-@pytest.mark.parametrize("ST,BST", [(2, 0), (2, 3), (3, 0), (3, 4)])
+@pytest.mark.parametrize("ST,BST", [(2, 0), (2, 3), (2, 4), (2, 6), (3, 0), (3, 4), (3, 6), (4, 7)])
 def test_model_rejects_a_wait_one_copy_short(ST, BST):
     """A wait that leaves one more copy instruction outstanding than the kernel's
     count lets a read find its tile partly landed: the model must see it."""

@@ -166,6 +166,5 @@ constexpr long kPanelRows = 128, kPanelCols = 64;
 
 template <int V> struct log2_of { static constexpr int value = 1 + log2_of<V / 2>::value; };
 template <> struct log2_of<1> { static constexpr int value = 0; };
-constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
 
 }  // namespace dev

@@ -76,6 +76,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <long V> struct ic { static constexpr long value = V; };
 
+constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+
 // f(ic<I>{}, kt0 + I) for I = FROM .. TO-1, unrolled at compile time.
 template <long FROM, long TO, typename F>
 __device__ __forceinline__ void unroll_steps(F&& f, long kt0)
@@ -159,7 +161,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     static_assert(BST == 0 || (DMA && BST > STAGES && BST <= 7), "W buffers beyond X's on the global->LDS ring");
     constexpr int NB = SPLIT ? BST : STAGES;          // W buffers
     constexpr int LEAD_B = SPLIT ? LEAD + BST - STAGES : LEAD;   // k-tiles of W in flight after the prologue
-    constexpr int PERIOD = SPLIT ? STAGES * BST / dev::gcd(STAGES, BST) : STAGES;  // ring positions before the buffer pattern repeats
+    constexpr int PERIOD = SPLIT ? STAGES * BST / gcd(STAGES, BST) : STAGES;  // ring positions before the buffer pattern repeats
     // copies younger than the ones waited for: at the prologue (after tile 0),
     // and in each step (after tile kt+1: with SPLIT, W of tile kt+2 goes out
     // right after X of tile kt+1)

@@ -38,7 +38,7 @@ KERNEL_LINES = [
     "constexpr bool SPLIT = BST != 0;",
     "constexpr int NB = SPLIT ? BST : STAGES;",
     "constexpr int LEAD_B = SPLIT ? LEAD + BST - STAGES : LEAD;",
-    "constexpr int PERIOD = SPLIT ? STAGES * BST / dev::gcd(STAGES, BST) : STAGES;",
+    "constexpr int PERIOD = SPLIT ? STAGES * BST / gcd(STAGES, BST) : STAGES;",
     "constexpr int WAIT0 = (LEAD - 1) * IA + (LEAD_B - 1) * IB;",
     "constexpr int WAITK = (SPLIT ? IB : 0) + (DMA && !EARLY ? (STAGES - 2) * PER_TILE : 0);",
 ]

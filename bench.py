@@ -351,10 +351,12 @@ def kernel_clock(N, K, name, X, Wrot, Y, M):
     """The engine clock the tuned GEMM `name` runs at under its own load, read
     inside a probe copy of it (shape_specialised_bf16_amd.clock_probe); None for
     candidates the probe does not cover (split-K, split tail) or if it fails."""
+    import subprocess
+
     from shape_specialised_bf16_amd import clock_probe
     try:
         r = clock_probe.measure(N, K, "bf16", name, X, Wrot, Y, M, launches=20, warm_s=0.1)
-    except (RuntimeError, ValueError, OSError) as e:
+    except (RuntimeError, ValueError, OSError, subprocess.SubprocessError) as e:
         log(f"  clock probe of {name} at M={M}: {e}")
         return None
     if r:

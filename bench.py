@@ -622,8 +622,8 @@ def rmsnorm_leg(plans, steps: int = 500):
 def packed_leg(plans, steps: int = 300, rounds: int = 3):
     """Weights in the packed layout (proj_pack_weights once, then
     proj_run_packed) against row-major, each on its own tuned plan: the
-    0.8B-like decode step (rotating weights) and the 27B-like gate/up at
-    M = 8192, timed in alternation."""
+    0.8B-like decode step (rotating weights), the 27B-like gate/up at
+    M = 8192 and the 4B-like layer at M = 128 and 512, timed in alternation."""
     import torch
 
     import synth
@@ -689,6 +689,33 @@ def packed_leg(plans, steps: int = 300, rounds: int = 3):
                                     kernel_packed=b.choice(M), weight_copies_rotated=n)
     log(f"  packed 27B gate/up M=8192: {out['gate_up_27b_m8192']['packed']} TFLOP/s vs row-major "
         f"{out['gate_up_27b_m8192']['rows']}")
+    del Wrot, Wprot, Ya, Yb
+    # the 4B-like layer at the row counts where its GEMMs stream W from HBM
+    cfg4 = synth.workload("prefill_4b_layer")
+    for M in (128, 512):
+        tr_sum = tp_sum = flops = 0.0
+        kern = {}
+        for i, p in enumerate(cfg4.projections):
+            wh, xh = weights(cfg4, i), synth.activations(cfg4, i, M)
+            W, X = upload(wh), upload(xh)
+            Wrot = rotation(W)
+            Wprot = [pack_weights(w) for w in Wrot]
+            n = len(Wrot)
+            a, b = plans.get(p.N, p.K, "bf16"), plans.get(p.N, p.K, "bf16", packed=True)
+            Ya, Yb = (torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+            tr, tp = alternate(lambda s: a.run_ptr(X.data_ptr(), Wrot[s % n].data_ptr(), Ya.data_ptr(), M, sh),
+                               lambda s: b.run_ptr(X.data_ptr(), Wprot[s % n].data_ptr(), Yb.data_ptr(), M, sh),
+                               max(n, 100))
+            _check_rows(Yb, xh, wh, [0, M // 2, M - 1], "bf16", f"packed {p.name} M={M}")
+            tr_sum, tp_sum, flops = tr_sum + tr, tp_sum + tp, flops + 2.0 * M * p.N * p.K
+            kern[p.name] = dict(rows=a.choice(M), packed=b.choice(M), rows_us=round(tr, 2), packed_us=round(tp, 2))
+            del Wrot, Wprot, W, X, Ya, Yb
+            torch.cuda.empty_cache()
+        out[f"prefill_4b_m{M}"] = dict(unit="TFLOP/s", rows=round(flops / tr_sum / 1e6, 1),
+                                       packed=round(flops / tp_sum / 1e6, 1), packed_over_rows=round(tr_sum / tp_sum, 3),
+                                       projections=kern)
+        log(f"  packed 4B layer M={M}: {out[f'prefill_4b_m{M}']['packed']} TFLOP/s vs row-major "
+            f"{out[f'prefill_4b_m{M}']['rows']}")
     return out
 
 

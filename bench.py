@@ -20,7 +20,9 @@ Reported (one JSON line on stdout; progress on stderr):
                traffic from the committed rocprofv3 counter runs
   per_shape    every M = 1 projection of the step alone: GB/s (mean over
                back-to-back launches) and median / p10 / p90 of single
-               launches (an event pair each)
+               launches (an event pair each); launch_bound marks shapes whose
+               ideal time at 8 TB/s is under 5 us
+  graph        the same step recorded as a HIP graph and replayed
   prefill_27b_m8192  the same layer at M = 8192: TFLOP/s per projection and
                for the layer, against 2.5 PFLOP/s and against
                256 CUs x 4096 flop/clk x the engine clock each kernel ran at,
@@ -297,7 +299,9 @@ def decode_layer(plans, wl: str, dtype: str, steps: int, warmup: int, graph: boo
         warm(one, 10.0)
         b2b = statistics.median(events_us(one, 200) for _ in range(3))
         single = per_call_us(one, 300)
+        ideal = bytes_of[i] / HBM_PEAK_GBS / 1e3      # us at 8 TB/s
         per.append(dict(proj=p.name, N=p.N, K=p.K, kernel=pl[i].choice(1), bytes=bytes_of[i],
+                        ideal_us=round(ideal, 2), launch_bound=ideal < 5.0,
                         mean_launch_us=round(b2b, 3), GBps=round(bytes_of[i] / b2b / 1e3, 1),
                         pct_peak=round(100 * bytes_of[i] / b2b / 1e3 / HBM_PEAK_GBS, 1),
                         single_launch_us=dist(single),
@@ -949,7 +953,7 @@ def main():
     plans = Plans()
 
     # ---- headline: the 27B-like layer at M = 1
-    d = decode_layer(plans, "layer_27b", "bf16", args.steps, args.warmup)
+    d = decode_layer(plans, "layer_27b", "bf16", args.steps, args.warmup, graph=True)
     value = d["step_bytes"] / d["step_us"] / 1e3
     dom = max(d["per_shape"], key=lambda x: x["bytes"])
     log(f"decode 27B layer M=1: {d['step_us']:.2f} us/step, {value:.0f} GB/s; "
@@ -995,6 +999,7 @@ def main():
             "single_launch_us": dom["single_launch_us"],
         },
         "per_shape": d["per_shape"],
+        "graph": d["graph"],
     }
     host27 = d.pop("host")
     torch.cuda.empty_cache()

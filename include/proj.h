@@ -79,7 +79,10 @@ enum {
  *
  * Environment (read at creation): PROJ_LOG=1 prints the tuner log to stderr;
  * PROJ_TUNE=0 skips timing and takes the first candidate that validates;
- * PROJ_TUNE_REPS=<n> sets timed launches per candidate; PROJ_FORCE=<name>
+ * PROJ_TUNE_REPS=<n> (default 10, at least 3) sets the timing rounds of each
+ * candidate that a first screen of three rounds puts within 10 % of the best (a
+ * round: launches back to back on rotating copies of the probe weights that
+ * exceed the last-level cache); PROJ_FORCE=<name>
  * keeps only that candidate (plus the plain kernel) where it applies;
  * PROJ_DUMP_DIR=<dir> writes the generated source and code object there;
  * PROJ_CACHE_DIR=<dir> turns on the persistent tuning cache: the choices of a
@@ -90,9 +93,10 @@ enum {
  * candidates, and tunes afresh any bucket whose cached choice is unknown or
  * fails the gate (the cache the pages propose, and doubt because machine state
  * drifts: "#004 the same compiler on Apple's chips", section "So, does it start
- * up more slowly?").  The compiled module is kept under the same key (<dir>/proj-<key>.co,
- * the key also covering the compile options), so such a plan skips hipRTC as
- * well; a file that does not load is compiled afresh and replaced.
+ * up more slowly?").  The compiled modules are kept under the same key
+ * (<dir>/proj-<key>.m<g>.co, the key also covering the compiler and its
+ * options), so such a plan skips hipRTC as well; a file that does not load is
+ * compiled afresh and replaced.
  * proj_plan_describe reports "cache" and "code_cache": off, miss, hit or stale.
  */
 proj_plan* proj_plan_create(int64_t N, int64_t K, int dtype);

@@ -1057,13 +1057,23 @@ int tune_plan(proj_plan* p)
         double best_us = -1;
         if (do_time && ok.size() > 1) {
             std::string tl;
+            // A screen of three rounds per candidate, then the full `reps`
+            // rounds for those within 10 % of the screen's best (most of the
+            // list is far slower and needs no more than the screen to say so).
+            const int screen = std::min(3, reps);
+            double screen_best = -1;
             for (int ci : ok) {
                 double us = 0;
-                if ((rc = T.time_candidate(p->cands[ci], Mfull, reps, &us))) return rc;
+                if ((rc = T.time_candidate(p->cands[ci], Mfull, screen, &us))) return rc;
                 p->timings[b].push_back({ci, us});
-                if (best_us < 0 || us < best_us) {
-                    best_us = us;
-                    best = ci;
+                if (screen_best < 0 || us < screen_best) screen_best = us;
+            }
+            for (auto& t : p->timings[b]) {
+                if (reps > screen && t.second <= screen_best * 1.10)
+                    if ((rc = T.time_candidate(p->cands[t.first], Mfull, reps, &t.second))) return rc;
+                if (best_us < 0 || t.second < best_us) {
+                    best_us = t.second;
+                    best = t.first;
                 }
             }
             // Finalists: the (at most four) candidates within 5 % of the fastest,

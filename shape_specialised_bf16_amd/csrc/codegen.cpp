@@ -187,9 +187,10 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         // four X and five W buffers: more k-tiles in flight per workgroup for the
         // few-hundred-row blocks, whose copies wait on HBM
         {128, 128, 64, 4, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5}, {128, 64, 64, 4, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5},
-        // W rings two to four buffers deeper than X's: at 128-512 rows the W copies
-        // miss the L2 and wait ~2 us on HBM, and only W k-tiles already in flight
-        // cover that; X (shared by every tile-column) stays in the L2
+        // W rings two to four buffers deeper than X's (the tuner's choice: they
+        // time within about 1 % of the one-deeper ring, because a wave's copies
+        // complete in order and its wait for X also covers the W copies it issued
+        // before; the 256 x 192 tile with four W buffers wins at 2048 rows)
         {128, 128, 64, 3, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 6}, {128, 128, 64, 2, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5},
         {128, 64, 64, 2, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 6}, {128, 160, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 5},
         {256, 128, 64, 2, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}, 5}, {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 4}};

@@ -23,6 +23,7 @@ Reported (one JSON line on stdout; progress on stderr):
                launches (an event pair each); launch_bound marks shapes whose
                ideal time at 8 TB/s is under 5 us
   graph        the same step recorded as a HIP graph and replayed
+  host_call_us the host time of one proj_run call through the binding
   prefill_27b_m8192  the same layer at M = 8192: TFLOP/s per projection and
                for the layer, against 2.5 PFLOP/s and against
                256 CUs x 4096 flop/clk x the engine clock each kernel ran at,
@@ -306,8 +307,16 @@ def decode_layer(plans, wl: str, dtype: str, steps: int, warmup: int, graph: boo
                         pct_peak=round(100 * bytes_of[i] / b2b / 1e3 / HBM_PEAK_GBS, 1),
                         single_launch_us=dist(single),
                         single_launch_GBps_median=round(bytes_of[i] / statistics.median(single) / 1e3, 1)))
+    # host cost of one proj_run call through the Python binding (argument
+    # checks, bucket lookup, the enqueue of its kernel): 200 calls, not waited for
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(200):
+        pl[0].run_ptr(xptr[0], wptr[0][0], yptr[0], 1, sh)
+    host_us = (time.perf_counter() - t0) * 1e6 / 200
+    torch.cuda.synchronize()
     out = dict(step_us=t_us, step_bytes=step_bytes, weight_copies_rotated=ncp, device_warmup_ms=round(warm_ms, 1),
-               step_dist_us=dist(step_us), per_shape=per)
+               step_dist_us=dist(step_us), per_shape=per, host_call_us=round(host_us, 2))
     if graph:
         # the same steps recorded by stream capture as one HIP graph per
         # rotation of the weight copies, replayed
@@ -1000,6 +1009,7 @@ def main():
         },
         "per_shape": d["per_shape"],
         "graph": d["graph"],
+        "host_call_us": d["host_call_us"],
     }
     host27 = d.pop("host")
     torch.cuda.empty_cache()
@@ -1018,7 +1028,7 @@ def main():
                                 value=round(v8, 1), unit="GB/s", pct_peak=round(100 * v8 / HBM_PEAK_GBS, 1),
                                 step_us=round(d8["step_us"], 3), step_dist_us=d8["step_dist_us"],
                                 bytes_per_step=d8["step_bytes"], weight_copies_rotated=d8["weight_copies_rotated"],
-                                per_shape=d8["per_shape"], graph=d8["graph"])
+                                per_shape=d8["per_shape"], graph=d8["graph"], host_call_us=d8["host_call_us"])
     hd = max(d8["per_shape"], key=lambda x: x["bytes"])
     result["decode_08b"]["roofline"] = dict(bound="hbm", kernel=hd["kernel"], shape=f"{hd['N']}x{hd['K']}",
                                             achieved=hd["GBps"], peak=HBM_PEAK_GBS, unit="GB/s",

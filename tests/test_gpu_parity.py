@@ -52,7 +52,10 @@ def test_odd_shape_1000x520(M):
 
 
 # ------------------------------------------------------------------ every candidate, exact integers
-@pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16"), (1000, 520, "f32")])
+# 3840 columns: a multiple of every tile width (64, 128, 160, 192, 256), so every GEMM
+# kind the generator has is compiled for it
+@pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16"), (1000, 520, "f32"),
+                                       (3840, 1024, "bf16")])
 def test_every_candidate_bit_exact_on_integer_probe(N, K, dtype):
     """With integer inputs in [-4, 4] every summation order is exact, so every
     compiled candidate -- not only the tuned winners -- must reproduce the
@@ -104,7 +107,7 @@ def test_split_tail_candidates_with_whole_and_tail_tiles(M):
         G.log(f"  {name} M={M}: bit-exact on sampled rows, all rows written")
 
 
-@pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16")])
+@pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16"), (3840, 1024, "bf16")])
 def test_every_candidate_within_tolerance_on_random_inputs(N, K, dtype):
     p = G.plan(N, K, dtype)
     W = synth.normal_bf16(62, 0, (N, K), 0.02)

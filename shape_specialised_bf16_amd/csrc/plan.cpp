@@ -433,6 +433,7 @@ struct Tuner {
     CheckStats* stats_d = nullptr;
     void* flush = nullptr;
     size_t flush_bytes = 0;
+    bool flush_tried = false;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     int64_t mmax = 0;
     static constexpr int64_t kGuardRows = 3;
@@ -511,18 +512,6 @@ struct Tuner {
             hipMalloc(&stats_d, sizeof(CheckStats)) != hipSuccess)
             return set_error(PROJ_ENOMEM, "tuner probe buffers (%zu MiB) could not be allocated",
                              (2 * xb + 2 * wb + yb) >> 20);
-        // A read of more than the 256 MB last-level cache before each timed launch,
-        // so the launch reads its weights from HBM, as every decode step does.
-        flush_bytes = (size_t)512 << 20;
-        if (hipMalloc(&flush, flush_bytes) != hipSuccess) {
-            // tuned without the flush; clear the runtime's last error so that a
-            // caller checking it later does not see this tolerated failure
-            (void)hipGetLastError();
-            flush = nullptr;
-            flush_bytes = 0;
-        } else {
-            HIP_TRY(hipMemsetAsync(flush, 0, flush_bytes, st));
-        }
         int rc;
         if ((rc = fill_probe(Xr, mmax * p->K, 1, 0, 1.0f))) return rc;
         if ((rc = fill_probe(Wr, p->N * p->K, 2, 0, 0.0625f))) return rc;
@@ -663,8 +652,24 @@ struct Tuner {
         return PROJ_OK;
     }
 
+    // A read of more than the 256 MB last-level cache before a timed launch, so
+    // the launch reads its weights from HBM (only where the rotating weight
+    // copies could not be allocated; the buffer is allocated on first use).
     int flush_cache()
     {
+        if (!flush && !flush_tried) {
+            flush_tried = true;
+            flush_bytes = (size_t)512 << 20;
+            if (hipMalloc(&flush, flush_bytes) != hipSuccess) {
+                // timed without the flush; clear the runtime's last error so that a
+                // caller checking it later does not see this tolerated failure
+                (void)hipGetLastError();
+                flush = nullptr;
+                flush_bytes = 0;
+            } else {
+                HIP_TRY(hipMemsetAsync(flush, 0, flush_bytes, st));
+            }
+        }
         if (!flush) return PROJ_OK;
         const void* fp = flush;
         long n16 = (long)(flush_bytes / 16);

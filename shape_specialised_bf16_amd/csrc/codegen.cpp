@@ -193,7 +193,9 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         // before; the 256 x 192 tile with four W buffers wins at 2048 rows)
         {128, 128, 64, 3, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 6}, {128, 128, 64, 2, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5},
         {128, 64, 64, 2, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 6}, {128, 160, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 5},
-        {256, 128, 64, 2, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}, 5}, {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 4}};
+        {256, 128, 64, 2, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}, 5}, {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 4},
+        // 96 columns (three 32-column MFMA blocks, four waves of 32 x 96)
+        {128, 96, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 4}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
         if (wpack && 64 % g.BK) continue;  // panel layout: a k-tile inside one 64-value block

@@ -158,7 +158,7 @@ def emitted_configs():
     """(BM, BN, BK, STAGES, WM, WN, SK, DMA, TAILS, BST) and K of every gemm_mfma
     instantiation the generator emits for a spread of shapes."""
     shapes = [(7168, 1024, "f32", {}), (2560, 9216, "bf16", {}), (34816, 5120, "bf16", {}),
-              (5120, 17408, "bf16", {}), (18432, 2560, "bf16", dict(epilogue="swiglu")),
+              (5120, 17408, "bf16", {}), (18432, 2560, "bf16", {}), (18432, 2560, "bf16", dict(epilogue="swiglu")),
               (7168, 1024, "bf16", dict(packed=True))]
     out = set()
     for N, K, dt, kw in shapes:

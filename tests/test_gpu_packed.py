@@ -62,11 +62,14 @@ def test_pack_rejects_bad_arguments():
         ssb.Plan(1000, 520, "f32", packed=True)
 
 
-@pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16"), (1024, 3584, "f32")])
+@pytest.mark.parametrize("N,K,dtype", [(7168, 1024, "f32"), (2560, 9216, "bf16"), (1024, 3584, "f32"),
+                                     (3840, 1024, "bf16")])
 def test_every_packed_candidate_equals_row_major(N, K, dtype):
     """Same candidate, same inputs: the packed plan's output equals the
     row-major plan's bit for bit, at full, partial and odd row counts, and
-    nothing is written past M."""
+    nothing is written past M.  (3840 columns are a multiple of every tile
+    width, 64 to 256, so tiles that straddle the 128-row panels are among
+    them.)"""
     import torch
     pk = G.plan(N, K, dtype, packed=True)
     pr = G.plan(N, K, dtype)

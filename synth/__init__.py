@@ -57,6 +57,33 @@ def int_bf16(seed: int, shape, lim: int = 4) -> np.ndarray:
     return bf16_from_f32(v)
 
 
+def norm_boundary_case(K: int, seed: int = 0):
+    """Rows and norm weights whose normalised values sit next to bf16 rounding
+    boundaries (for tests that must tell the divisor of the mean and the place
+    of epsilon apart, which a one-ulp comparison on random rows cannot).
+
+    Returns (X, gamma, lo, hi):
+      X      bf16 bits [2, K]: row 0 all ones, row 1 all 2^-10;
+      gamma  f32 [K]: gamma[j] = f32(m_j * (1 + 1/(4K))), where m_j is the
+             midpoint between a random bf16 value v_j (|v_j| in [0.5, 2), random
+             sign) and its neighbour one ulp further from zero;
+      lo, hi the bf16 bits of v_j and of that neighbour."""
+    g = rng(90000 + K, seed, 0)
+    mag = g.uniform(0.5, 2.0, size=K).astype(np.float32)
+    lo = bf16_from_f32(mag)
+    lo = np.where(lo >= 0x4000, np.uint16(0x3FFF), lo).astype(np.uint16)   # keep |v| < 2 after the step up
+    hi = (lo + 1).astype(np.uint16)
+    sign = (g.random(size=K) < 0.5).astype(np.uint16) << 15
+    lo, hi = lo | sign, hi | sign
+    wide = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    mid = (wide(lo) + wide(hi)) / 2.0
+    gamma = (mid * (1.0 + 1.0 / (4.0 * K))).astype(np.float32)
+    X = np.empty((2, K), dtype=np.uint16)
+    X[0] = 0x3F80                     # 1.0
+    X[1] = 0x3A80                     # 2^-10
+    return X, gamma, lo, hi
+
+
 @dataclass(frozen=True)
 class Projection:
     name: str

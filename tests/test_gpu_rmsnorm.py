@@ -57,6 +57,51 @@ def test_norm_kernel_against_oracle(K):
     assert np.all(np.abs(got - R) <= tolerance.bf16_ulp(R)), np.max(np.abs(got - R) / tolerance.bf16_ulp(R))
 
 
+@pytest.mark.parametrize("K", [520, 1024, 5120, 17408])
+def test_norm_kernel_on_boundary_rows(K):
+    """Rows whose normalised values sit next to bf16 rounding boundaries
+    (synth.norm_boundary_case; the oracle's pins show that a mean over K - 1
+    terms rounds row 0 the other way at every element, and that a misplaced or
+    different epsilon moves row 1 by more than an ulp): row 0 must come out
+    exactly as the oracle rounds it, row 1 within one bf16 ulp."""
+    import shape_specialised_bf16_amd as ssb
+    import torch
+    X, g, lo, hi = synth.norm_boundary_case(K)
+    Xn = G.host(ssb.rmsnorm(G.dev(X), torch.from_numpy(g).cuda(), EPS)).view(np.uint16)   # bits as uploaded
+    R = oracle.round_bf16(oracle.rmsnorm(X, g, EPS))
+    assert np.array_equal(R[0], hi)
+    assert np.array_equal(Xn[0], R[0]), f"{int(np.sum(Xn[0] != R[0]))} of {K} elements of row 0 differ"
+    got1, ref1 = oracle.bf16_bits_to_f64(Xn[1]), oracle.bf16_bits_to_f64(R[1])
+    assert np.all(np.abs(got1 - ref1) <= tolerance.bf16_ulp(ref1))
+
+
+def test_folded_norm_on_boundary_row():
+    """The norm folded into the M = 1 decode kernels on the same row 0: every
+    folded candidate equals the plain candidate run on the separate kernel's
+    output, whose bits the test above fixes exactly."""
+    import shape_specialised_bf16_amd as ssb
+    import torch
+    N, K = 2048, 1024
+    X, g, lo, hi = synth.norm_boundary_case(K)
+    gd = torch.from_numpy(g).cuda()
+    W = synth.normal_bf16(98, 0, (N, K), 0.02)
+    Wd = G.dev(W)
+    pn, pp = G.plan(N, K, "f32", rmsnorm_eps=EPS), G.plan(N, K, "f32")
+    Xd = G.dev(X[:1])
+    Xn = ssb.rmsnorm(Xd, gd, EPS)
+    assert np.array_equal(G.host(Xn).view(np.uint16)[0], hi)
+    folded = [i for i, n in enumerate(pn.candidates()) if n.endswith("_nf")]
+    assert folded, "no folded candidate"
+    for i in folded:
+        name = pn.candidates()[i]
+        j = pp.candidates().index(name[: -len("_nf")])
+        Yf = G.empty_out(1, N, "f32")
+        pn.run_candidate(i, Xd, Wd, Yf, gamma=gd)
+        Yp = G.empty_out(1, N, "f32")
+        pp.run_candidate(j, Xn, Wd, Yp)
+        assert np.array_equal(G.host(Yf).view(np.uint8), G.host(Yp).view(np.uint8)), name
+
+
 @pytest.mark.parametrize("N,K,dtype", [(2048, 1024, "f32"), (10240, 5120, "bf16"), (1000, 520, "f32")])
 def test_folded_norm_equals_unfused(N, K, dtype):
     import torch

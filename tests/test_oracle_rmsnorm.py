@@ -83,3 +83,37 @@ def test_tolerance_accepts_device_like_rounding_and_rejects_mistakes(dtype):
     nog = oracle.rmsnorm_matmul(X, np.ones(1024, np.float32), W, 1e-6)
     nog_out = oracle.round_bf16(nog) if dtype == "bf16" else oracle.round_f32(nog)
     assert not tolerance.check_norm_projection(nog_out, ref, terms, dtype).ok
+
+
+def _planted(X, g, eps, k_minus_one=False, eps_outside=False):
+    """The normalisation with one planted mistake (a mean over K - 1 terms, or
+    epsilon added outside the square root), plain numpy in fp64: what an
+    implementation with that mistake would produce."""
+    x = oracle.bf16_bits_to_f64(X)
+    K = x.shape[1]
+    ms = (x * x).sum(axis=1) / (K - 1 if k_minus_one else K)
+    r = 1.0 / (np.sqrt(ms) + eps) if eps_outside else 1.0 / np.sqrt(ms + eps)
+    return x * r[:, None] * g.astype(np.float64)[None, :]
+
+
+@pytest.mark.parametrize("K", [520, 1024, 5120, 17408])
+def test_boundary_rows_fix_the_rounded_result(K):
+    """Row 0 of synth.norm_boundary_case is all ones, so its mean square is
+    exactly 1 and each normalised value is gamma_j / sqrt(1 + eps) =
+    m_j (1 + 1/(4K)) / sqrt(1 + 1e-6): above the rounding midpoint m_j by a
+    relative 1/(4K) - 5e-7, far more than f32 arithmetic can move it, so it
+    rounds to the neighbour `hi` for every j.  A mean over K - 1 terms scales it
+    by 1/sqrt(K/(K-1)), about 1 - 1/(2K), below every midpoint: every value
+    rounds to `lo` instead.  Row 1 (all 2^-10, mean square 2^-20 next to
+    eps = 1e-6) moves by far more than a bf16 ulp when epsilon is added outside
+    the square root, or is a different constant."""
+    eps = 1e-6
+    X, g, lo, hi = synth.norm_boundary_case(K)
+    got = oracle.round_bf16(oracle.rmsnorm(X, g, eps))
+    assert np.array_equal(got[0], hi)
+    assert np.array_equal(oracle.round_bf16(_planted(X, g, eps, k_minus_one=True))[0], lo)
+    ref1 = oracle.bf16_bits_to_f64(got[1])
+    ulp1 = tolerance.bf16_ulp(ref1)
+    for wrong in (_planted(X, g, eps, eps_outside=True), _planted(X, g, 1e-5), _planted(X, g, 0.0)):
+        w = oracle.bf16_bits_to_f64(oracle.round_bf16(wrong))[1]
+        assert np.all(np.abs(w - ref1) > ulp1)

@@ -51,6 +51,26 @@ def test_prefill_4b_layer(wl, pi, dtype):
                       (0x7FC1 if dtype == "bf16" else 0x7FC00001)), "row M was written"
 
 
+@pytest.mark.parametrize("wl,pi", _proj_cases("prefill_4b_layer"))
+def test_prefill_4b_bucket_lower_edges(wl, pi):
+    """Each row bucket's choice is timed at the bucket's upper end but also runs
+    at its lowest row count, where the last tile row holds one row: the 4B-like
+    projections at M = 17, 129, 513, 1025 and 2049 (bf16 Y, a NaN-filled guard
+    row), sampled rows against the oracle."""
+    cfg = synth.workload(wl)
+    p = cfg.projections[pi]
+    W = synth.weights(cfg, pi)
+    Wd = G.dev(W)
+    plan = G.plan(p.N, p.K, "bf16")
+    for M in (17, 129, 513, 1025, 2049):
+        X = synth.activations(cfg, pi, M)
+        Y = G.empty_out(M, p.N, "bf16", extra_rows=1)
+        plan.run(G.dev(X), Wd, Y)
+        G.check_against_oracle(Y, X, W, "bf16", rows=G.sample_rows(M, seed=M),
+                               label=f"{p.name} {p.N}x{p.K} M={M} {plan.choice(M)}")
+        assert np.all(G.host(Y)[M].view(np.uint16) == 0x7FC1), f"M={M}: row M was written"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_long_prompt_blocks_and_head(dtype):
     """8192 prompt rows as 8 blocks of 1024 through each 4B-like projection, then

@@ -793,8 +793,8 @@ static bool applies(const Candidate& c, int b, const proj_plan* p)
         return b == 1 && c.MMAX == 16;
     case Family::GemvMfma: return b <= 1;
     case Family::Gemm:
-        if (b <= 1) return false;
-        if (b == 2) return c.BM <= 128;
+        if (b == 0) return false;
+        if (b <= 2) return c.BM <= 128;
         if (b == 3) return c.BM <= 256;
         return c.BM >= 128 && c.SK <= 2;
     case Family::Plain: return false;  // only as a last resort

@@ -125,6 +125,24 @@ def test_27b_layer(wl, pi):
         assert np.all(G.host(Y)[M].view(np.uint16) == 0x7FC1)
 
 
+@pytest.mark.parametrize("wl,pi", _proj_cases("layer_27b"))
+def test_27b_layer_few_rows(wl, pi):
+    """The 27B-like projections at 2, 7 and 16 rows (the 2..16-row bucket, where
+    the tuner weighs the MFMA GEMV against GEMMs of up to 128 rows): every row
+    against the oracle, and the row past M untouched."""
+    cfg = synth.workload(wl)
+    p = cfg.projections[pi]
+    W = synth.weights(cfg, pi)
+    Wd = G.dev(W)
+    plan = G.plan(p.N, p.K, "bf16")
+    for M in (2, 7, 16):
+        X = synth.activations(cfg, pi, M)
+        Y = G.empty_out(M, p.N, "bf16", extra_rows=1)
+        plan.run(G.dev(X), Wd, Y)
+        G.check_against_oracle(Y, X, W, "bf16", label=f"{p.name} {p.N}x{p.K} M={M} {plan.choice(M)}")
+        assert np.all(G.host(Y)[M].view(np.uint16) == 0x7FC1), f"M={M}: row M was written"
+
+
 def test_epilogue_rounding_all_f32_patterns():
     """The epilogue's f32 -> bf16 conversion on all 2^32 f32 bit patterns:
     bit-equal to torch's device cast (a library routine, RNE) for every non-NaN

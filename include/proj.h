@@ -168,9 +168,10 @@ proj_plan* proj_plan_create_ex(int64_t N, int64_t K, int dtype, int flags, float
 
 /*
  * Enqueue Y[0:M, :] = X[0:M, :] . W^T on `stream`.  Rows of Y at or past M are
- * never written.  M == 0 returns PROJ_OK without launching; M < 0, null or
- * misaligned pointers, or a current device other than the plan's give
- * PROJ_EINVAL; a failed launch gives PROJ_EDEVICE.  M above 8192 is processed
+ * never written.  M == 0 returns PROJ_OK without launching; M < 0, an M for
+ * which X or Y would exceed 2^48 bytes, null or misaligned pointers, or a
+ * current device other than the plan's give PROJ_EINVAL; a failed launch
+ * gives PROJ_EDEVICE.  M above 8192 is processed
  * as consecutive blocks of at most 8192 rows.
  *
  * Only kernel launches are enqueued (one, or two for split-K and split-tail

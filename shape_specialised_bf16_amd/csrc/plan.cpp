@@ -1371,6 +1371,10 @@ int check_run_args(const proj_plan* p, const void* X, const void* W, void* Y, in
     if (!p) return set_error(PROJ_EINVAL, "plan is NULL");
     if (M < 0) return set_error(PROJ_EINVAL, "M=%lld is negative", (long long)M);
     if (M == 0) return PROJ_OK;
+    // X (M x K bf16) and Y (M x NO, at most 4 bytes each) must stay below 2^48
+    // bytes, far beyond any device memory, so the size arithmetic below cannot wrap
+    if (M > (int64_t(1) << 48) / (4 * std::max<int64_t>(p->K, p->NO)))
+        return set_error(PROJ_EINVAL, "M=%lld: X or Y would exceed 2^48 bytes", (long long)M);
     if (!X || !W || !Y) return set_error(PROJ_EINVAL, "null pointer (X=%p W=%p Y=%p)", X, W, (void*)Y);
     if (((uintptr_t)X | (uintptr_t)W | (uintptr_t)Y) & 15)
         return set_error(PROJ_EINVAL, "X, W and Y must be 16-byte aligned (X=%p W=%p Y=%p)", X, W, (void*)Y);

@@ -184,6 +184,8 @@ def test_wrong_arguments_are_rejected():
         p.run_ptr(X.data_ptr() + 2, W.data_ptr(), Y.data_ptr(), 4, None)
     with pytest.raises(ProjError, match="negative"):
         p.run_ptr(X.data_ptr(), W.data_ptr(), Y.data_ptr(), -1, None)
+    with pytest.raises(ProjError, match="2\\^48"):                 # sizes that would wrap: nothing enqueued
+        p.run_ptr(X.data_ptr(), W.data_ptr(), Y.data_ptr(), 1 << 60, None)
     with pytest.raises(ProjError, match="null"):
         p.run_ptr(0, W.data_ptr(), Y.data_ptr(), 4, None)
     with pytest.raises(ProjError, match="overlaps"):               # Y on top of W's last rows

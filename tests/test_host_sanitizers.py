@@ -85,6 +85,23 @@ int main(int argc, char** argv) {
     CHECK(proj_swiglu((void*)0x100000, (void*)0x100040, 4, 8, 0, nullptr) == PROJ_EINVAL);
     CHECK(proj_round_bf16((const float*)0x100000, (uint16_t*)0x100020, 16, nullptr) == PROJ_EINVAL);
     proj_plan_destroy(nullptr);
+    {   // proj_run's size and overlap checks on a plan built here (they come before any device call)
+        proj_plan q;
+        q.N = 5120; q.NO = 5120; q.K = 17408; q.dtype = 0;
+        char* const base = (char*)(uintptr_t(1) << 40);
+        CHECK(proj_run(&q, base, base + (1 << 30), base + (2 << 30), int64_t(1) << 60, nullptr) == PROJ_EINVAL);
+        CHECK(std::strstr(proj_last_error(), "2^48") != nullptr);
+        // the largest M the bound allows for K = 17408 is 2^48 / (4 K) = 4042322160
+        CHECK(proj_run(&q, base, base + (1 << 30), base + (2 << 30), 4042322161LL, nullptr) == PROJ_EINVAL);
+        CHECK(std::strstr(proj_last_error(), "2^48") != nullptr);
+        CHECK(proj_run(&q, base, base + (1 << 30), base + (2 << 30), 4042322160LL, nullptr) == PROJ_EINVAL);
+        CHECK(std::strstr(proj_last_error(), "overlaps") != nullptr);    // past the bound check, X reaches W
+        CHECK(proj_run(&q, base, base + (1 << 30), base + 4096, 4, nullptr) == PROJ_EINVAL);   // Y inside X
+        CHECK(std::strstr(proj_last_error(), "overlaps") != nullptr);
+        // separate buffers pass every argument check; what follows is the device lookup
+        (void)proj_run(&q, base, base + (1 << 30), base + (2 << 30), 4, nullptr);
+        CHECK(std::strstr(proj_last_error(), "2^48") == nullptr && std::strstr(proj_last_error(), "overlaps") == nullptr);
+    }
     // 3. one plan's modules compiled (the helper is looked up beside the binary
     //    that holds the library code -- this driver -- so here in this process)
     double sec = 0;

@@ -165,24 +165,28 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
     // BST = ST + 1: one more LDS buffer for W than for X (W copies a k-tile further ahead).
     // At a few hundred rows the GEMM streams W from HBM much as the GEMV does, and
     // a 128 x 128 tile with four W buffers keeps more of it in flight per CU.
-    struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[5]; int BST = 0; };
+    // kp: the entry also gets whole-tile and split-tail variants whose tiles visit
+    // the k-tiles of each block of four in a rotated order of their own (KP = 4),
+    // so tiles sharing a W or X panel under one L2 do not all miss on the same
+    // k-tile at once; given to the tiles the tuner picks across the workloads.
+    struct GT { int BM, BN, BK, ST, WM, WN, SWZ, maxSK, GM, DMA; int tails[5]; int BST = 0; bool kp = false; };
     const GT gts[] = {
         {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}}, {256, 256, 64, 2, 2, 4, 1, 1, 4, 1, {2}},
-        {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3},
-        {192, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3},
-        {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
+        {256, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3, true},
+        {192, 256, 64, 2, 2, 4, 1, 1, 8, 1, {2, 4}, 3, true},
+        {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}, 0, true}, {256, 128, 64, 3, 4, 2, 1, 1, 8, 1, {}},
         {256, 128, 64, 3, 4, 2, 1, 1, 4, 1, {2, 4}, 4},
         {128, 256, 64, 3, 2, 4, 1, 1, 4, 1, {2, 4}},
         {128, 128, 64, 2, 2, 2, 1, 8, 8, 1, {2, 4}}, {128, 128, 64, 2, 2, 2, 1, 2, 8, 0, {}},
         {128, 128, 64, 3, 2, 2, 1, 8, 8, 1, {2, 3, 4, 6}, 4},
-        {128, 64, 64, 3, 2, 2, 1, 8, 8, 1, {2, 3, 4, 6}, 4},
+        {128, 64, 64, 3, 2, 2, 1, 8, 8, 1, {2, 3, 4, 6}, 4, true},
         {128, 128, 32, 3, 2, 2, 2, 4, 8, 1, {}}, {64, 128, 64, 2, 1, 2, 1, 8, 8, 1, {}},
         // tiles 160 or 192 wide make whole rounds of 256 CUs where the power-of-two
         // widths leave part of a round: 5120 columns at 2048 rows are 8 x 32
         // tiles of 256 x 160, 2560 columns 16 x 16 tiles of 128 x 160, 18432
         // columns 8 x 96 tiles of 256 x 192 (160 = five 32-column MFMA blocks:
         // one wave column, so four waves of 64 x 160 or 32 x 160)
-        {256, 160, 64, 2, 4, 1, 1, 1, 8, 1, {2}, 3}, {128, 160, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 4},
+        {256, 160, 64, 2, 4, 1, 1, 1, 8, 1, {2}, 3}, {128, 160, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 4, true},
         {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 3},
         // four X and five W buffers: more k-tiles in flight per workgroup for the
         // few-hundred-row blocks, whose copies wait on HBM
@@ -193,9 +197,9 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         // before; the 256 x 192 tile with four W buffers wins at 2048 rows)
         {128, 128, 64, 3, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 6}, {128, 128, 64, 2, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 5},
         {128, 64, 64, 2, 2, 2, 1, 1, 8, 1, {2, 3, 4, 6}, 6}, {128, 160, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 5},
-        {256, 128, 64, 2, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}, 5}, {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 4},
+        {256, 128, 64, 2, 4, 2, 1, 1, 4, 1, {2, 3, 4, 6}, 5}, {256, 192, 64, 2, 4, 2, 1, 1, 8, 1, {2}, 4, true},
         // 96 columns (three 32-column MFMA blocks, four waves of 32 x 96)
-        {128, 96, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 4}};
+        {128, 96, 64, 3, 4, 1, 1, 1, 8, 1, {2}, 4, true}};
     for (const GT& g : gts) {
         if (N % g.BN) continue;
         if (wpack && 64 % g.BK) continue;  // panel layout: a k-tile inside one 64-value block
@@ -204,17 +208,19 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
         const int lds = (g.BST ? g.ST * g.BM + g.BST * g.BN : g.ST * (g.BM + g.BN)) * g.BK * 2;
         if (lds > 160 * 1024) continue;   // the LDS of one workgroup
         const int per_cu = std::max(1, std::min(2, 160 * 1024 / lds));
-        auto add = [&](int SK, int TL) {
+        auto add = [&](int SK, int TL, int KP = 0) {
             Candidate c;
             c.fam = Family::Gemm;
             c.BM = g.BM; c.BN = g.BN; c.BK = g.BK; c.ST = g.ST; c.WM = g.WM; c.WN = g.WN;
             c.SK = SK; c.GM = g.GM; c.SWZ = g.SWZ; c.DMA = g.DMA; c.BST = g.BST;
             c.TAILS = TL;
+            c.KP = KP;
             c.ROUND = TL > 1 ? cus * per_cu : 0;
             c.threads = 64 * g.WM * g.WN;
             c.max_m = kMaxBlockRows;
             c.name = fmt("gemm_%dx%dx%d_st%d_w%dx%d_sw%d_g%d_sk%d%s%s", c.BM, c.BN, c.BK, c.ST, c.WM, c.WN, c.SWZ,
                          c.GM, c.SK, c.DMA ? "" : "_reg", c.BST ? fmt("_b%d", c.BST).c_str() : "");
+            if (KP > 1) c.name += fmt("_kp%d", KP);
             if (TL > 1) c.name += fmt("_tail%d_r%d", TL, c.ROUND);
             if (SK > 1) c.reduce_name = fmt("splitk_reduce_sk%d", SK);
             if (TL > 1) c.reduce_name = c.name + "_reduce";
@@ -228,6 +234,11 @@ static std::vector<Candidate> enumerate_family(int64_t N, int64_t K, int cus, in
             if (SK <= g.maxSK && K % (g.BK * SK) == 0) add(SK, 1);
         for (int TL : g.tails)   // pieces of at least two k-tiles (KT / TL or one more)
             if (TL > 1 && K % g.BK == 0 && K / g.BK >= 2 * TL) add(1, TL);
+        if (g.kp && K % (4 * g.BK) == 0) {   // whole tiles of whole blocks of four k-tiles
+            add(1, 1, 4);
+            for (int TL : g.tails)
+                if (TL > 1 && K / g.BK >= 2 * TL) add(1, TL, 4);
+        }
     }
 
     // ---- plain kernel, any shape (K % 8 == 0)
@@ -335,7 +346,7 @@ static void emit_wrappers(std::ostringstream& s, const Candidate& c, int64_t N, 
         s << "extern \"C\" __global__ __launch_bounds__(" << c.threads << ") void " << c.name << sig
           << "\n{ gemm_mfma<" << c.BM << ", " << c.BN << ", " << c.BK << ", " << c.ST << ", " << c.WM << ", "
           << c.WN << ", " << c.SK << ", " << c.GM << ", " << c.SWZ << ", " << out << ", " << c.DMA << ", "
-          << c.TAILS << ", " << c.ROUND << ", " << c.E << ", " << c.BST << ">(X, W, Y, ws, M); }\n";
+          << c.TAILS << ", " << c.ROUND << ", " << c.E << ", " << c.BST << ", " << c.KP << ">(X, W, Y, ws, M); }\n";
         if (c.TAILS > 1) {
             s << "// " << c.reduce_name << ": tail tiles of " << c.name << ", " << c.TAILS
               << " pieces each, rounds of " << c.ROUND << " workgroups\n";

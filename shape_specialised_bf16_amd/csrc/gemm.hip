@@ -42,6 +42,15 @@
 // Both reductions use a fixed order, so results do not depend on which block
 // finishes first.
 //
+// K order (KP > 1): the k-tiles of each aligned block of KP are visited in an
+// order rotated by the tile's phase (tile-row + tile-column) mod KP, so tiles
+// that share a panel of W (same tile-column) or of X (same tile-row) and run
+// together under one L2 ask for different k-tiles first: each k-tile of a
+// block is fetched from beyond the L2 by one of them and found in the L2 by
+// the others a step or more later, instead of every tile waiting on the same
+// misses at once.  The order is fixed per tile, so results do not depend on
+// timing; a trailing KT % KP k-tiles keep their order.
+//
 // Tile order: the hardware deals consecutive workgroup ids round-robin to the
 // 8 XCDs, each with its own L2.  Whole-tile ids are first remapped so that
 // each XCD gets a contiguous range, then tile ids walk the tile grid GROUP_M
@@ -118,10 +127,23 @@ __device__ __forceinline__ long xcd_remap(long pid0, long nblk)
     return (xcd < rem) ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
 }
 
+// The k-tile read at step t (0 <= t < nkt) of a tile whose k order has phase
+// ph: inside the whole blocks of KP k-tiles (t < kpb = nkt - nkt % KP) the
+// block's k-tiles rotated by ph, so each block is permuted onto itself; the
+// trailing k-tiles, and every k-tile with KP <= 1, in order.
+template <int KP>
+__device__ __forceinline__ long ktile_order(long t, long kpb, long ph)
+{
+    if constexpr (KP > 1) {
+        if (t < kpb) t = (t & ~(long)(KP - 1)) | ((t + ph) & (KP - 1));
+    }
+    return t;
+}
+
 }  // namespace gemm_detail
 
 template <int BM, int BN, int BK, int STAGES, int WM, int WN, int SK, int GROUP_M, int SWZ, int OUT, int DMA = 1,
-          int TAILS = 1, int ROUND = 0, int E = 0, int BST = 0>
+          int TAILS = 1, int ROUND = 0, int E = 0, int BST = 0, int KP = 0>
 __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* __restrict__ W,
                                           void* __restrict__ Y, float* __restrict__ ws, int M)
 {
@@ -133,6 +155,7 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     static_assert(STAGES >= 2 && STAGES <= 4, "2..4 buffers");
     static_assert(K % (SK * BK) == 0, "K splits are whole k-tiles");
     static_assert(TAILS == 1 || (SK == 1 && ROUND > 0 && K % BK == 0 && K / BK >= TAILS), "tail pieces are whole k-tiles");
+    static_assert(KP == 0 || KP == 2 || KP == 4 || KP == 8, "k-tile blocks of a power of two");
     constexpr long KS = K / SK;
     constexpr long KT = KS / BK;                      // k-tiles of a whole (split-K) tile
     // tail piece z takes k-tiles [z*KT/TAILS, (z+1)*KT/TAILS): KT_TAIL of them, or
@@ -226,6 +249,8 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     long tm, tn;
     group_order<GROUP_M>(pid, tiles_m, TILES_N, &tm, &tn);
     const long m0 = tm * BM;
+    // the tile's phase in its blocks of KP k-tiles (uniform across the workgroup)
+    const long kph = KP > 1 ? ((tm + tn) & (KP - 1)) : 0;
     // first weight row of the tile (with the SwiGLU epilogue: its first gate row,
     // which is also its first output column; the tile reads BN/2 gate rows and
     // the BN/2 up rows NO below them)
@@ -397,17 +422,22 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
     auto kloop = [&](auto nkt) {
         constexpr long NKT = decltype(nkt)::value;
         auto clamp = [&](long t) -> long { return t < NKT ? t : NKT - 1; };
+        // the k-tile the copy for step t reads: t past the end re-reads the
+        // last one; inside the whole blocks of KP, the tile's rotated order (a
+        // permutation of each block, so every index stays below NKT)
+        constexpr long KPB = KP > 1 ? NKT - NKT % KP : 0;
+        auto src = [&](long t) -> long { return ktile_order<KP>(clamp(t), KPB, kph); };
         // prologue: X of tiles 0 .. LEAD-1 and W of tiles 0 .. LEAD_B-1 in flight,
         // in tile order (DMA), or tile 0 through registers; then tile 0
         // published and its first fragments read.
         if constexpr (DMA) {
 #pragma unroll
             for (int s = 0; s < LEAD_B; ++s) {
-                if (s < LEAD) issueA(bufA(s), clamp(s));
-                issueB(bufB(s), clamp(s));
+                if (s < LEAD) issueA(bufA(s), src(s));
+                issueB(bufB(s), src(s));
             }
         } else {
-            gload(0);
+            gload(src(0));
             lstore(bufA(0), bufB(0));
         }
         wait_vm_lds<DMA ? WAIT0 : 0>();
@@ -434,10 +464,10 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
             u32x4* bB = bufB(R);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (!DMA) {
-                gload(clamp(kt + 1));
+                gload(src(kt + 1));
             } else if constexpr (!EARLY) {
-                issueA(bufA(R + STAGES - 1), clamp(kt + LEAD));
-                issueB(bufB(R + NB - 1), clamp(kt + LEAD_B));
+                issueA(bufA(R + STAGES - 1), src(kt + LEAD));
+                issueB(bufB(R + NB - 1), src(kt + LEAD_B));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -456,8 +486,8 @@ __device__ __forceinline__ void gemm_mfma(const u16* __restrict__ X, const u16* 
             barrier_lds();
             read_frags(bufA(R + 1), bufB(R + 1), 0, 0);
             if constexpr (EARLY) {
-                issueA(bA, clamp(kt + LEAD));
-                issueB(bB, clamp(kt + LEAD_B));
+                issueA(bA, src(kt + LEAD));
+                issueB(bB, src(kt + LEAD_B));
             }
             mfmas((KK - 1) & 1);
             // the reads first, then the MFMAs with any copies slotted between them

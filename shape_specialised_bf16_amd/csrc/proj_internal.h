@@ -42,6 +42,7 @@ struct Candidate {
     int BST = 0;  // ST + 1: W in one LDS buffer more than X (0: X and W share each buffer)
     int TAILS = 1;   // >1: whole tiles plus a tail split TAILS ways along K
     int ROUND = 0;   // workgroups the device runs at once (CU count x blocks per CU)
+    int KP = 0;      // >1: each tile visits the k-tiles of every block of KP in its own rotated order
 
     int module = 0;            // index of the compiled module that holds it
     std::string name;          // extern "C" wrapper name in the generated module

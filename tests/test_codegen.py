@@ -200,3 +200,24 @@ def test_rmsnorm_and_swiglu_module_compiles(tmp_path):
                         "-std=c++17", "-include", "hip/hip_runtime.h", str(f), "-o", str(f) + ".o"],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
+
+
+def test_k_order_variants_pass_kp_to_their_kernel():
+    """Each "_kp4" GEMM is its row-ordered twin with KP = 4 as the last template
+    argument of gemm_mfma (every other argument equal), and every other GEMM
+    passes KP = 0; the fused-SwiGLU GEMMs have no K-order variant."""
+    src = ssb.emit_source(18432, 2560, "bf16")
+    calls = dict(re.findall(r'void (gemm_\w+)\([^)]*\)\n\{ gemm_mfma<([^>]*)>\(X, W, Y, ws, M\); \}', src))
+    kp = [n for n in calls if "_kp4" in n]
+    assert len(kp) >= 7
+    for name, args in calls.items():
+        a = [x.strip() for x in args.split(",")]
+        assert len(a) == 16, (name, a)
+        assert a[15] == ("4" if "_kp4" in name else "0"), (name, a)
+    for name in kp:
+        twin = name.replace("_kp4", "")
+        assert twin in calls, name
+        assert calls[name].rsplit(",", 1)[0] == calls[twin].rsplit(",", 1)[0], (name, twin)
+    fused = ssb.emit_source(18432, 2560, "bf16", epilogue="swiglu")
+    fused_calls = re.findall(r'void (gemm_\w+)\([^)]*\)\n\{ gemm_mfma<[^>]*>', fused)
+    assert fused_calls and not [n for n in fused_calls if "_kp4" in n and not n.endswith("_uf")]
